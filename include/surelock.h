@@ -1,0 +1,242 @@
+/*
+ * surelock.h — C ABI of the SureLock decoding step on one AMD MI355X (gfx950).
+ *
+ * SureLock (arXiv 2602.06412, "Stopping Computation for Converged Tokens in
+ * Masked Diffusion-LM Decoding") keeps, at every step of a masked diffusion LM
+ * sampler, an active set A_t of positions that are still computed and a locked
+ * set L_t of positions that are skipped.  A locked position no longer computes
+ * its Q projection or FFN; its K/V stay in a per-layer cache so the active
+ * queries still attend to it, and its posterior stays frozen (zhaoyang97
+ * Paper-Notes, 方法详解: 整体框架 and 永久锁定机制).  A position locks once the step
+ * divergence KL(p_t || p_{t-1}) is at most eps, optionally AND-ed with the
+ * confidence gate 1 - max_v p_t(v) <= q_m (same notes, 锁定判据 and
+ * 可选置信度门控).  Attention then costs O(M N d) and the FFN O(M d^2)
+ * instead of O(N^2 d) and O(N d^2) (paperdance abstract; gist.science/nl §2,
+ * Complexiteitsvermindering).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers unless the comment says "host".  The
+ *    caller allocates and owns every buffer, including workspaces; the library
+ *    never allocates device memory, never frees, and keeps no pointer after a
+ *    call returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The only host synchronisation happens when an `m_tot_host`
+ *    pointer is given: the call then waits for the stream and stores the new
+ *    active count there.
+ *  - Arguments are checked on the host before anything is launched: a NULL
+ *    required pointer, a non-positive size, an inconsistent size or an
+ *    unsupported shape returns SL_ERR_INVALID / SL_ERR_UNSUPPORTED and launches
+ *    nothing.  A failed launch returns SL_ERR_HIP; sl_last_error() gives the
+ *    message (per thread).  No exception crosses the ABI.
+ *  - Device contents (active lists, offsets) are trusted: an act_idx entry must
+ *    lie in [0, N) and be strictly ascending within its sequence, and act_off
+ *    must be non-decreasing with act_off[B] == M_tot.  sl_compact produces
+ *    exactly such lists.
+ *  - Element type: SL_BF16 (bfloat16 bit patterns, 2 bytes) or SL_F32
+ *    (4 bytes) for weights, activations, K/V caches and logits; the type is the
+ *    storage and MFMA operand type, accumulation is always fp32.
+ *  - Active lists: act_idx[M_tot] holds positions within their own sequence
+ *    (0..N-1), ascending; sequence b owns rows act_off[b] .. act_off[b+1]-1.
+ *    Row m of a compact [M_tot][...] buffer is the active position
+ *    (b, act_idx[m]); its row in a full [B*N][...] buffer is b*N + act_idx[m].
+ *  - Inputs are assumed finite; NaN propagates and is not checked.
+ */
+#ifndef SURELOCK_H
+#define SURELOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SL_OK = 0,
+  SL_ERR_INVALID = 1,     /* bad argument: NULL pointer, size <= 0, inconsistent sizes */
+  SL_ERR_UNSUPPORTED = 2, /* valid but not supported by these kernels (see each call) */
+  SL_ERR_HIP = 3          /* a HIP runtime call or launch failed */
+} sl_status;
+
+typedef enum { SL_BF16 = 0, SL_F32 = 1 } sl_dtype;
+
+typedef void* sl_stream; /* hipStream_t */
+
+/* Human-readable name of a status code (static string). */
+const char* sl_status_string(sl_status s);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* sl_last_error(void);
+/* Library version string. */
+const char* sl_version(void);
+
+/*
+ * sl_compact — active set A_t from the lock mask (stream compaction).
+ * A_t is every position not in L_t, kept in ascending order per sequence
+ * (zhaoyang97 notes, 整体框架: active set vs locked set).
+ *   locked   [B*N] uint8, 0 = active, nonzero = locked.
+ *   act_idx  [B*N] capacity; receives the M_tot active positions.
+ *   act_off  [B+1]; act_off[B] = M_tot.
+ *   m_tot_host  host int32* or NULL: if given, the stream is synchronised and
+ *               M_tot is stored there.
+ * Limits: B >= 1, N >= 1, B*N < 2^31.
+ */
+sl_status sl_compact(const uint8_t* locked, int B, int N, int32_t* act_idx, int32_t* act_off,
+                     int32_t* m_tot_host, sl_stream stream);
+
+/*
+ * sl_cache_scatter — write the fresh K/V rows of the active positions into a
+ * layer's cache, leaving locked positions' cached rows untouched
+ * (zhaoyang97 notes, 永久锁定机制: K^all[L_t] <- C.k[L_t]; gist.science/it §2:
+ * K/V cached for every layer).
+ *   k_cache, v_cache  [B][N][H][Dh] of `dtype`, updated in place.
+ *   k_new, v_new      [M_tot][H][Dh] of `dtype`.
+ * Limits: (H*Dh*elem_size) % 16 == 0.
+ */
+sl_status sl_cache_scatter(int dtype, void* k_cache, void* v_cache, const void* k_new,
+                           const void* v_new, const int32_t* act_idx, const int32_t* act_off,
+                           int B, int N, int M_tot, int H, int Dh, sl_stream stream);
+
+/*
+ * sl_attn_active — bidirectional attention of the M_tot active queries over
+ * all N cached keys of their own sequence: o = softmax(q K^T * scale) V per
+ * head, no mask.  Locked positions take part through their cached K/V
+ * (zhaoyang97 notes, 永久锁定机制; cost O(M N d), paperdance abstract).
+ *   q        [M_tot][H][Dh] of `dtype`, RoPE already applied.
+ *   k_cache, v_cache [B][N][H][Dh] of `dtype`.
+ *   out      [M_tot][H*Dh] of `dtype`.
+ *   ws       workspace of at least sl_attn_workspace_size(...) bytes (any
+ *            contents; used for split-KV partial results).
+ * Limits: Dh in {32, 64, 128}; N % 64 == 0.
+ */
+sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* act_off, int B, int N, int M_tot, int H, int Dh,
+                         float scale, void* out, void* ws, size_t ws_bytes, sl_stream stream);
+size_t sl_attn_workspace_size(int B, int N, int M_tot, int H, int Dh);
+
+/* Lock rule parameters (zhaoyang97 notes, 锁定判据 and 可选置信度门控). */
+typedef struct {
+  float eps;     /* lock when KL <= eps; eps <= 0 disables locking */
+  float gate_q;  /* quantile m in [0,1] of the gate u <= q_m(u); < 0 disables the gate */
+  int mask_id;   /* [MASK] token id excluded from the argmax; -1 = none */
+  int have_prev; /* 0 on the first step: no previous posterior, KL = +inf, nothing locks */
+} sl_lock_params;
+
+/*
+ * sl_kl_lock — the vocabulary pass plus the lock update and compaction.
+ * For every active row r (position (b, act_idx[r])):
+ *   A = LSE(cur), p = softmax(cur); kl[r] = KL(p || softmax(prev)) (nats,
+ *   +inf when have_prev == 0); u[r] = 1 - max_v p(v); lse[r] = A;
+ *   argmax[r] = argmax over v != mask_id (lowest id on ties); conf[r] = p(argmax).
+ * Then per sequence gate_thr[b] = the floor(m*(M_b-1))-th smallest u of its
+ * active rows (lower nearest rank; +inf when the gate is off), and a position
+ * locks, permanently, when cand (NULL = every active row) && have_prev &&
+ * eps > 0 && kl <= eps && (gate off || u <= gate_thr[b])
+ * (zhaoyang97 notes, 锁定判据 / 可选置信度门控 / 永久锁定机制; gist.science/it §2).
+ * Finally the new active list is compacted from the updated mask.
+ *   logits_cur, logits_prev [B*N][V] of `dtype`; only the active rows are read.
+ *   cand     [B*N] uint8 or NULL.
+ *   locked   [B*N] uint8, in/out (only 0 -> 1 transitions).
+ *   kl, u, lse, conf [M_tot] float; argmax [M_tot] int32 (conf/argmax may be NULL).
+ *   gate_thr [B] float or NULL.
+ *   new_act_idx [B*N] capacity, new_act_off [B+1] (may alias act_idx / act_off).
+ *   ws       at least sl_kl_lock_workspace_size(...) bytes, zero-filled before
+ *            its first use; every call leaves its counters zero again.
+ * Limits: V % 8 == 0 (bf16) or V % 4 == 0 (f32); N <= 65536.
+ */
+sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
+                     const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
+                     const uint8_t* cand, const sl_lock_params* params, uint8_t* locked,
+                     float* kl, float* u, float* lse, int32_t* argmax, float* conf,
+                     float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                     int32_t* m_tot_host, void* ws, size_t ws_bytes, sl_stream stream);
+size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V);
+
+/*
+ * sl_rope_table — cos/sin table of rotary position embeddings (rotate-half
+ * form: pair j = (x_j, x_{j+Dh/2}) rotated by pos * theta^(-2j/Dh)), computed
+ * on the device in double precision and stored as float pairs.
+ *   table [n_pos][Dh/2][2] float (cos, sin).
+ */
+sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_stream stream);
+
+/* One layer's weights, each stored [out_features][in_features] row-major. */
+typedef struct {
+  const void* wq; /* [d][d] */
+  const void* wk; /* [d][d] */
+  const void* wv; /* [d][d] */
+  const void* wo; /* [d][d] */
+  const void* wg; /* [F][d] SwiGLU gate */
+  const void* wu; /* [F][d] SwiGLU up */
+  const void* wd; /* [d][F] down */
+} sl_layer_weights;
+
+typedef struct {
+  int dtype;                       /* sl_dtype */
+  int n_layers, d, n_heads, head_dim, ffn, vocab;
+  float rms_eps;                   /* RMSNorm epsilon (unit gains, no biases) */
+  const sl_layer_weights* layers;  /* HOST array [n_layers] of device pointers */
+  const void* embed;               /* [V][d] or NULL (then the state gives h_in) */
+  const void* lm_head;             /* [V][d] or NULL (then the step stops after the layers) */
+  const float* rope;               /* [rope_n][Dh/2][2] from sl_rope_table */
+  int rope_n;                      /* >= N */
+} sl_model;
+
+typedef struct {
+  int B, N;
+  int M_tot;             /* host: active rows in act_idx (from the last compaction) */
+  int t;                 /* step index: logits[t%2] is written, logits[(t+1)%2] is p_{t-1} */
+  int32_t* tok;          /* [B*N] token ids (needed with embed, or with unmask_k > 0) */
+  uint8_t* cand;         /* [B*N] lock candidates (unmasked positions) or NULL = all */
+  uint8_t* locked;       /* [B*N] lock mask, in/out */
+  int32_t* act_idx;      /* [B*N] capacity: A_t in, A_{t+1} out (when locking) */
+  int32_t* act_off;      /* [B+1] */
+  void* k_cache;         /* [n_layers][B][N][H][Dh] */
+  void* v_cache;         /* [n_layers][B][N][H][Dh] */
+  const void* h_in;      /* [B*N][d] layer-0 input rows, or NULL to use embed[tok] */
+  float* h_out;          /* [M_tot][d] fp32 final hidden rows (residual stream), or NULL */
+  void* logits[2];       /* [B*N][V] each: double-buffered posterior store */
+  float* kl;             /* [M_tot] per-row statistics of this step (may be NULL when */
+  float* u;              /*  lm_head is NULL)                                          */
+  float* lse;
+  float* conf;
+  int32_t* argmax;
+  float* gate_thr;       /* [B] or NULL */
+  int32_t* lock_step;    /* [B*N] or NULL: step at which each position locked */
+  int32_t* m_tot_host;   /* host int32* or NULL: receives M_{t+1} (synchronises) */
+} sl_state;
+
+typedef struct {
+  float eps;      /* as sl_lock_params */
+  float gate_q;
+  int mask_id;
+  int do_lock;    /* 0: stop after the logits (no vocabulary pass, no lock) */
+  int unmask_k;   /* > 0: sampler unmasks this many [MASK] positions per sequence */
+} sl_step_params;
+
+/*
+ * sl_step — one whole SureLock iteration:
+ *   gather the active rows (embedding of tok, or h_in rows) -> for every layer:
+ *   RMSNorm, fused QKV projection + RoPE with the K/V rows scattered into the
+ *   layer cache, active-query attention over all N cached rows, O projection
+ *   + residual, RMSNorm, SwiGLU FFN + residual -> final RMSNorm, LM head
+ *   writing logits rows b*N+pos of logits[t%2] -> sl_kl_lock against
+ *   logits[(t+1)%2] -> optional sampler (the unmask_k most confident [MASK]
+ *   positions per sequence take their argmax token and become candidates)
+ *   -> compaction of A_{t+1} into act_idx/act_off.
+ * Locked rows are never read or written by any stage except as cached K/V
+ * (zhaoyang97 notes, 永久锁定机制: posterior frozen, K/V cached; gist.science/it
+ * §2: block input frozen, K/V cached for every layer).  A_t within A_{t-1}
+ * guarantees logits[(t+1)%2] holds p_{t-1} for every active row.
+ *   ws: at least sl_step_workspace_size(...) bytes, zero-filled before its
+ *       first use (its counters are left zero by every call).
+ * Limits: d % 128 == 0, ffn % 64 == 0, vocab % 128 == 0, head_dim in {32, 64, 128},
+ * n_heads*head_dim == d, N % 64 == 0, rope_n >= N.
+ */
+sl_status sl_step(const sl_model* model, sl_state* state, const sl_step_params* params,
+                  void* ws, size_t ws_bytes, sl_stream stream);
+size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SURELOCK_H */

@@ -1,0 +1,68 @@
+"""CPU checks of the C ABI: the library loads and exports every function include/surelock.h declares,
+and host-side argument checks reject bad calls before any GPU work (no device needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "surelock.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(sl_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sl_step", "sl_attn_active", "sl_kl_lock", "sl_compact", "sl_cache_scatter"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import token_locking_sparse_amd.surelock as S
+    L = S.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), "libsurelock.so does not export %s" % n
+    assert set(S.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings_and_host_checks():
+    import token_locking_sparse_amd.surelock as S
+    L = S.lib()
+    assert L.sl_status_string(0) == b"SL_OK"
+    assert L.sl_status_string(2) == b"SL_ERR_UNSUPPORTED"
+    # NULL pointers are rejected on the host before any launch
+    st = L.sl_compact(None, 1, 8, None, None, None, None)
+    assert st == 1 and b"NULL" in L.sl_last_error()
+    st = L.sl_rope_table(0, 32, ctypes.c_float(1e4), None, None)
+    assert st == 1
+    p = S.sl_lock_params(0.01, 0.5, -1, 1)
+    st = L.sl_kl_lock(7, None, None, 8, None, None, 1, 8, 0, None, ctypes.byref(p), None, None, None, None,
+                      None, None, None, None, None, None, None, 0, None)
+    assert st == 1 and b"dtype" in L.sl_last_error()
+    # unsupported head_dim
+    st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 64, 0, 1, 48,
+                          ctypes.c_float(1.0), None, ctypes.c_void_p(16), 1024, None)
+    assert st == 2
+
+
+def test_workspace_sizes_are_monotone_in_rows():
+    import token_locking_sparse_amd.surelock as S
+    a = S.sl_kl_lock_workspace_size(1, 4096, 100, 126464)
+    b = S.sl_kl_lock_workspace_size(1, 4096, 1639, 126464)
+    assert b >= a > 0
+    assert S.sl_attn_workspace_size(1, 1024, 64, 32, 128) > 0
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "token_locking_sparse_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.replace("oracle of", ""), "%s mentions the oracle" % f

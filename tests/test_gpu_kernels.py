@@ -1,0 +1,254 @@
+"""GPU parity of the kernel-level entry points against the CPU oracle.
+
+sl_compact and the lock/compaction decisions of sl_kl_lock are integer work:
+bit-exact, except (for sl_kl_lock) positions whose oracle KL lies within 1e-3
+of eps (the tolerance band the lock rule allows) or whose oracle u lies within
+GATE_BAND of the oracle gate threshold (fp32 vs fp64 ordering of u values;
+derivation in the design doc).  Floating-point outputs: KL within 1e-3 absolute;
+LSE, u, conf within the fp32 accumulation error of a V-term sum; attention
+outputs within bf16 / fp32 rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.surelock_oracle as O
+import workloads as W
+from tests.gpu_util import dev, host64, say, tdtype
+
+pytestmark = pytest.mark.gpu
+
+GATE_BAND = 1e-5
+KL_BAND = 1e-3
+
+
+def _sl():
+    import token_locking_sparse_amd as sl
+    return sl
+
+
+# ------------------------------------------------------------------ compaction
+@pytest.mark.parametrize("B,N,p", [(1, 1, 0.5), (1, 4096, 0.6), (3, 1000, 0.3), (8, 2048, 0.5),
+                                   (2, 64, 0.0), (2, 64, 1.0), (5, 3001, 0.97), (1, 65536, 0.5)])
+def test_compact_bit_exact(B, N, p):
+    sl = _sl()
+    say("compact", B, N, p)
+    locked = W.random_mask(B * N, p, seed=11, key=B * N + int(p * 100))
+    ai = torch.full((B * N,), -7, dtype=torch.int32, device="cuda")
+    ao = torch.full((B + 1,), -7, dtype=torch.int32, device="cuda")
+    m = sl.PinnedInt()
+    M = sl.sl_compact(torch.from_numpy(locked).cuda(), B, N, ai, ao, m)
+    ref_idx, ref_off = O.active_set(locked, B, N)
+    assert M == int(ref_off[-1])
+    np.testing.assert_array_equal(ao.cpu().numpy(), ref_off)
+    np.testing.assert_array_equal(ai[:M].cpu().numpy(), ref_idx)
+    assert np.all(ai[M:].cpu().numpy() == -7)          # nothing written past M_tot
+
+
+def test_compact_rejects_bad_args():
+    sl = _sl()
+    t = torch.zeros(8, dtype=torch.uint8, device="cuda")
+    ai = torch.empty(8, dtype=torch.int32, device="cuda")
+    ao = torch.empty(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(sl.SureLockError):
+        sl.sl_compact(t, 0, 4, ai, ao)
+    with pytest.raises(sl.SureLockError):
+        sl.sl_compact(t, 2, -1, ai, ao)
+
+
+# ------------------------------------------------------------------ KL-lock pass
+def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True):
+    sl = _sl()
+    B, N, V, M = case.B, case.N, case.V, case.M_tot
+    dt = tdtype(case.dtype)
+    glob = np.concatenate([b * N + case.act_idx[case.act_off[b]:case.act_off[b + 1]] for b in range(B)]).astype(np.int64)
+    fill = float("nan") if unlock_rows_nan else 0.0
+    cur = torch.full((B * N, V), fill, dtype=dt, device="cuda")
+    prev = torch.full((B * N, V), fill, dtype=dt, device="cuda")
+    gi = torch.from_numpy(glob).cuda()
+    cur.index_copy_(0, gi, dev(case.cur, case.dtype))
+    prev.index_copy_(0, gi, dev(case.prev, case.dtype))
+    locked = torch.from_numpy(case.locked.copy()).cuda()
+    ai = torch.from_numpy(case.act_idx).cuda()
+    ao = torch.from_numpy(case.act_off).cuda()
+    out = dict(kl=torch.empty(max(M, 1), device="cuda"), u=torch.empty(max(M, 1), device="cuda"),
+               lse=torch.empty(max(M, 1), device="cuda"), conf=torch.empty(max(M, 1), device="cuda"),
+               argmax=torch.empty(max(M, 1), dtype=torch.int32, device="cuda"),
+               gate_thr=torch.empty(B, device="cuda"))
+    nai = torch.full((B * N,), -7, dtype=torch.int32, device="cuda")
+    nao = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(sl.sl_kl_lock_workspace_size(B, N, M, V), dtype=torch.uint8, device="cuda")
+    cand = None if case.cand is None else torch.from_numpy(case.cand).cuda()
+    m = sl.PinnedInt()
+    Mn = sl.sl_kl_lock(cur, prev, V, ai, ao, B, N, M, cand, eps, gate_q, mask_id, have_prev, locked,
+                       out["kl"], out["u"], out["lse"], out["argmax"], out["conf"], out["gate_thr"], nai, nao,
+                       ws, m)
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["locked"] = locked.cpu().numpy()
+    res["act_idx"] = nai.cpu().numpy()
+    res["act_off"] = nao.cpu().numpy()
+    res["M"] = Mn
+    res["ws_clean"] = int(ws[:256 + 4 * max(M, 1)].count_nonzero().item()) == 0
+    return res
+
+
+def _oracle_kl(case, eps, gate_q, mask_id, have_prev):
+    z = O.widen(case.cur, case.dtype)
+    y = O.widen(case.prev, case.dtype) if have_prev else None
+    st = O.posterior_stats(z, y, mask_id)
+    lr = O.lock_update(case.locked, case.act_idx, case.act_off, case.B, case.N, st.kl, st.u, case.cand,
+                       eps, gate_q, have_prev)
+    return st, lr
+
+
+def _compare_kl(case, g, st, lr, eps, gate_q, have_prev):
+    M = case.M_tot
+    if M:
+        if have_prev:
+            assert np.max(np.abs(g["kl"][:M] - st.kl)) <= KL_BAND
+            assert np.max(np.abs(g["kl"][:M] - st.kl)) <= 2e-5   # what fp32 actually achieves here
+        else:
+            assert np.all(np.isinf(g["kl"][:M]))
+        np.testing.assert_allclose(g["lse"][:M], st.lse, rtol=2e-6, atol=2e-5)
+        np.testing.assert_allclose(g["u"][:M], st.u, rtol=0, atol=2e-6)
+        np.testing.assert_allclose(g["conf"][:M], st.conf, rtol=1e-5, atol=1e-7)
+        np.testing.assert_array_equal(g["argmax"][:M], st.argmax)   # exact: comparisons of exact inputs
+    if gate_q >= 0:
+        np.testing.assert_allclose(g["gate_thr"], lr.gate_thr, rtol=0, atol=2e-6)
+    # lock mask: exact except near-threshold positions
+    diff = np.flatnonzero(g["locked"] != lr.locked)
+    if len(diff):
+        rows_seq = O.seq_of_rows(case.act_off)
+        glob = rows_seq * case.N + case.act_idx.astype(np.int64)
+        row_of = {int(gp): i for i, gp in enumerate(glob)}
+        for gp in diff:
+            i = row_of.get(int(gp))
+            assert i is not None, "a position outside A_t changed its lock state"
+            near_kl = abs(st.kl[i] - eps) <= KL_BAND
+            near_gate = gate_q >= 0 and abs(st.u[i] - lr.gate_thr[rows_seq[i]]) <= GATE_BAND
+            assert near_kl or near_gate, "lock mismatch at %d (kl %.6g u %.9g thr %.9g)" % (
+                gp, st.kl[i], st.u[i], lr.gate_thr[rows_seq[i]])
+    assert np.all(g["locked"] >= case.locked)                          # monotone
+    # compaction of the GPU's own mask (property), and equality with the oracle when masks agree
+    ri, ro = O.active_set(g["locked"], case.B, case.N)
+    assert g["M"] == int(ro[-1])
+    np.testing.assert_array_equal(g["act_off"], ro)
+    np.testing.assert_array_equal(g["act_idx"][:g["M"]], ri)
+    if len(diff) == 0:
+        np.testing.assert_array_equal(g["act_idx"][:g["M"]], lr.act_idx)
+    assert g["ws_clean"], "workspace counters not restored to zero"
+    return len(diff)
+
+
+KL_CASES = [
+    # N, V, B, locked_frac, dtype, eps, gate_q, mask_id, have_prev, cand_frac
+    (64, 5000, 1, 0.6, "bf16", 0.01, 0.5, -1, True, None),
+    (300, 4096, 2, 0.3, "bf16", 0.002, -1.0, -1, True, 0.7),
+    (257, 12288, 3, 0.5, "bf16", 0.05, 0.3, 12287, True, 0.8),
+    (128, 2048, 2, 0.0, "f32", 0.01, 0.9, 2047, True, None),
+    (64, 512, 1, 0.25, "f32", 0.05, -1.0, 511, False, 0.5),
+    (64, 1000, 2, 1.0, "bf16", 0.05, 0.5, -1, True, None),            # every row locked: M = 0
+    (100, 126464, 1, 0.9, "bf16", 0.01, 0.5, 126463, True, None),     # full vocabulary, ragged chunks
+    (4096, 256, 1, 0.2, "bf16", 0.0, 0.5, -1, True, None),            # eps = 0: nothing locks
+]
+
+
+@pytest.mark.parametrize("N,V,B,lf,dtype,eps,gq,mask,hp,cf", KL_CASES)
+def test_kl_lock_parity(N, V, B, lf, dtype, eps, gq, mask, hp, cf):
+    say("kl_lock", N, V, B, lf, dtype, eps, gq, mask, hp, cf)
+    case = W.kl_lock_case(N=N, V=V, B=B, locked_frac=lf, dtype=dtype, cand_frac=cf, key=N + V)
+    g = _run_kl(case, eps, gq, mask, hp)
+    st, lr = _oracle_kl(case, eps, gq, mask, hp)
+    _compare_kl(case, g, st, lr, eps, gq, hp)
+    if eps <= 0 or not hp:
+        np.testing.assert_array_equal(g["locked"], case.locked)
+
+
+def test_kl_lock_repeat_reuses_workspace():
+    """Two calls in a row on one workspace (counters must come back to zero)."""
+    say("kl_lock repeat")
+    case = W.kl_lock_case(N=200, V=4096, B=2, locked_frac=0.5, dtype="bf16", key=77)
+    for _ in range(2):
+        g = _run_kl(case, 0.01, 0.5, -1, True)
+        st, lr = _oracle_kl(case, 0.01, 0.5, -1, True)
+        _compare_kl(case, g, st, lr, 0.01, 0.5, True)
+
+
+@pytest.mark.slow
+def test_kl_lock_full_size():
+    """The KL-lock workload at full size: N=4096, V=126464, 60 % locked (M=1639), eps=0.01, gate 0.5."""
+    say("kl_lock full size")
+    case = W.kl_lock_case()
+    assert case.M_tot == 1639
+    g = _run_kl(case, 0.01, 0.5, -1, True)
+    st, lr = _oracle_kl(case, 0.01, 0.5, -1, True)
+    nd = _compare_kl(case, g, st, lr, 0.01, 0.5, True)
+    say("full-size KL-lock: new locks gpu %d oracle %d, exempt mismatches %d" % (
+        int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
+
+
+# ------------------------------------------------------------------ attention
+ATTN_CASES = [
+    # dtype, Dh, H, N, Ms
+    ("bf16", 128, 2, 256, [256, 37]),
+    ("bf16", 128, 3, 1024, [5]),          # few query tiles: split over keys + merge
+    ("bf16", 64, 2, 128, [1, 128, 70]),
+    ("bf16", 32, 4, 64, [64]),
+    ("f32", 32, 4, 64, [64, 3]),
+    ("f32", 128, 2, 192, [150]),
+    ("f32", 64, 1, 512, [9, 300]),
+]
+
+
+@pytest.mark.parametrize("dtype,Dh,H,N,Ms", ATTN_CASES)
+def test_attention_parity(dtype, Dh, H, N, Ms):
+    sl = _sl()
+    say("attn", dtype, Dh, H, N, Ms)
+    B = len(Ms)
+    g = W.rng(123, Dh, N, len(Ms))
+    acts = [np.sort(g.permutation(N)[:M]).astype(np.int32) for M in Ms]
+    off = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int32)
+    M_tot = int(off[-1])
+    q = W.to_storage(W.normal(g, (M_tot, H, Dh), 1.0), dtype)
+    Kc = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+    Vc = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+    out = torch.empty(M_tot, H * Dh, dtype=tdtype(dtype), device="cuda")
+    ws = torch.empty(max(1, sl.sl_attn_workspace_size(B, N, M_tot, H, Dh)), dtype=torch.uint8, device="cuda")
+    sl.sl_attn_active(dev(q, dtype), dev(Kc, dtype), dev(Vc, dtype), torch.from_numpy(off).cuda(), B, N, M_tot,
+                      H, Dh, 1.0 / math.sqrt(Dh), out, ws)
+    got = host64(out).reshape(M_tot, H, Dh)
+    q64, K64, V64 = O.widen(q, dtype), O.widen(Kc, dtype), O.widen(Vc, dtype)
+    tol = 2e-2 if dtype == "bf16" else 2e-5
+    for b in range(B):
+        ref = O.attention(q64[off[b]:off[b + 1]], K64[b], V64[b], 1.0 / math.sqrt(Dh))
+        np.testing.assert_allclose(got[off[b]:off[b + 1]], ref, atol=tol, rtol=0)
+
+
+# ------------------------------------------------------------------ cache scatter
+def test_cache_scatter_bit_exact():
+    sl = _sl()
+    say("scatter")
+    B, N, H, Dh = 3, 128, 2, 64
+    for dtype in ("bf16", "f32"):
+        g = W.rng(5, 5)
+        Ms = [0, 77, 128]
+        acts = [np.sort(g.permutation(N)[:M]).astype(np.int32) for M in Ms]
+        ai = np.concatenate(acts).astype(np.int32)
+        off = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int32)
+        M = int(off[-1])
+        kc0 = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+        vc0 = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+        kn = W.to_storage(W.normal(g, (M, H, Dh), 1.0), dtype)
+        vn = W.to_storage(W.normal(g, (M, H, Dh), 1.0), dtype)
+        kc, vc = dev(kc0, dtype), dev(vc0, dtype)
+        sl.sl_cache_scatter(kc, vc, dev(kn, dtype), dev(vn, dtype), torch.from_numpy(ai).cuda(),
+                            torch.from_numpy(off).cuda(), B, N, M, H, Dh)
+        ek, ev = kc0.copy(), vc0.copy()
+        for b in range(B):
+            ek[b, acts[b]] = kn[off[b]:off[b + 1]]
+            ev[b, acts[b]] = vn[off[b]:off[b + 1]]
+        view = (lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)) if dtype == "bf16" else (lambda t: t.cpu().numpy())
+        np.testing.assert_array_equal(view(kc), ek)
+        np.testing.assert_array_equal(view(vc), ev)

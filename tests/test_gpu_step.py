@@ -1,0 +1,290 @@
+"""GPU parity of sl_step (whole SureLock iterations) against the CPU oracle.
+
+Hidden rows and K/V: relative L2 <= 1e-2 and |d| <= 2e-2*max(1,|ref|) (bf16
+storage; fp32 storage is held to 1e-4).  Logits: max-abs 2e-2.  KL: 1e-3
+absolute.  Lock masks and active lists: bit-exact except near-threshold
+positions (|KL-eps| <= 1e-3, or |u - q| <= 1e-5 when the gate is on).
+Locked positions' cache rows and posterior rows: bitwise unchanged.
+Multi-step loops are checked teacher-forced: every GPU step starts from the
+oracle's state (rounded to the storage type).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.surelock_oracle as O
+import workloads as W
+from tests.gpu_util import check_rel, dev, host64, round_storage, say, tdtype
+
+pytestmark = pytest.mark.gpu
+
+KL_BAND, GATE_BAND = 1e-3, 1e-5
+
+
+def _sl():
+    import token_locking_sparse_amd as sl
+    return sl
+
+
+def _odims(dm):
+    return O.OracleDims(dm.d, dm.n_heads, dm.head_dim, dm.ffn, dm.vocab, dm.rms_eps, dm.rope_theta)
+
+
+def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
+    sl = _sl()
+    layers = [{k: dev(v, dm.dtype) for k, v in L.items()} for L in layers_np]
+    return sl.DeviceModel(dtype=tdtype(dm.dtype), n_layers=dm.n_layers, d=dm.d, n_heads=dm.n_heads,
+                          head_dim=dm.head_dim, ffn=dm.ffn, vocab=dm.vocab, rms_eps=dm.rms_eps,
+                          rope_theta=dm.rope_theta, layers=layers,
+                          embed=None if embed is None else dev(embed, dm.dtype),
+                          lm_head=None if head is None else dev(head, dm.dtype), rope_n=rope_n)
+
+
+# ------------------------------------------------------------------ one layer, hidden rows in
+def _layer_case_run(dm, N, Ms, key, tol):
+    sl = _sl()
+    case = W.layer_case(dm, N, Ms, key=key)
+    B, M = case.B, case.M_tot
+    Wnp = W.layer_weights(dm, 0)
+    model = _dev_model(dm, [Wnp], rope_n=N)
+    locked = np.ones(B * N, np.uint8)
+    for b in range(B):
+        locked[b * N + case.act_idx[case.act_off[b]:case.act_off[b + 1]]] = 0
+    kc = dev(case.k_cache, dm.dtype).reshape(1, B, N, dm.n_heads, dm.head_dim)
+    vc = dev(case.v_cache, dm.dtype).reshape(1, B, N, dm.n_heads, dm.head_dim)
+    kc0, vc0 = kc.clone(), vc.clone()
+    st = sl.DeviceState(model, B, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, dm.dtype),
+                        k_cache=kc, v_cache=vc, with_h_out=True)
+    assert st.M_tot == M
+    np.testing.assert_array_equal(st.act_idx[:M].cpu().numpy(), case.act_idx)
+    st.step(eps=0.0, do_lock=False)
+    torch.cuda.synchronize()
+    got_h = st.h_out[:M].cpu().numpy().astype(np.float64)
+    # oracle
+    od = _odims(dm)
+    W64 = {k: O.widen(v, dm.dtype) for k, v in Wnp.items()}
+    h_in = O.widen(case.h_in, dm.dtype)
+    K64 = O.widen(case.k_cache, dm.dtype)
+    V64 = O.widen(case.v_cache, dm.dtype)
+    ostate = O.OracleState(B=B, N=N, t=0, locked=locked, kc=[K64], vc=[V64], h_in=h_in)
+    om = O.OracleModel(od, 1, lambda l: W64)
+    out = O.step(om, ostate, 0.0, -1.0, do_lock=False)
+    check_rel(got_h, out.h, tol[0], tol[1], "hidden rows")
+    gk = host64(kc).reshape(B * N, -1)
+    gv = host64(vc).reshape(B * N, -1)
+    rk = ostate.kc[0].reshape(B * N, -1)
+    rv = ostate.vc[0].reshape(B * N, -1)
+    act_g = np.flatnonzero(locked == 0)
+    check_rel(gk[act_g], rk[act_g], tol[0], tol[1], "fresh K rows")
+    check_rel(gv[act_g], rv[act_g], tol[0], tol[1], "fresh V rows")
+    lk = np.flatnonzero(locked != 0)
+    assert torch.equal(kc.reshape(B * N, -1)[torch.from_numpy(lk).cuda()], kc0.reshape(B * N, -1)[torch.from_numpy(lk).cuda()])
+    assert torch.equal(vc.reshape(B * N, -1)[torch.from_numpy(lk).cuda()], vc0.reshape(B * N, -1)[torch.from_numpy(lk).cuda()])
+
+
+SMALL_BF16 = W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16")
+SMALL_F32 = W.Dims(n_layers=1, d=128, n_heads=4, head_dim=32, ffn=384, vocab=512, dtype="f32")
+TOL = {"bf16": (1e-2, 2e-2), "f32": (1e-4, 1e-4)}
+
+
+@pytest.mark.parametrize("dm,N,Ms", [
+    (SMALL_BF16, 256, [256]), (SMALL_BF16, 256, [100]), (SMALL_BF16, 256, [1]),
+    (SMALL_BF16, 128, [128, 3, 77]), (SMALL_F32, 64, [64]), (SMALL_F32, 64, [20, 64]),
+    (W.Dims(n_layers=1, d=512, n_heads=8, head_dim=64, ffn=1024, vocab=1024, dtype="bf16"), 320, [300, 17]),
+    (SMALL_BF16, 1024, [700]),   # enough rows for the largest GEMM tile
+])
+def test_layer_step_parity(dm, N, Ms):
+    say("layer step", dm.d, dm.dtype, N, Ms)
+    _layer_case_run(dm, N, Ms, key=N + sum(Ms), tol=TOL[dm.dtype])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1024, 512, 256, 64])
+def test_layer_step_full_llada_shape(M):
+    """One LLaDA-8B-shaped layer (d=4096, 32x128, FFN 12288), N=1024, M active rows."""
+    say("full layer step M=%d" % M)
+    _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M, tol=TOL["bf16"])
+
+
+# ------------------------------------------------------------------ tiny fp32 sampler loop (teacher-forced)
+def _tiny_setup(dm, B, N, n_prompt):
+    layers = [W.layer_weights(dm, l) for l in range(dm.n_layers)]
+    emb = W.embed_weights(dm)
+    head = W.lm_head_weights(dm)
+    od = _odims(dm)
+    L64 = [{k: O.widen(v, dm.dtype) for k, v in L.items()} for L in layers]
+    om = O.OracleModel(od, dm.n_layers, lambda l: L64[l], O.widen(emb, dm.dtype), O.widen(head, dm.dtype))
+    tok0 = W.prompt_tokens(dm, B, N, n_prompt)
+    return layers, emb, head, om, tok0
+
+
+def _load_state(st, ost, dm, B, N, t):
+    """GPU state <- oracle state before step t (oracle -> GPU inputs, rounded to storage)."""
+    sl = _sl()
+    st.tok.copy_(torch.from_numpy(ost.tok).cuda())
+    st.cand.copy_(torch.from_numpy(ost.cand).cuda())
+    st.locked.copy_(torch.from_numpy(ost.locked).cuda())
+    for l in range(dm.n_layers):
+        st.k_cache[l].copy_(round_storage(ost.kc[l], dm.dtype))
+        st.v_cache[l].copy_(round_storage(ost.vc[l], dm.dtype))
+    if ost.post is not None:
+        post = np.nan_to_num(ost.post, nan=0.0)
+        st.logits[(t + 1) & 1].copy_(round_storage(post, dm.dtype))
+    st.M_tot = sl.sl_compact(st.locked, B, N, st.act_idx, st.act_off, st.m_host)
+    st.t = t
+
+
+def _step_compare(st, ost_before, out, dm, B, N, eps, gate_q, tol_logit):
+    """Compare one GPU step with the oracle step that started from the same state."""
+    M = len(out.act_idx)
+    rows_seq = O.seq_of_rows(out.act_off)
+    glob = rows_seq * N + out.act_idx.astype(np.int64)
+    cur = host64(st.logits[st.t & 1])    # st.t not yet advanced by the caller
+    assert np.max(np.abs(cur[glob] - out.logits)) <= tol_logit
+    kl = st.kl[:M].cpu().numpy()
+    u = st.u[:M].cpu().numpy()
+    if st.t > 0:
+        assert np.max(np.abs(kl - out.stats.kl)) <= KL_BAND
+    np.testing.assert_allclose(u, out.stats.u, atol=1e-4)
+    locked = st.locked.cpu().numpy()
+    diff = np.flatnonzero(locked != out.lock.locked)
+    for gp in diff:
+        i = int(np.flatnonzero(glob == gp)[0])
+        near = abs(out.stats.kl[i] - eps) <= KL_BAND or (gate_q >= 0 and abs(out.stats.u[i] - out.lock.gate_thr[rows_seq[i]]) <= GATE_BAND)
+        assert near, "lock mismatch at %d kl=%.6g" % (gp, out.stats.kl[i])
+    return len(diff)
+
+
+def test_tiny_loop_teacher_forced():
+    """2-layer fp32 model, d=128, 4x32 heads, FFN 384, V=512, N=64 (16 prompt + 48 masked),
+    16 steps, 3 unmasks per step, eps=0.05, gate off."""
+    sl = _sl()
+    dm = W.TINY
+    B, N, T, eps = 1, 64, 16, 0.05
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+    ost = O.OracleState(B=B, N=N, t=0, locked=np.zeros(B * N, np.uint8),
+                        kc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
+                        vc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
+                        tok=tok0.copy(), cand=(tok0 != dm.mask_id).astype(np.uint8),
+                        lock_step=np.full(B * N, -1, np.int32))
+    total_mismatch, Ms = 0, []
+    for t in range(T):
+        say("tiny loop step", t)
+        _load_state(st, ost, dm, B, N, t)
+        post_before = None if ost.post is None else ost.post.copy()
+        M_before = st.M_tot
+        ost.t = t
+        out = O.step(om, ost, eps, -1.0, True, dm.mask_id)
+        tok_o = ost.tok.copy()
+        O.sampler_unmask(ost.tok, ost.cand, out.act_idx, out.act_off, N, out.stats.argmax, out.stats.conf,
+                         dm.mask_id, 3)
+        p = sl.surelock.sl_step_params(eps, -1.0, dm.mask_id, 1, 3)
+        sl.sl_step(model.s, st.struct(), p, st.ws)
+        torch.cuda.synchronize()
+        total_mismatch += _step_compare(st, None, out, dm, B, N, eps, -1.0, 1e-4)
+        # sampler: same positions unmasked to the same tokens (teacher-forced, fp32)
+        np.testing.assert_array_equal(st.tok.cpu().numpy(), ost.tok)
+        Ms.append(M_before)
+    assert total_mismatch == 0
+    assert all(a >= b for a, b in zip(Ms, Ms[1:]))
+
+
+def test_tiny_loop_free_running_invariants():
+    """The GPU loop on its own: monotone A_t, frozen posterior and cache rows of locked positions."""
+    sl = _sl()
+    dm = W.TINY
+    B, N, T, eps = 2, 64, 16, 0.05
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+    frozen = {}
+    prevM = st.M_tot
+    for t in range(T):
+        say("free loop step", t)
+        locked_before = st.locked.clone()
+        st.step(eps, -1.0, dm.mask_id, True, 3)
+        torch.cuda.synchronize()
+        assert st.M_tot <= prevM
+        prevM = st.M_tot
+        assert bool(torch.all(st.locked >= locked_before))
+        new = torch.nonzero(st.locked > locked_before).flatten().tolist()
+        for g in new:
+            buf = t & 1
+            frozen[g] = (st.logits[buf][g].clone(), st.k_cache[:, g // N, g % N].clone(),
+                         st.v_cache[:, g // N, g % N].clone(), buf)
+            assert int(st.lock_step[g]) == t
+        for g, (p, k, v, buf) in frozen.items():
+            assert torch.equal(st.logits[buf][g], p)
+            assert torch.equal(st.k_cache[:, g // N, g % N], k)
+            assert torch.equal(st.v_cache[:, g // N, g % N], v)
+    assert len(frozen) > 0
+
+
+# ------------------------------------------------------------------ batched ragged step with LM head and lock
+@pytest.mark.parametrize("dm,B,N,gate", [
+    (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=2048, dtype="bf16"), 3, 128, 0.5),
+    (W.Dims(n_layers=2, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16"), 2, 192, -1.0),
+])
+def test_batched_ragged_step(dm, B, N, gate):
+    sl = _sl()
+    say("batched step", B, N, gate)
+    eps = 0.05
+    Ms = W.ragged_ms(B, N, key=B * N)
+    case = W.layer_case(dm, N, Ms, key=B + N)
+    layers = [W.layer_weights(dm, l) for l in range(dm.n_layers)]
+    head = W.lm_head_weights(dm)
+    od = _odims(dm)
+    L64 = [{k: O.widen(v, dm.dtype) for k, v in L.items()} for L in layers]
+    om = O.OracleModel(od, dm.n_layers, lambda l: L64[l], None, O.widen(head, dm.dtype))
+    locked = np.ones(B * N, np.uint8)
+    for b in range(B):
+        locked[b * N + case.act_idx[case.act_off[b]:case.act_off[b + 1]]] = 0
+    K0 = [O.widen(case.k_cache, dm.dtype) for _ in range(dm.n_layers)]
+    V0 = [O.widen(case.v_cache, dm.dtype) for _ in range(dm.n_layers)]
+    h_in = O.widen(case.h_in, dm.dtype)
+    # previous posterior: the oracle's logits of this very step plus N(0, 0.05^2) drift, rounded
+    probe = O.OracleState(B=B, N=N, t=0, locked=locked.copy(), kc=[k.copy() for k in K0],
+                          vc=[v.copy() for v in V0], h_in=h_in)
+    z0 = O.step(om, probe, 0.0, -1.0, do_lock=False).logits
+    rows_seq = O.seq_of_rows(case.act_off)
+    glob = rows_seq * N + case.act_idx.astype(np.int64)
+    prev_full = np.zeros((B * N, dm.vocab))
+    prev_full[glob] = z0 + W.normal(W.rng(W.SEED_DRIFT, 42), z0.shape, 0.05)
+    prev_st = W.to_storage(prev_full.astype(np.float32), dm.dtype)
+    prev64 = O.widen(prev_st, dm.dtype)
+    # oracle step at t=1 against that previous posterior
+    ost = O.OracleState(B=B, N=N, t=1, locked=locked.copy(), kc=[k.copy() for k in K0],
+                        vc=[v.copy() for v in V0], h_in=h_in, post=prev64.copy())
+    out = O.step(om, ost, eps, gate, True, -1)
+    # GPU
+    model = _dev_model(dm, layers, None, head, rope_n=N)
+    kc = torch.stack([dev(case.k_cache, dm.dtype)] * dm.n_layers)
+    vc = torch.stack([dev(case.v_cache, dm.dtype)] * dm.n_layers)
+    st = sl.DeviceState(model, B, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, dm.dtype),
+                        k_cache=kc, v_cache=vc)
+    st.logits[0].copy_(dev(prev_st, dm.dtype))     # buffer (t+1)%2 = 0 holds p_{t-1} at t = 1
+    st.t = 1
+    p = sl.surelock.sl_step_params(eps, gate, -1, 1, 0)
+    sl.sl_step(model.s, st.struct(), p, st.ws)
+    torch.cuda.synchronize()
+    st.M_tot = st.m_host.value
+    cur = host64(st.logits[1])
+    assert np.max(np.abs(cur[glob] - out.logits)) <= 2e-2
+    M = len(glob)
+    kl = st.kl[:M].cpu().numpy()
+    assert np.max(np.abs(kl - out.stats.kl)) <= KL_BAND
+    g_locked = st.locked.cpu().numpy()
+    diff = np.flatnonzero(g_locked != out.lock.locked)
+    for gp in diff:
+        i = int(np.flatnonzero(glob == gp)[0])
+        near = abs(out.stats.kl[i] - eps) <= KL_BAND or (gate >= 0 and abs(out.stats.u[i] - out.lock.gate_thr[rows_seq[i]]) <= GATE_BAND)
+        assert near
+    ri, ro = O.active_set(g_locked, B, N)
+    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(st.act_idx[:st.M_tot].cpu().numpy(), ri)

@@ -1,0 +1,327 @@
+// C ABI of the SureLock step: host-side argument checks, workspace layout and
+// the per-step launch sequence.  Declarations and contracts: include/surelock.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/surelock.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sl_status fail(sl_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sl_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SL_OK;
+  return fail(SL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SL_TRY(expr, what)                          \
+  do {                                              \
+    sl_status _st = hip_check((expr), (what));      \
+    if (_st != SL_OK) return _st;                   \
+  } while (0)
+
+#define SL_REQUIRE(cond, code, ...)                 \
+  do {                                              \
+    if (!(cond)) return fail((code), __VA_ARGS__);  \
+  } while (0)
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline int elem_bytes(int dtype) { return dtype == SL_BF16 ? 2 : 4; }
+
+// Workspace layout of sl_step.  The KL counters sit at offset 0 and are sized
+// for B*N rows, so their place does not move when M_tot shrinks between steps.
+struct StepLayout {
+  size_t kl_cnt, kl_part, h32, x, q, o, act, attn, total;
+  StepLayout(const sl_model* m, int B, int N, int M_tot) {
+    const int eb = elem_bytes(m->dtype);
+    const size_t M = (size_t)(M_tot > 0 ? M_tot : 1);
+    size_t off = 0;
+    kl_cnt = off; off += align256(sl::kl_counter_bytes(B * N));
+    kl_part = off; off += align256(m->lm_head ? sl::kl_part_bytes(M_tot, m->vocab, eb) : 256);
+    h32 = off; off += align256(M * m->d * 4);
+    x = off; off += align256(M * m->d * eb);
+    q = off; off += align256(M * m->d * eb);
+    o = off; off += align256(M * m->d * eb);
+    act = off; off += align256(M * m->ffn * eb);
+    attn = off; off += align256(sl::attn_ws_bytes(B, N, M_tot, m->n_heads, m->head_dim));
+    total = off;
+  }
+};
+
+sl_status check_dtype(int dtype) {
+  SL_REQUIRE(dtype == SL_BF16 || dtype == SL_F32, SL_ERR_INVALID, "dtype %d is neither SL_BF16 nor SL_F32", dtype);
+  return SL_OK;
+}
+
+sl_status check_model(const sl_model* m) {
+  SL_REQUIRE(m, SL_ERR_INVALID, "model is NULL");
+  sl_status st = check_dtype(m->dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(m->n_layers >= 1 && m->d > 0 && m->n_heads > 0 && m->head_dim > 0 && m->ffn > 0,
+             SL_ERR_INVALID, "non-positive model dimension");
+  SL_REQUIRE(m->n_heads * m->head_dim == m->d, SL_ERR_INVALID, "n_heads*head_dim (%d) != d (%d)",
+             m->n_heads * m->head_dim, m->d);
+  SL_REQUIRE(m->head_dim == 32 || m->head_dim == 64 || m->head_dim == 128, SL_ERR_UNSUPPORTED,
+             "head_dim %d not in {32, 64, 128}", m->head_dim);
+  SL_REQUIRE(m->d % 128 == 0, SL_ERR_UNSUPPORTED, "d %% 128 != 0 (d = %d)", m->d);
+  SL_REQUIRE(m->ffn % 64 == 0, SL_ERR_UNSUPPORTED, "ffn %% 64 != 0 (ffn = %d)", m->ffn);
+  SL_REQUIRE(m->layers, SL_ERR_INVALID, "layers is NULL");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const sl_layer_weights& w = m->layers[l];
+    SL_REQUIRE(w.wq && w.wk && w.wv && w.wo && w.wg && w.wu && w.wd, SL_ERR_INVALID,
+               "layer %d has a NULL weight pointer", l);
+  }
+  SL_REQUIRE(m->rope && m->rope_n > 0, SL_ERR_INVALID, "rope table missing");
+  if (m->lm_head) {
+    SL_REQUIRE(m->vocab > 0 && m->vocab % 128 == 0, SL_ERR_UNSUPPORTED, "vocab %% 128 != 0 (vocab = %d)", m->vocab);
+  }
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sl_status_string(sl_status s) {
+  switch (s) {
+    case SL_OK: return "SL_OK";
+    case SL_ERR_INVALID: return "SL_ERR_INVALID";
+    case SL_ERR_UNSUPPORTED: return "SL_ERR_UNSUPPORTED";
+    case SL_ERR_HIP: return "SL_ERR_HIP";
+  }
+  return "SL_ERR_UNKNOWN";
+}
+
+const char* sl_last_error(void) { return g_err; }
+const char* sl_version(void) { return "surelock-gfx950 0.1"; }
+
+sl_status sl_compact(const uint8_t* locked, int B, int N, int32_t* act_idx, int32_t* act_off,
+                     int32_t* m_tot_host, sl_stream stream) {
+  g_err[0] = 0;
+  SL_REQUIRE(locked && act_idx && act_off, SL_ERR_INVALID, "NULL pointer argument");
+  SL_REQUIRE(B >= 1 && N >= 1, SL_ERR_INVALID, "B and N must be positive");
+  SL_REQUIRE((long long)B * N < (1LL << 31), SL_ERR_UNSUPPORTED, "B*N too large");
+  hipStream_t s = (hipStream_t)stream;
+  SL_TRY(sl::launch_compact(locked, B, N, act_idx, act_off, s), "sl_compact launch");
+  if (m_tot_host) {
+    SL_TRY(hipMemcpyAsync(m_tot_host, act_off + B, 4, hipMemcpyDeviceToHost, s), "sl_compact copy");
+    SL_TRY(hipStreamSynchronize(s), "sl_compact sync");
+  }
+  return SL_OK;
+}
+
+sl_status sl_cache_scatter(int dtype, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
+                           int H, int Dh, sl_stream stream) {
+  g_err[0] = 0;
+  sl_status st = check_dtype(dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(k_cache && v_cache && act_off, SL_ERR_INVALID, "NULL pointer argument");
+  SL_REQUIRE(B >= 1 && N >= 1 && H >= 1 && Dh >= 1 && M_tot >= 0, SL_ERR_INVALID, "bad size");
+  SL_REQUIRE(M_tot == 0 || act_idx, SL_ERR_INVALID, "NULL act_idx");
+  SL_REQUIRE((long long)M_tot <= (long long)B * N, SL_ERR_INVALID, "M_tot > B*N");
+  SL_REQUIRE(M_tot == 0 || (k_new && v_new), SL_ERR_INVALID, "NULL k_new / v_new");
+  SL_REQUIRE(((long long)H * Dh * elem_bytes(dtype)) % 16 == 0, SL_ERR_UNSUPPORTED, "row bytes %% 16 != 0");
+  SL_TRY(sl::launch_cache_scatter(dtype, k_cache, v_cache, k_new, v_new, act_idx, act_off, B, N, M_tot,
+                                  H * Dh, (hipStream_t)stream),
+         "sl_cache_scatter launch");
+  return SL_OK;
+}
+
+size_t sl_attn_workspace_size(int B, int N, int M_tot, int H, int Dh) {
+  return sl::attn_ws_bytes(B, N, M_tot, H, Dh);
+}
+
+sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* act_off, int B, int N, int M_tot, int H, int Dh, float scale,
+                         void* out, void* ws, size_t ws_bytes, sl_stream stream) {
+  g_err[0] = 0;
+  sl_status st = check_dtype(dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(k_cache && v_cache && act_off, SL_ERR_INVALID, "NULL pointer argument");
+  SL_REQUIRE(B >= 1 && N >= 1 && H >= 1 && M_tot >= 0, SL_ERR_INVALID, "bad size");
+  SL_REQUIRE((long long)M_tot <= (long long)B * N, SL_ERR_INVALID, "M_tot > B*N");
+  SL_REQUIRE(M_tot == 0 || (q && out), SL_ERR_INVALID, "NULL q / out");
+  SL_REQUIRE(Dh == 32 || Dh == 64 || Dh == 128, SL_ERR_UNSUPPORTED, "head_dim %d not in {32, 64, 128}", Dh);
+  SL_REQUIRE(N % 64 == 0, SL_ERR_UNSUPPORTED, "N %% 64 != 0 (N = %d)", N);
+  SL_REQUIRE(ws_bytes >= sl::attn_ws_bytes(B, N, M_tot, H, Dh) && ws, SL_ERR_INVALID,
+             "workspace too small (%zu < %zu)", ws_bytes, sl::attn_ws_bytes(B, N, M_tot, H, Dh));
+  SL_TRY(sl::launch_attn(dtype, q, k_cache, v_cache, act_off, B, N, M_tot, H, Dh, scale, out, ws,
+                         (hipStream_t)stream),
+         "sl_attn_active launch");
+  return SL_OK;
+}
+
+size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V) {
+  // counters, then the segment partials sized for whichever element type splits rows more
+  const size_t p2 = sl::kl_part_bytes(M_tot, V, 2), p4 = sl::kl_part_bytes(M_tot, V, 4);
+  return align256(sl::kl_counter_bytes(B * N)) + align256(p2 > p4 ? p2 : p4);
+}
+
+sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
+                     const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
+                     const uint8_t* cand, const sl_lock_params* params, uint8_t* locked, float* kl,
+                     float* u, float* lse, int32_t* argmax, float* conf, float* gate_thr,
+                     int32_t* new_act_idx, int32_t* new_act_off, int32_t* m_tot_host, void* ws,
+                     size_t ws_bytes, sl_stream stream) {
+  g_err[0] = 0;
+  sl_status st = check_dtype(dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(params, SL_ERR_INVALID, "params is NULL");
+  SL_REQUIRE(act_off && locked && new_act_idx && new_act_off && ws, SL_ERR_INVALID, "NULL pointer argument");
+  SL_REQUIRE(M_tot == 0 || act_idx, SL_ERR_INVALID, "NULL act_idx");
+  SL_REQUIRE(B >= 1 && N >= 1 && V > 0 && M_tot >= 0, SL_ERR_INVALID, "bad size");
+  SL_REQUIRE((long long)M_tot <= (long long)B * N, SL_ERR_INVALID, "M_tot > B*N");
+  SL_REQUIRE(N <= 65536, SL_ERR_UNSUPPORTED, "N > 65536");
+  SL_REQUIRE((V * elem_bytes(dtype)) % 16 == 0, SL_ERR_UNSUPPORTED, "V*elem_size %% 16 != 0 (V = %d)", V);
+  SL_REQUIRE(M_tot == 0 || (logits_cur && kl && u && lse), SL_ERR_INVALID, "NULL logits / kl / u / lse");
+  SL_REQUIRE(M_tot == 0 || !params->have_prev || logits_prev, SL_ERR_INVALID, "NULL logits_prev");
+  SL_REQUIRE(params->gate_q <= 1.f, SL_ERR_INVALID, "gate_q > 1");
+  SL_REQUIRE(params->mask_id < V, SL_ERR_INVALID, "mask_id >= V");
+  const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
+  SL_REQUIRE(ws_bytes >= need, SL_ERR_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+  sl::KLRowParams rp{logits_cur, logits_prev, V, kl, u, lse, argmax, conf};
+  sl::TailParams tp{};
+  tp.B = B; tp.N = N; tp.M_tot = M_tot;
+  tp.eps = params->eps; tp.gate_q = params->gate_q; tp.mask_id = params->mask_id;
+  tp.have_prev = params->have_prev ? 1 : 0; tp.t = 0;
+  tp.act_idx = act_idx; tp.act_off = act_off; tp.cand = cand; tp.locked = locked; tp.lock_step = nullptr;
+  tp.kl = kl; tp.u = u; tp.conf = conf; tp.argmax = argmax; tp.gate_thr = gate_thr;
+  tp.tok = nullptr; tp.cand_out = nullptr; tp.unmask_k = 0;
+  tp.new_act_idx = new_act_idx; tp.new_act_off = new_act_off;
+  char* w = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  SL_TRY(sl::launch_kl_lock(dtype, rp, tp, (int*)w, (float*)(w + align256(sl::kl_counter_bytes(B * N))), s),
+         "sl_kl_lock launch");
+  if (m_tot_host) {
+    SL_TRY(hipMemcpyAsync(m_tot_host, new_act_off + B, 4, hipMemcpyDeviceToHost, s), "sl_kl_lock copy");
+    SL_TRY(hipStreamSynchronize(s), "sl_kl_lock sync");
+  }
+  return SL_OK;
+}
+
+sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_stream stream) {
+  g_err[0] = 0;
+  SL_REQUIRE(table, SL_ERR_INVALID, "table is NULL");
+  SL_REQUIRE(n_pos > 0 && head_dim > 0 && head_dim % 2 == 0 && theta > 0.f, SL_ERR_INVALID, "bad size");
+  SL_TRY(sl::launch_rope_table(n_pos, head_dim, theta, table, (hipStream_t)stream), "sl_rope_table launch");
+  return SL_OK;
+}
+
+size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot) {
+  if (!model) return 0;
+  return StepLayout(model, B, N, M_tot).total;
+}
+
+sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void* ws, size_t ws_bytes,
+                  sl_stream stream) {
+  g_err[0] = 0;
+  sl_status cs = check_model(m);
+  if (cs != SL_OK) return cs;
+  SL_REQUIRE(st && p, SL_ERR_INVALID, "state or params is NULL");
+  const int B = st->B, N = st->N, M = st->M_tot;
+  SL_REQUIRE(B >= 1 && N >= 1 && M >= 0 && (long long)M <= (long long)B * N, SL_ERR_INVALID,
+             "bad B / N / M_tot (%d, %d, %d)", B, N, M);
+  SL_REQUIRE(N % 64 == 0, SL_ERR_UNSUPPORTED, "N %% 64 != 0 (N = %d)", N);
+  SL_REQUIRE(N <= 65536, SL_ERR_UNSUPPORTED, "N > 65536");
+  SL_REQUIRE(m->rope_n >= N, SL_ERR_INVALID, "rope table has %d positions < N = %d", m->rope_n, N);
+  SL_REQUIRE(st->locked && st->act_idx && st->act_off && st->k_cache && st->v_cache, SL_ERR_INVALID,
+             "NULL state buffer");
+  SL_REQUIRE(st->h_in || (m->embed && st->tok), SL_ERR_INVALID, "need h_in, or embed and tok");
+  SL_REQUIRE(st->t >= 0, SL_ERR_INVALID, "t < 0");
+  const bool head = m->lm_head != nullptr;
+  const bool lock = head && p->do_lock;
+  if (head) SL_REQUIRE(st->logits[0] && st->logits[1], SL_ERR_INVALID, "logits buffers missing");
+  if (lock) {
+    SL_REQUIRE(st->kl && st->u && st->lse, SL_ERR_INVALID, "kl / u / lse missing");
+    SL_REQUIRE(p->gate_q <= 1.f, SL_ERR_INVALID, "gate_q > 1");
+    SL_REQUIRE(p->mask_id < m->vocab, SL_ERR_INVALID, "mask_id >= vocab");
+  }
+  if (lock && p->unmask_k > 0) {
+    SL_REQUIRE(st->tok && st->cand && st->argmax && st->conf && p->mask_id >= 0, SL_ERR_INVALID,
+               "sampler needs tok, cand, argmax, conf and a mask id");
+  }
+  const StepLayout L(m, B, N, M);
+  SL_REQUIRE(ws && ws_bytes >= L.total, SL_ERR_INVALID, "workspace too small (%zu < %zu)", ws_bytes, L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = m->dtype, eb = elem_bytes(dt);
+  const int d = m->d, F = m->ffn, H = m->n_heads, Dh = m->head_dim;
+  char* w = (char*)ws;
+  float* h32 = st->h_out ? st->h_out : (float*)(w + L.h32);
+  void* x = w + L.x;
+  void* q = w + L.q;
+  void* o = w + L.o;
+  void* act = w + L.act;
+  void* attn_ws = w + L.attn;
+  const size_t cache_layer = (size_t)B * N * d * eb;
+  const float scale = 1.f / sqrtf((float)Dh);
+
+  if (M > 0) {
+    SL_TRY(sl::launch_gather_norm(dt, st->h_in, m->embed, st->tok, st->act_idx, st->act_off, B, N, M, d,
+                                  m->rms_eps, h32, x, s),
+           "gather");
+    for (int l = 0; l < m->n_layers; ++l) {
+      const sl_layer_weights& W = m->layers[l];
+      char* kc = (char*)st->k_cache + l * cache_layer;
+      char* vc = (char*)st->v_cache + l * cache_layer;
+      sl::GemmArgs g{};
+      g.act_idx = st->act_idx; g.act_off = st->act_off; g.B = B; g.N = N; g.M = M; g.d = d; g.Dh = Dh;
+      g.split_k = 1;
+      // QKV + RoPE + K/V scatter into the layer cache
+      g.A = x; g.K = d; g.Nv = 3 * d; g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
+      g.out0 = q; g.out1 = kc; g.out2 = vc; g.rope = m->rope;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_QKV, g, s), "qkv gemm");
+      SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, B, N, M, H, Dh, scale, o, attn_ws, s), "attention");
+      // O projection + residual
+      g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s), "o gemm");
+      SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+      // SwiGLU FFN + residual
+      g.A = x; g.K = d; g.Nv = 2 * F; g.w0 = W.wg; g.w1 = W.wu; g.out0 = act;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_SWIGLU, g, s), "gate/up gemm");
+      g.A = act; g.K = F; g.Nv = d; g.w0 = W.wd; g.w1 = nullptr; g.out0 = h32;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s), "down gemm");
+      if (head || l + 1 < m->n_layers)
+        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+    }
+    if (head) {
+      sl::GemmArgs g{};
+      g.act_idx = st->act_idx; g.act_off = st->act_off; g.B = B; g.N = N; g.M = M; g.d = d; g.Dh = Dh;
+      g.split_k = 1;
+      g.A = x; g.K = d; g.Nv = m->vocab; g.w0 = m->lm_head; g.out0 = st->logits[st->t & 1];
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_LOGITS, g, s), "lm head gemm");
+    }
+  }
+  if (lock) {
+    sl::KLRowParams rp{st->logits[st->t & 1], st->logits[(st->t + 1) & 1], m->vocab, st->kl, st->u,
+                       st->lse, st->argmax, st->conf};
+    sl::TailParams tp{};
+    tp.B = B; tp.N = N; tp.M_tot = M;
+    tp.eps = p->eps; tp.gate_q = p->gate_q; tp.mask_id = p->mask_id; tp.have_prev = st->t > 0; tp.t = st->t;
+    tp.act_idx = st->act_idx; tp.act_off = st->act_off; tp.cand = st->cand; tp.locked = st->locked;
+    tp.lock_step = st->lock_step; tp.kl = st->kl; tp.u = st->u; tp.conf = st->conf; tp.argmax = st->argmax;
+    tp.gate_thr = st->gate_thr; tp.tok = st->tok; tp.cand_out = st->cand;
+    tp.unmask_k = p->unmask_k > 0 ? p->unmask_k : 0;
+    tp.new_act_idx = st->act_idx; tp.new_act_off = st->act_off;
+    SL_TRY(sl::launch_kl_lock(dt, rp, tp, (int*)(w + L.kl_cnt), (float*)(w + L.kl_part), s), "kl lock");
+    if (st->m_tot_host) {
+      SL_TRY(hipMemcpyAsync(st->m_tot_host, st->act_off + B, 4, hipMemcpyDeviceToHost, s), "M copy");
+      SL_TRY(hipStreamSynchronize(s), "M sync");
+    }
+  }
+  return SL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Host-side launchers of the SureLock kernels (internal; the public ABI is include/surelock.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sl {
+
+// Parameters of the lock / sampler tail that runs after the vocabulary pass.
+struct TailParams {
+  int B, N, M_tot;
+  float eps, gate_q;
+  int mask_id, have_prev;
+  int t;                 // step index recorded in lock_step
+  const int32_t* act_idx;
+  const int32_t* act_off;
+  const uint8_t* cand;   // may be NULL
+  uint8_t* locked;
+  int32_t* lock_step;    // may be NULL
+  const float* kl;
+  const float* u;
+  const float* conf;     // may be NULL when unmask_k == 0
+  const int32_t* argmax; // may be NULL when unmask_k == 0
+  float* gate_thr;       // may be NULL
+  int32_t* tok;          // sampler (unmask_k > 0)
+  uint8_t* cand_out;     // sampler marks unmasked positions as candidates
+  int unmask_k;
+  int32_t* new_act_idx;
+  int32_t* new_act_off;
+};
+
+struct KLRowParams {
+  const void* cur;
+  const void* prev;
+  int V;
+  float* kl;
+  float* u;
+  float* lse;
+  int32_t* argmax;  // may be NULL
+  float* conf;      // may be NULL
+};
+
+// Workspace of the vocabulary pass: a counter region (zero before first use,
+// left zero by every call; sized for the largest row count) and a partials region.
+size_t kl_counter_bytes(int max_rows);
+size_t kl_part_bytes(int M_tot, int V, int elem_bytes);
+hipError_t launch_compact(const uint8_t* locked, int B, int N, int32_t* act_idx, int32_t* act_off,
+                          hipStream_t s);
+hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, int* counters,
+                          float* part, hipStream_t s);
+
+hipError_t launch_cache_scatter(int dtype, void* kc, void* vc, const void* kn, const void* vn,
+                                const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                                int M_tot, int row_elems, hipStream_t s);
+
+size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh);
+hipError_t launch_attn(int dtype, const void* q, const void* kc, const void* vc,
+                       const int32_t* act_off, int B, int N, int M_tot, int H, int Dh, float scale,
+                       void* out, void* ws, hipStream_t s);
+
+hipError_t launch_rope_table(int n_pos, int Dh, float theta, float* table, hipStream_t s);
+
+// Row gather / RMSNorm.
+hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, const int32_t* tok,
+                              const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                              int M_tot, int d, float eps, float* h32, void* x, hipStream_t s);
+hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x,
+                       hipStream_t s);
+
+// GEMM family: C[m][n] = sum_k A[m][k] * W[n][k] with fused epilogues.
+enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+struct GemmArgs {
+  const void* A;       // [M][K]
+  int M, K;
+  int Nv;              // virtual output columns
+  // weights
+  const void* w0;      // QKV: wq, SWIGLU: wg, else the only matrix
+  const void* w1;      // QKV: wk, SWIGLU: wu
+  const void* w2;      // QKV: wv
+  // epilogue destinations
+  void* out0;          // QKV: q [M][d]; RESID: h32 (float) [M][Nv]; SWIGLU: act [M][F]; LOGITS: logits [B*N][V]
+  void* out1;          // QKV: k cache (one layer)
+  void* out2;          // QKV: v cache (one layer)
+  const float* rope;   // QKV: [rope_n][Dh/2][2]
+  int d, Dh;           // QKV geometry
+  const int32_t* act_idx;
+  const int32_t* act_off;
+  int B, N;
+  int split_k;         // RESID only (atomic accumulation)
+};
+hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s);
+int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh);
+
+}  // namespace sl

@@ -1,0 +1,219 @@
+"""ctypes binding of libsurelock.so (argument marshalling only).
+
+Every entry point mirrors the C function of the same name in
+include/surelock.h; tensors are passed as device pointers and the current
+torch stream is passed as the HIP stream.  Every step of the computation runs
+in the HIP library: there is no Python or CPU fallback, and a missing library
+raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsurelock.so")
+
+SL_BF16, SL_F32 = 0, 1
+_STATUS = {0: "SL_OK", 1: "SL_ERR_INVALID", 2: "SL_ERR_UNSUPPORTED", 3: "SL_ERR_HIP"}
+
+
+class SureLockError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s: %s" % (fn, _STATUS.get(status, status), msg))
+        self.status = status
+
+
+class sl_lock_params(C.Structure):
+    _fields_ = [("eps", C.c_float), ("gate_q", C.c_float), ("mask_id", C.c_int), ("have_prev", C.c_int)]
+
+
+class sl_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")]
+
+
+class sl_model(C.Structure):
+    _fields_ = [("dtype", C.c_int), ("n_layers", C.c_int), ("d", C.c_int), ("n_heads", C.c_int),
+                ("head_dim", C.c_int), ("ffn", C.c_int), ("vocab", C.c_int), ("rms_eps", C.c_float),
+                ("layers", C.POINTER(sl_layer_weights)), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
+                ("rope", C.c_void_p), ("rope_n", C.c_int)]
+
+
+class sl_state(C.Structure):
+    _fields_ = [("B", C.c_int), ("N", C.c_int), ("M_tot", C.c_int), ("t", C.c_int),
+                ("tok", C.c_void_p), ("cand", C.c_void_p), ("locked", C.c_void_p),
+                ("act_idx", C.c_void_p), ("act_off", C.c_void_p),
+                ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("h_in", C.c_void_p), ("h_out", C.c_void_p), ("logits", C.c_void_p * 2),
+                ("kl", C.c_void_p), ("u", C.c_void_p), ("lse", C.c_void_p), ("conf", C.c_void_p),
+                ("argmax", C.c_void_p), ("gate_thr", C.c_void_p), ("lock_step", C.c_void_p),
+                ("m_tot_host", C.c_void_p)]
+
+
+class sl_step_params(C.Structure):
+    _fields_ = [("eps", C.c_float), ("gate_q", C.c_float), ("mask_id", C.c_int), ("do_lock", C.c_int),
+                ("unmask_k", C.c_int)]
+
+
+EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
+           "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
+           "sl_rope_table", "sl_step", "sl_step_workspace_size")
+
+_lib = None
+
+
+def lib():
+    """Load libsurelock.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsurelock.so is not built (expected at %s); run __graft_entry__.build()" % LIB_PATH)
+    L = C.CDLL(LIB_PATH)
+    vp, i, f, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+    sig = {
+        "sl_status_string": (C.c_char_p, [i]),
+        "sl_last_error": (C.c_char_p, []),
+        "sl_version": (C.c_char_p, []),
+        "sl_compact": (i, [vp, i, i, vp, vp, vp, vp]),
+        "sl_cache_scatter": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]),
+        "sl_attn_active": (i, [i, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]),
+        "sl_attn_workspace_size": (sz, [i, i, i, i, i]),
+        "sl_kl_lock": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
+                           vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sl_kl_lock_workspace_size": (sz, [i, i, i, i]),
+        "sl_rope_table": (i, [i, i, f, vp, vp]),
+        "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
+        "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t, name="tensor", dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise SureLockError(fn, st, lib().sl_last_error().decode())
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return SL_BF16
+    if t == torch.float32:
+        return SL_F32
+    raise TypeError("storage dtype must be bfloat16 or float32, got %s" % t)
+
+
+class PinnedInt:
+    """A pinned host int32 that receives an active count (m_tot_host)."""
+
+    def __init__(self):
+        self.t = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+
+    @property
+    def ptr(self):
+        return self.t.data_ptr()
+
+    @property
+    def value(self) -> int:
+        return int(self.t[0])
+
+
+# ------------------------------------------------------------------ entry points
+def sl_compact(locked, B, N, act_idx, act_off, m_tot_host: PinnedInt | None = None, stream=None):
+    st = lib().sl_compact(_ptr(locked, "locked", torch.uint8), B, N, _ptr(act_idx, "act_idx", torch.int32),
+                          _ptr(act_off, "act_off", torch.int32), m_tot_host.ptr if m_tot_host else None,
+                          _stream(stream))
+    _check("sl_compact", st)
+    return m_tot_host.value if m_tot_host else None
+
+
+def sl_cache_scatter(k_cache, v_cache, k_new, v_new, act_idx, act_off, B, N, M_tot, H, Dh, stream=None):
+    dt = dtype_code(k_cache.dtype)
+    st = lib().sl_cache_scatter(dt, _ptr(k_cache, "k_cache", k_cache.dtype), _ptr(v_cache, "v_cache", k_cache.dtype),
+                                _ptr(k_new, "k_new", k_cache.dtype, optional=M_tot == 0),
+                                _ptr(v_new, "v_new", k_cache.dtype, optional=M_tot == 0),
+                                _ptr(act_idx, "act_idx", torch.int32), _ptr(act_off, "act_off", torch.int32),
+                                B, N, M_tot, H, Dh, _stream(stream))
+    _check("sl_cache_scatter", st)
+
+
+def sl_attn_workspace_size(B, N, M_tot, H, Dh) -> int:
+    return int(lib().sl_attn_workspace_size(B, N, M_tot, H, Dh))
+
+
+def sl_attn_active(q, k_cache, v_cache, act_off, B, N, M_tot, H, Dh, scale, out, ws, stream=None):
+    dt = dtype_code(k_cache.dtype)
+    st = lib().sl_attn_active(dt, _ptr(q, "q", k_cache.dtype, optional=M_tot == 0),
+                              _ptr(k_cache, "k_cache", k_cache.dtype), _ptr(v_cache, "v_cache", k_cache.dtype),
+                              _ptr(act_off, "act_off", torch.int32), B, N, M_tot, H, Dh, float(scale),
+                              _ptr(out, "out", k_cache.dtype, optional=M_tot == 0), _ptr(ws, "ws"),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    _check("sl_attn_active", st)
+
+
+def sl_kl_lock_workspace_size(B, N, M_tot, V) -> int:
+    return int(lib().sl_kl_lock_workspace_size(B, N, M_tot, V))
+
+
+def sl_kl_lock(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, eps, gate_q, mask_id,
+               have_prev, locked, kl, u, lse, argmax, conf, gate_thr, new_act_idx, new_act_off, ws,
+               m_tot_host: PinnedInt | None = None, stream=None):
+    dt = dtype_code(logits_cur.dtype)
+    p = sl_lock_params(float(eps), float(gate_q), int(mask_id), int(bool(have_prev)))
+    st = lib().sl_kl_lock(dt, _ptr(logits_cur, "logits_cur", logits_cur.dtype),
+                          _ptr(logits_prev, "logits_prev", logits_cur.dtype, optional=not have_prev), V,
+                          _ptr(act_idx, "act_idx", torch.int32) if M_tot > 0 else None,
+                          _ptr(act_off, "act_off", torch.int32), B, N, M_tot, _ptr(cand, "cand", torch.uint8, optional=True), C.byref(p),
+                          _ptr(locked, "locked", torch.uint8), _ptr(kl, "kl", torch.float32),
+                          _ptr(u, "u", torch.float32), _ptr(lse, "lse", torch.float32),
+                          _ptr(argmax, "argmax", torch.int32, optional=True),
+                          _ptr(conf, "conf", torch.float32, optional=True),
+                          _ptr(gate_thr, "gate_thr", torch.float32, optional=True),
+                          _ptr(new_act_idx, "new_act_idx", torch.int32), _ptr(new_act_off, "new_act_off", torch.int32),
+                          m_tot_host.ptr if m_tot_host else None, _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                          _stream(stream))
+    _check("sl_kl_lock", st)
+    return m_tot_host.value if m_tot_host else None
+
+
+def sl_rope_table(n_pos, head_dim, theta, table, stream=None):
+    st = lib().sl_rope_table(n_pos, head_dim, float(theta), _ptr(table, "table", torch.float32), _stream(stream))
+    _check("sl_rope_table", st)
+
+
+def sl_step_workspace_size(model: sl_model, B, N, M_tot) -> int:
+    return int(lib().sl_step_workspace_size(C.byref(model), B, N, M_tot))
+
+
+def sl_step(model: sl_model, state: sl_state, params: sl_step_params, ws, stream=None):
+    st = lib().sl_step(C.byref(model), C.byref(state), C.byref(params), _ptr(ws, "ws"),
+                       ws.numel() * ws.element_size(), _stream(stream))
+    _check("sl_step", st)
