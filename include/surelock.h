@@ -139,8 +139,7 @@ typedef struct {
  *   kl, u, lse, conf [M_tot] float; argmax [M_tot] int32 (conf/argmax may be NULL).
  *   gate_thr [B] float or NULL.
  *   new_act_idx [B*N] capacity, new_act_off [B+1] (may alias act_idx / act_off).
- *   ws       at least sl_kl_lock_workspace_size(...) bytes, zero-filled before
- *            its first use; every call leaves its counters zero again.
+ *   ws       at least sl_kl_lock_workspace_size(...) bytes (any contents).
  * Limits: V % 8 == 0 (bf16) or V % 4 == 0 (f32); N <= 65536.
  */
 sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
@@ -158,6 +157,32 @@ size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V);
  *   table [n_pos][Dh/2][2] float (cos, sin).
  */
 sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_stream stream);
+
+/* Epilogues of sl_gemm. */
+typedef enum {
+  SL_EPI_QKV_ROPE = 0, /* q -> out0 [M][d]; RoPE on q and k; k, v -> caches out1/out2 at rows b*N+pos */
+  SL_EPI_RESIDUAL = 1, /* out0 (fp32 [M][n_out]) += A W^T */
+  SL_EPI_SWIGLU = 2,   /* out0 [M][n_out/2] = SiLU(A W0^T) * (A W1^T) */
+  SL_EPI_LOGITS = 3    /* out0 rows b*N+pos of a [B*N][n_out] buffer = A W0^T */
+} sl_epilogue;
+
+/*
+ * sl_gemm — the gathered-row projections of the active rows, C = A W^T with a
+ * fused epilogue.  Only the M active rows are multiplied: locked rows skip
+ * their Q projection and FFN (zhaoyang97 notes, 永久锁定机制; O(M d^2),
+ * gist.science/nl §2).  sl_step calls the same kernels.
+ *   A        [M][K] of `dtype` (compact active rows).
+ *   w0,w1,w2 [n][K] weights: QKV_ROPE takes wq, wk, wv (n = d each, n_out = 3d);
+ *            SWIGLU takes the gate and up matrices (n = n_out/2 each);
+ *            RESIDUAL and LOGITS take w0 only (n = n_out).
+ *   rope     [>=N][head_dim/2][2] from sl_rope_table (QKV_ROPE only).
+ *   act_idx/act_off/B/N map compact rows to positions (QKV_ROPE, LOGITS).
+ * Limits: K*elem_size % 128 == 0; n_out % 64 == 0; QKV_ROPE needs d % 128 == 0.
+ */
+sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
+                  const void* w1, const void* w2, void* out0, void* out1, void* out2,
+                  const float* rope, int d, int head_dim, const int32_t* act_idx,
+                  const int32_t* act_off, int B, int N, sl_stream stream);
 
 /* One layer's weights, each stored [out_features][in_features] row-major. */
 typedef struct {
@@ -227,8 +252,8 @@ typedef struct {
  * (zhaoyang97 notes, 永久锁定机制: posterior frozen, K/V cached; gist.science/it
  * §2: block input frozen, K/V cached for every layer).  A_t within A_{t-1}
  * guarantees logits[(t+1)%2] holds p_{t-1} for every active row.
- *   ws: at least sl_step_workspace_size(...) bytes, zero-filled before its
- *       first use (its counters are left zero by every call).
+ *   ws: at least sl_step_workspace_size(...) bytes (any contents).  A workspace
+ *       sized for the first step's M_tot serves every later step (M only shrinks).
  * Limits: d % 128 == 0, ffn % 64 == 0, vocab % 128 == 0, head_dim in {32, 64, 128},
  * n_heads*head_dim == d, N % 64 == 0, rope_n >= N.
  */

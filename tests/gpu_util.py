@@ -44,3 +44,21 @@ def check_rel(got: np.ndarray, ref: np.ndarray, rel_l2: float, rel_max: float, w
     assert l2 <= rel_l2, "%s: relative L2 error %.3e > %.1e" % (what, l2, rel_l2)
     assert not bad.any(), "%s: %d elements beyond %.1e*max(1,|ref|); worst |d| %.3e at ref %.3e" % (
         what, int(bad.sum()), rel_max, float(np.abs(d)[bad].max()), float(ref[bad][np.argmax(np.abs(d)[bad])]))
+
+
+def check_hidden(got: np.ndarray, ref: np.ndarray, rel_l2: float, what: str, k_out: float = 7.0, rel_max: float = 2e-2):
+    """Tolerance for rows that went through bf16 intermediates (activations, q/k/v, P, o, FFN activation).
+
+    The error is the sum of many independent rounding errors, so it is close to
+    Gaussian: require relative L2 <= rel_l2, and per element
+    |d| <= max(k_out * rms(d), rel_max * max(1, |ref|)), i.e. no outliers beyond
+    7 standard deviations (a Gaussian over 4M elements peaks near 5.3)."""
+    d = got - ref
+    nr = np.linalg.norm(ref)
+    l2 = np.linalg.norm(d) / (nr if nr > 0 else 1.0)
+    rms = float(np.sqrt(np.mean(d * d))) if d.size else 0.0
+    lim = np.maximum(k_out * rms, rel_max * np.maximum(1.0, np.abs(ref)))
+    bad = np.abs(d) > lim
+    assert l2 <= rel_l2, "%s: relative L2 error %.3e > %.1e" % (what, l2, rel_l2)
+    assert not bad.any(), "%s: %d outliers; worst |d| %.3e with rms %.3e" % (what, int(bad.sum()), float(np.abs(d).max()), rms)
+    return l2, rms, float(np.abs(d).max()) if d.size else 0.0

@@ -79,7 +79,7 @@ def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True):
                gate_thr=torch.empty(B, device="cuda"))
     nai = torch.full((B * N,), -7, dtype=torch.int32, device="cuda")
     nao = torch.empty(B + 1, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(sl.sl_kl_lock_workspace_size(B, N, M, V), dtype=torch.uint8, device="cuda")
+    ws = torch.full((sl.sl_kl_lock_workspace_size(B, N, M, V),), 0xA5, dtype=torch.uint8, device="cuda")
     cand = None if case.cand is None else torch.from_numpy(case.cand).cuda()
     m = sl.PinnedInt()
     Mn = sl.sl_kl_lock(cur, prev, V, ai, ao, B, N, M, cand, eps, gate_q, mask_id, have_prev, locked,
@@ -90,7 +90,6 @@ def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True):
     res["act_idx"] = nai.cpu().numpy()
     res["act_off"] = nao.cpu().numpy()
     res["M"] = Mn
-    res["ws_clean"] = int(ws[:256 + 4 * max(M, 1)].count_nonzero().item()) == 0
     return res
 
 
@@ -138,7 +137,6 @@ def _compare_kl(case, g, st, lr, eps, gate_q, have_prev):
     np.testing.assert_array_equal(g["act_idx"][:g["M"]], ri)
     if len(diff) == 0:
         np.testing.assert_array_equal(g["act_idx"][:g["M"]], lr.act_idx)
-    assert g["ws_clean"], "workspace counters not restored to zero"
     return len(diff)
 
 
@@ -167,7 +165,7 @@ def test_kl_lock_parity(N, V, B, lf, dtype, eps, gq, mask, hp, cf):
 
 
 def test_kl_lock_repeat_reuses_workspace():
-    """Two calls in a row on one workspace (counters must come back to zero)."""
+    """Two calls in a row on one (garbage-filled) workspace give the same, correct result."""
     say("kl_lock repeat")
     case = W.kl_lock_case(N=200, V=4096, B=2, locked_frac=0.5, dtype="bf16", key=77)
     for _ in range(2):

@@ -39,15 +39,13 @@ sl_status hip_check(hipError_t e, const char* what) {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline int elem_bytes(int dtype) { return dtype == SL_BF16 ? 2 : 4; }
 
-// Workspace layout of sl_step.  The KL counters sit at offset 0 and are sized
-// for B*N rows, so their place does not move when M_tot shrinks between steps.
+// Workspace layout of sl_step (contents need no initialisation).
 struct StepLayout {
-  size_t kl_cnt, kl_part, h32, x, q, o, act, attn, total;
+  size_t kl_part, h32, x, q, o, act, attn, total;
   StepLayout(const sl_model* m, int B, int N, int M_tot) {
     const int eb = elem_bytes(m->dtype);
     const size_t M = (size_t)(M_tot > 0 ? M_tot : 1);
     size_t off = 0;
-    kl_cnt = off; off += align256(sl::kl_counter_bytes(B * N));
     kl_part = off; off += align256(m->lm_head ? sl::kl_part_bytes(M_tot, m->vocab, eb) : 256);
     h32 = off; off += align256(M * m->d * 4);
     x = off; off += align256(M * m->d * eb);
@@ -164,9 +162,10 @@ sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const vo
 }
 
 size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V) {
-  // counters, then the segment partials sized for whichever element type splits rows more
+  // segment partials, sized for whichever element type splits rows more
+  (void)B; (void)N;
   const size_t p2 = sl::kl_part_bytes(M_tot, V, 2), p4 = sl::kl_part_bytes(M_tot, V, 4);
-  return align256(sl::kl_counter_bytes(B * N)) + align256(p2 > p4 ? p2 : p4);
+  return align256(p2 > p4 ? p2 : p4);
 }
 
 sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
@@ -202,8 +201,7 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
   tp.new_act_idx = new_act_idx; tp.new_act_off = new_act_off;
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
-  SL_TRY(sl::launch_kl_lock(dtype, rp, tp, (int*)w, (float*)(w + align256(sl::kl_counter_bytes(B * N))), s),
-         "sl_kl_lock launch");
+  SL_TRY(sl::launch_kl_lock(dtype, rp, tp, (float*)w, s), "sl_kl_lock launch");
   if (m_tot_host) {
     SL_TRY(hipMemcpyAsync(m_tot_host, new_act_off + B, 4, hipMemcpyDeviceToHost, s), "sl_kl_lock copy");
     SL_TRY(hipStreamSynchronize(s), "sl_kl_lock sync");
@@ -216,6 +214,35 @@ sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_s
   SL_REQUIRE(table, SL_ERR_INVALID, "table is NULL");
   SL_REQUIRE(n_pos > 0 && head_dim > 0 && head_dim % 2 == 0 && theta > 0.f, SL_ERR_INVALID, "bad size");
   SL_TRY(sl::launch_rope_table(n_pos, head_dim, theta, table, (hipStream_t)stream), "sl_rope_table launch");
+  return SL_OK;
+}
+
+sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
+                  const void* w1, const void* w2, void* out0, void* out1, void* out2, const float* rope,
+                  int d, int head_dim, const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                  sl_stream stream) {
+  g_err[0] = 0;
+  sl_status st = check_dtype(dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(epilogue >= SL_EPI_QKV_ROPE && epilogue <= SL_EPI_LOGITS, SL_ERR_INVALID, "bad epilogue %d", epilogue);
+  SL_REQUIRE(M >= 0 && K > 0 && n_out > 0, SL_ERR_INVALID, "bad size");
+  if (M == 0) return SL_OK;
+  SL_REQUIRE(A && w0 && out0, SL_ERR_INVALID, "NULL pointer argument");
+  const sl::EpiKind epi = (sl::EpiKind)epilogue;
+  SL_REQUIRE(sl::gemm_supported(dtype, epi, n_out, K, d, head_dim), SL_ERR_UNSUPPORTED,
+             "unsupported GEMM shape (K=%d, n_out=%d)", K, n_out);
+  if (epi == sl::EPI_QKV) {
+    SL_REQUIRE(w1 && w2 && out1 && out2 && rope && act_idx && act_off, SL_ERR_INVALID, "QKV needs wk, wv, caches, rope, act lists");
+    SL_REQUIRE(n_out == 3 * d && d % 128 == 0 && head_dim > 0 && d % head_dim == 0 && head_dim % 2 == 0,
+               SL_ERR_UNSUPPORTED, "QKV needs n_out = 3d, d %% 128 == 0");
+  }
+  if (epi == sl::EPI_SWIGLU) SL_REQUIRE(w1, SL_ERR_INVALID, "SwiGLU needs the up matrix");
+  if (epi == sl::EPI_LOGITS) SL_REQUIRE(act_idx && act_off && B >= 1 && N >= 1, SL_ERR_INVALID, "LOGITS needs act lists");
+  sl::GemmArgs g{};
+  g.A = A; g.M = M; g.K = K; g.Nv = n_out; g.w0 = w0; g.w1 = w1; g.w2 = w2;
+  g.out0 = out0; g.out1 = out1; g.out2 = out2; g.rope = rope; g.d = d; g.Dh = head_dim;
+  g.act_idx = act_idx; g.act_off = act_off; g.B = B; g.N = N; g.split_k = 1;
+  SL_TRY(sl::launch_gemm(dtype, epi, g, (hipStream_t)stream), "sl_gemm launch");
   return SL_OK;
 }
 
@@ -315,7 +342,7 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
     tp.gate_thr = st->gate_thr; tp.tok = st->tok; tp.cand_out = st->cand;
     tp.unmask_k = p->unmask_k > 0 ? p->unmask_k : 0;
     tp.new_act_idx = st->act_idx; tp.new_act_off = st->act_off;
-    SL_TRY(sl::launch_kl_lock(dt, rp, tp, (int*)(w + L.kl_cnt), (float*)(w + L.kl_part), s), "kl lock");
+    SL_TRY(sl::launch_kl_lock(dt, rp, tp, (float*)(w + L.kl_part), s), "kl lock");
     if (st->m_tot_host) {
       SL_TRY(hipMemcpyAsync(st->m_tot_host, st->act_off + B, 4, hipMemcpyDeviceToHost, s), "M copy");
       SL_TRY(hipStreamSynchronize(s), "M sync");

@@ -41,14 +41,11 @@ struct KLRowParams {
   float* conf;      // may be NULL
 };
 
-// Workspace of the vocabulary pass: a counter region (zero before first use,
-// left zero by every call; sized for the largest row count) and a partials region.
-size_t kl_counter_bytes(int max_rows);
+// Workspace of the vocabulary pass: per-segment partials of split rows.
 size_t kl_part_bytes(int M_tot, int V, int elem_bytes);
 hipError_t launch_compact(const uint8_t* locked, int B, int N, int32_t* act_idx, int32_t* act_off,
                           hipStream_t s);
-hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, int* counters,
-                          float* part, hipStream_t s);
+hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s);
 
 hipError_t launch_cache_scatter(int dtype, void* kc, void* vc, const void* kn, const void* vn,
                                 const int32_t* act_idx, const int32_t* act_off, int B, int N,

@@ -3,10 +3,12 @@
 // Per active row (one or a few workgroups per row): one streaming pass over
 // the current and previous logits with an online (rescaled) log-sum-exp,
 // giving LSE, the step KL(p_t || p_{t-1}), 1 - max p and the argmax
-// (zhaoyang97 notes on SureLock, 锁定判据 and 可选置信度门控).  The last
-// workgroup to finish runs the tail: per-sequence gate quantile (radix select),
-// monotone lock update, optional unmasking sampler and stream compaction of the
-// next active set (same notes, 永久锁定机制; 整体框架).
+// (zhaoyang97 notes on SureLock, 锁定判据 and 可选置信度门控).  A second,
+// single-workgroup kernel merges split rows and runs the tail: per-sequence
+// gate quantile (radix select), monotone lock update, optional unmasking
+// sampler and stream compaction of the next active set (same notes,
+// 永久锁定机制; 整体框架).  The kernel boundary is the only hand-off between
+// workgroups, so no device-wide fences are needed.
 #include <float.h>
 #include <math.h>
 
@@ -17,6 +19,7 @@ namespace sl {
 
 constexpr int kKLThreads = 256;
 constexpr int kPartWords = 8;
+constexpr int kTailThreads = 1024;
 
 // ------------------------------------------------------------------ compaction
 // Ascending positions with locked == 0 of B sequences of N, written with the
@@ -85,7 +88,7 @@ __device__ float block_select_kth(const float* u, int o0, int o1, int k, TailSha
     for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
     __syncthreads();
     for (int m = o0 + tid; m < o1; m += blockDim.x) {
-      const uint32_t v = __float_as_uint(load_agent(u + m));
+      const uint32_t v = __float_as_uint(u[m]);
       if ((v & pmask) == prefix) atomicAdd(&sh.hist[(v >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -134,8 +137,8 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
       for (int m = o0 + tid; m < o1; m += blockDim.x) {
         const int64_t g = (int64_t)b * p.N + p.act_idx[m];
         bool ok = (p.cand == nullptr) || (p.cand[g] != 0);
-        ok = ok && (load_agent(p.kl + m) <= p.eps);
-        if (gate) ok = ok && (load_agent(p.u + m) <= thr);
+        ok = ok && (p.kl[m] <= p.eps);
+        if (gate) ok = ok && (p.u[m] <= thr);
         if (ok) {
           p.locked[g] = 1;
           if (p.lock_step) p.lock_step[g] = p.t;
@@ -150,7 +153,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
         const int pos = p.act_idx[m];
         const int64_t g = (int64_t)b * p.N + pos;
         if (p.tok[g] != p.mask_id) continue;
-        const float c = load_agent(p.conf + m);
+        const float c = p.conf[m];
         if (c > bc || (c == bc && pos < bp)) { bc = c; bp = pos; bm = m; }
       }
 #pragma unroll
@@ -167,7 +170,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
         }
         if (bm >= 0) {
           const int64_t g = (int64_t)b * p.N + bp;
-          p.tok[g] = load_agent(p.argmax + bm);
+          p.tok[g] = p.argmax[bm];
           p.cand_out[g] = 1;
         }
       }
@@ -178,10 +181,6 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
   block_compact(p.locked, p.B, p.N, p.new_act_idx, p.new_act_off, sh.w);
 }
 
-__global__ void __launch_bounds__(kKLThreads) tail_kernel(TailParams p) {
-  __shared__ TailShared sh;
-  tail_phase(p, sh);
-}
 
 // ------------------------------------------------------------------ row pass
 struct Part {
@@ -218,14 +217,38 @@ __device__ __forceinline__ Part shfl_part(const Part& x, int o) {
   return r;
 }
 
+// Row statistics from a (combined) partial: with S_a = sum e^(a - max a),
+// A = max a + ln S_a, max p = 1/S_a, KL = sum p (a - b) - A + B.
+template <typename T, bool PREV>
+__device__ void finish_row(const KLRowParams& rp, const Part& t, const char* crow, int C, int mask_id, int r) {
+  constexpr int E = Chunk<T>::kElems;
+  const float A = t.ma + logf(t.sa);
+  rp.lse[r] = A;
+  rp.u[r] = 1.f - 1.f / t.sa;
+  if (PREV) rp.kl[r] = t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb);
+  else rp.kl[r] = INFINITY;
+  // exact argmax inside the winning chunk (lowest id equal to the max, not the mask)
+  int am = 0;
+  if (t.bidx >= 0 && t.bidx < C) {   // always true for finite logits
+    float a[E];
+    Chunk<T>::unpack(ld16(crow + (size_t)t.bidx * 16), a);
+    am = t.bidx * E;
+    for (int j = E - 1; j >= 0; --j)
+      if (a[j] == t.best && t.bidx * E + j != mask_id) am = t.bidx * E + j;
+  }
+  if (rp.argmax) rp.argmax[r] = am;
+  if (rp.conf) rp.conf[r] = __expf(t.best - t.ma) / t.sa;
+}
+
+// Row pass: workgroup (row r, segment) streams its slice of the current and
+// previous logits once.  With one segment per row it finishes the row itself;
+// otherwise it stores its partial for the tail kernel.  No inter-workgroup
+// communication happens inside this kernel.
 template <typename T, bool PREV>
 __global__ void __launch_bounds__(kKLThreads)
-kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* part, int* rowcnt,
-               int* done) {
+kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* part) {
   constexpr int E = Chunk<T>::kElems;
   __shared__ Part s_part[kKLThreads / 64];
-  __shared__ int s_flag;
-  __shared__ TailShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x / n_seg, seg = blockIdx.x - r * n_seg;
   const int b = seq_of_row(tp.act_off, tp.B, r);
@@ -283,74 +306,51 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
       for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(bb[j], kLog2e, -mbl));
     }
   }
-  // workgroup reduction
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc = combine(acc, shfl_part(acc, o));
   if (lane == 0) s_part[wid] = acc;
   __syncthreads();
-
   if (tid == 0) {
     Part t = s_part[0];
     for (int w = 1; w < kKLThreads / 64; ++w) t = combine(t, s_part[w]);
-    bool row_done = true;
-    if (n_seg > 1) {
+    if (n_seg == 1) {
+      finish_row<T, PREV>(rp, t, crow, C, mask_id, r);
+    } else {
       float* pp = part + ((size_t)r * n_seg + seg) * kPartWords;
       pp[0] = t.ma; pp[1] = t.sa; pp[2] = t.ta; pp[3] = t.mb; pp[4] = t.sb; pp[5] = t.best;
       pp[6] = __int_as_float(t.bidx);
-      __threadfence();
-      const int prev_cnt = atomic_add_agent(rowcnt + r, 1);
-      row_done = (prev_cnt == n_seg - 1);
-      if (row_done) {
-        __threadfence();
-        const float* q = part + (size_t)r * n_seg * kPartWords;
-        Part x;
-        x.ma = load_agent(q + 0); x.sa = load_agent(q + 1); x.ta = load_agent(q + 2);
-        x.mb = load_agent(q + 3); x.sb = load_agent(q + 4); x.best = load_agent(q + 5);
-        x.bidx = __float_as_int(load_agent(q + 6));
-        for (int s = 1; s < n_seg; ++s) {
-          const float* qs = q + s * kPartWords;
-          Part y;
-          y.ma = load_agent(qs + 0); y.sa = load_agent(qs + 1); y.ta = load_agent(qs + 2);
-          y.mb = load_agent(qs + 3); y.sb = load_agent(qs + 4); y.best = load_agent(qs + 5);
-          y.bidx = __float_as_int(load_agent(qs + 6));
-          x = combine(x, y);
-        }
-        t = x;
-        store_agent(rowcnt + r, 0);
-      }
-    }
-    if (row_done) {
-      // Statistics of row r.  With S_a = sum e^(a - max a): A = max a + ln S_a,
-      // max p = 1/S_a, KL = sum p (a - b) - A + B.
-      const float A = t.ma + logf(t.sa);
-      rp.lse[r] = A;
-      rp.u[r] = 1.f - 1.f / t.sa;
-      if (PREV) rp.kl[r] = t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb);
-      else rp.kl[r] = INFINITY;
-      // exact argmax inside the winning chunk (lowest id equal to the max, not the mask)
-      int am = 0;
-      if (t.bidx >= 0 && t.bidx < C) {   // always true for finite logits
-        float a[E];
-        Chunk<T>::unpack(ld16(crow + (size_t)t.bidx * 16), a);
-        am = t.bidx * E;
-        for (int j = E - 1; j >= 0; --j)
-          if (a[j] == t.best && t.bidx * E + j != mask_id) am = t.bidx * E + j;
-      }
-      if (rp.argmax) rp.argmax[r] = am;
-      if (rp.conf) rp.conf[r] = __expf(t.best - t.ma) / t.sa;
-      __threadfence();
-      const int d = atomic_add_agent(done, 1);
-      s_flag = (d == tp.M_tot - 1);
-    } else {
-      s_flag = 0;
     }
   }
-  __syncthreads();
-  if (s_flag) {
-    __threadfence();
-    tail_phase(tp, sh);
-    if (tid == 0) store_agent(done, 0);
+}
+
+// Tail kernel (one workgroup): merge the segment partials of every row (when a
+// row was split), then gate quantile, lock update, sampler and compaction.
+template <typename T, bool PREV>
+__global__ void __launch_bounds__(kTailThreads)
+kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
+  __shared__ TailShared sh;
+  if (n_seg > 1) {
+    const int C = rp.V / Chunk<T>::kElems;
+    const size_t rowbytes = (size_t)rp.V * sizeof(T);
+    for (int r = threadIdx.x; r < tp.M_tot; r += blockDim.x) {
+      const float* q = part + (size_t)r * n_seg * kPartWords;
+      Part x;
+      x.ma = q[0]; x.sa = q[1]; x.ta = q[2]; x.mb = q[3]; x.sb = q[4]; x.best = q[5];
+      x.bidx = __float_as_int(q[6]);
+      for (int s2 = 1; s2 < n_seg; ++s2) {
+        const float* qs = q + s2 * kPartWords;
+        Part y;
+        y.ma = qs[0]; y.sa = qs[1]; y.ta = qs[2]; y.mb = qs[3]; y.sb = qs[4]; y.best = qs[5];
+        y.bidx = __float_as_int(qs[6]);
+        x = combine(x, y);
+      }
+      const int b = seq_of_row(tp.act_off, tp.B, r);
+      const int64_t g = (int64_t)b * tp.N + tp.act_idx[r];
+      finish_row<T, PREV>(rp, x, (const char*)rp.cur + g * rowbytes, C, tp.mask_id, r);
+    }
+    __syncthreads();
   }
+  tail_phase(tp, sh);
 }
 
 static int kl_nseg(int M_tot, int V, int elem_bytes) {
@@ -362,36 +362,33 @@ static int kl_nseg(int M_tot, int V, int elem_bytes) {
   return n < 1 ? 1 : n;
 }
 
-size_t kl_counter_bytes(int max_rows) {
-  return 256 + ((size_t)(max_rows > 0 ? max_rows : 1) * 4 + 255) / 256 * 256;
-}
-
 size_t kl_part_bytes(int M_tot, int V, int elem_bytes) {
   const int n_seg = kl_nseg(M_tot, V, elem_bytes);
   if (n_seg <= 1) return 256;
   return (size_t)(M_tot > 0 ? M_tot : 1) * n_seg * kPartWords * 4;
 }
 
-hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, int* counters,
-                          float* part, hipStream_t s) {
-  const int eb = dtype == 0 ? 2 : 4;
-  if (tp.M_tot <= 0) {
-    hipLaunchKernelGGL(tail_kernel, dim3(1), dim3(kKLThreads), 0, s, tp);
-    return hipGetLastError();
+template <typename T, bool PREV>
+static void kl_launch_t(const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s) {
+  const int n_seg = kl_nseg(tp.M_tot, rp.V, sizeof(T));
+  if (tp.M_tot > 0) {
+    const int C = rp.V * (int)sizeof(T) / 16;
+    const int seg_chunks = (C + n_seg - 1) / n_seg;
+    hipLaunchKernelGGL((kl_rows_kernel<T, PREV>), dim3((unsigned)tp.M_tot * n_seg), dim3(kKLThreads), 0, s, rp, tp,
+                       n_seg, seg_chunks, part);
   }
-  const int n_seg = kl_nseg(tp.M_tot, rp.V, eb);
-  const int C = rp.V * eb / 16;
-  const int seg_chunks = (C + n_seg - 1) / n_seg;
-  int* done = counters;
-  int* rowcnt = counters + 64;
-  const dim3 grid((unsigned)tp.M_tot * n_seg), block(kKLThreads);
+  hipLaunchKernelGGL((kl_tail_kernel<T, PREV>), dim3(1), dim3(kTailThreads), 0, s, rp, tp,
+                     tp.M_tot > 0 ? n_seg : 1, (const float*)part);
+}
+
+hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s) {
   const bool prev = tp.have_prev != 0;
   if (dtype == 0) {
-    if (prev) hipLaunchKernelGGL((kl_rows_kernel<bf16, true>), grid, block, 0, s, rp, tp, n_seg, seg_chunks, part, rowcnt, done);
-    else hipLaunchKernelGGL((kl_rows_kernel<bf16, false>), grid, block, 0, s, rp, tp, n_seg, seg_chunks, part, rowcnt, done);
+    if (prev) kl_launch_t<bf16, true>(rp, tp, part, s);
+    else kl_launch_t<bf16, false>(rp, tp, part, s);
   } else {
-    if (prev) hipLaunchKernelGGL((kl_rows_kernel<float, true>), grid, block, 0, s, rp, tp, n_seg, seg_chunks, part, rowcnt, done);
-    else hipLaunchKernelGGL((kl_rows_kernel<float, false>), grid, block, 0, s, rp, tp, n_seg, seg_chunks, part, rowcnt, done);
+    if (prev) kl_launch_t<float, true>(rp, tp, part, s);
+    else kl_launch_t<float, false>(rp, tp, part, s);
   }
   return hipGetLastError();
 }

@@ -77,8 +77,8 @@ class DeviceState:
         self.m_host = S.PinnedInt()
         self.M_tot = S.sl_compact(self.locked, B, N, self.act_idx, self.act_off, self.m_host)
         self.t = 0
-        # zero-filled once; the library leaves its counters zero after every call
-        self.ws = torch.zeros(model.workspace_size(B, N, B * N), dtype=torch.uint8, device=device)
+        # sized for M_tot = B*N, so it serves every later step (M only shrinks)
+        self.ws = torch.empty(model.workspace_size(B, N, B * N), dtype=torch.uint8, device=device)
 
     def struct(self) -> S.sl_state:
         st = S.sl_state()

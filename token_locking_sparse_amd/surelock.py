@@ -59,7 +59,7 @@ class sl_step_params(C.Structure):
 
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
-           "sl_rope_table", "sl_step", "sl_step_workspace_size")
+           "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_gemm")
 
 _lib = None
 
@@ -87,6 +87,7 @@ def lib():
         "sl_rope_table": (i, [i, i, f, vp, vp]),
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
+        "sl_gemm": (i, [i, i, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp, vp, i, i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -217,3 +218,18 @@ def sl_step(model: sl_model, state: sl_state, params: sl_step_params, ws, stream
     st = lib().sl_step(C.byref(model), C.byref(state), C.byref(params), _ptr(ws, "ws"),
                        ws.numel() * ws.element_size(), _stream(stream))
     _check("sl_step", st)
+
+
+SL_EPI_QKV_ROPE, SL_EPI_RESIDUAL, SL_EPI_SWIGLU, SL_EPI_LOGITS = 0, 1, 2, 3
+
+
+def sl_gemm(epilogue, A, M, K, n_out, w0, w1=None, w2=None, out0=None, out1=None, out2=None, rope=None,
+            d=0, head_dim=0, act_idx=None, act_off=None, B=0, N=0, stream=None):
+    dt = dtype_code(A.dtype)
+    st = lib().sl_gemm(dt, int(epilogue), _ptr(A, "A", A.dtype), M, K, n_out, _ptr(w0, "w0", A.dtype),
+                       _ptr(w1, "w1", A.dtype, optional=True), _ptr(w2, "w2", A.dtype, optional=True),
+                       _ptr(out0, "out0"), _ptr(out1, "out1", optional=True), _ptr(out2, "out2", optional=True),
+                       _ptr(rope, "rope", torch.float32, optional=True), d, head_dim,
+                       _ptr(act_idx, "act_idx", torch.int32, optional=True),
+                       _ptr(act_off, "act_off", torch.int32, optional=True), B, N, _stream(stream))
+    _check("sl_gemm", st)

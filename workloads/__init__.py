@@ -156,6 +156,23 @@ class KLLockCase:
         return int(self.act_off[-1])
 
 
+def kl_lock_mask(N: int, B: int = 1, locked_frac: float = 0.6, key: int = 0):
+    """floor(locked_frac*N) positions per sequence locked by a seeded permutation.
+
+    Returns (locked uint8 [B*N], act_idx int32 [M_tot], act_off int32 [B+1])."""
+    locked = np.zeros(B * N, dtype=np.uint8)
+    acts, offs = [], [0]
+    for b in range(B):
+        perm = rng(SEED_SETS, key, b).permutation(N)
+        nl = int(np.floor(locked_frac * N))
+        locked[b * N + perm[:nl]] = 1
+        act = np.sort(perm[nl:]).astype(np.int32)
+        acts.append(act)
+        offs.append(offs[-1] + len(act))
+    act_idx = np.concatenate(acts).astype(np.int32) if B else np.zeros(0, np.int32)
+    return locked, act_idx, np.asarray(offs, dtype=np.int32)
+
+
 def kl_lock_case(N: int = 4096, V: int = 126464, B: int = 1, locked_frac: float = 0.6,
                  spike_frac: float = 0.7, spike: float = 8.0, std: float = 2.0,
                  drift: float = 0.05, dtype: str = "bf16", cand_frac: float | None = None,
@@ -167,23 +184,15 @@ def kl_lock_case(N: int = 4096, V: int = 126464, B: int = 1, locked_frac: float 
     get +spike at one seeded token (same token in both steps); prev = cur +
     N(0, drift^2).  Only active rows are materialised.
     """
-    locked = np.zeros(B * N, dtype=np.uint8)
-    acts, offs = [], [0]
+    locked, act_idx, act_off = kl_lock_mask(N, B, locked_frac, key)
+    acts = [act_idx[act_off[b]:act_off[b + 1]] for b in range(B)]
     spike_rows = np.zeros(B * N, dtype=bool)
     spike_tok = np.zeros(B * N, dtype=np.int64)
     for b in range(B):
-        perm = rng(SEED_SETS, key, b).permutation(N)
-        nl = int(np.floor(locked_frac * N))
-        locked[b * N + perm[:nl]] = 1
-        act = np.sort(perm[nl:]).astype(np.int32)
-        acts.append(act)
-        offs.append(offs[-1] + len(act))
         gs = rng(SEED_SPIKE, key, b)
         rows = gs.permutation(N)[: int(round(spike_frac * N))]
         spike_rows[b * N + rows] = True
         spike_tok[b * N:(b + 1) * N] = gs.integers(0, V, size=N)
-    act_idx = np.concatenate(acts).astype(np.int32)
-    act_off = np.asarray(offs, dtype=np.int32)
     M = len(act_idx)
     glob = np.concatenate([b * N + a for b, a in enumerate(acts)]) if M else np.zeros(0, np.int64)
     cur = np.empty((M, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
