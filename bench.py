@@ -201,7 +201,7 @@ def gpu_part(args):
         "kl_lock": {"ms": round(ms_kl, 4), "gbs": round(kb / (ms_kl * 1e-3) / 1e9, 1), "bytes": kb, "M": M_kl,
                     "M_after": M_after, "frac_hbm_peak": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_ms_M1024": {k: round(v, 4) for k, v in br.items()},
-        "roofline": {"kernel": "gemm_kernel<bf16,...,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_kernel<bf16,128x256,...,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)", "bound": "mfma",
                      "achieved": round(fl_gu / (ms_gu * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fl_gu / (ms_gu * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": fl_gu, "avg_launch_ms": round(ms_gu, 4)},

@@ -41,10 +41,6 @@ struct AttnCfg {
   static_assert(KLoads >= 1 && kBKV * KC % kAttnThreads == 0, "K tile split");
 };
 
-__device__ __forceinline__ int kswz(int row, int c, int nchunks) {
-  const int m = (nchunks < 8 ? nchunks : 8) - 1;
-  return c ^ (row & m);
-}
 
 // LDS position of key k (0..63) of a tile inside V^T rows.
 template <typename T>
@@ -129,7 +125,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
     for (int i = 0; i < C::KLoads; ++i) {
       const int id = tid + i * kAttnThreads;
       const int kr = id / C::KC, c = id % C::KC;
-      st16(ks + kr * (Dh * (int)sizeof(T)) + kswz(kr, c, C::KC) * 16, kreg[i]);
+      st16(ks + kr * (Dh * (int)sizeof(T)) + swz<Dh * (int)sizeof(T)>(kr, c) * 16, kreg[i]);
     }
 #pragma unroll
     for (int i = 0; i < C::VLoads; ++i) {
@@ -146,7 +142,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
             const int d = dc * E + j;
             const uint32_t x0 = (j & 1) ? (a0[j >> 1] >> 16) : (a0[j >> 1] & 0xffffu);
             const uint32_t x1 = (j & 1) ? (a1[j >> 1] & 0xffff0000u) : (a1[j >> 1] << 16);
-            *(uint32_t*)(vs + d * (kBKV * 2) + ((pc ^ (d & 7)) << 4) + po) = x0 | x1;
+            *(uint32_t*)(vs + d * (kBKV * 2) + (swz<kBKV * 2>(d, pc) << 4) + po) = x0 | x1;
           }
         } else {
           const uint32_t* a0 = (const uint32_t*)&vreg[i][0];
@@ -155,7 +151,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
           for (int j = 0; j < E; ++j) {
             const int d = dc * E + j;
             uint2 pr; pr.x = a0[j]; pr.y = a1[j];
-            *(uint2*)(vs + d * (kBKV * 4) + ((pc ^ (d & 7)) << 4) + po) = pr;
+            *(uint2*)(vs + d * (kBKV * 4) + (swz<kBKV * 4>(d, pc) << 4) + po) = pr;
           }
         }
       }
@@ -188,7 +184,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
         const int kr = sub * 32 + l32;
 #pragma unroll
         for (int kk = 0; kk < C::nKK; ++kk) {
-          const u32x4 a = *(const u32x4*)(ks + kr * (Dh * (int)sizeof(T)) + kswz(kr, 2 * kk + hl, C::KC) * 16);
+          const u32x4 a = *(const u32x4*)(ks + kr * (Dh * (int)sizeof(T)) + swz<Dh * (int)sizeof(T)>(kr, 2 * kk + hl) * 16);
           Mfma<T>::run(s[sub], a, qf[kk]);
         }
       }
@@ -235,7 +231,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
 #pragma unroll
         for (int dt = 0; dt < Dh / 32; ++dt) {
           const int d = dt * 32 + l32;
-          const u32x4 a = *(const u32x4*)(vs + d * (kBKV * (int)sizeof(T)) + (((2 * ks2 + hl) ^ (d & 7)) << 4));
+          const u32x4 a = *(const u32x4*)(vs + d * (kBKV * (int)sizeof(T)) + (swz<kBKV * (int)sizeof(T)>(d, 2 * ks2 + hl) << 4));
           Mfma<T>::run(oacc[dt], a, pb);
         }
       }

@@ -69,6 +69,20 @@ template <> struct Mfma<float> {
   }
 };
 
+// ------------------------------------------------------------------ LDS swizzle
+// LDS tiles are rows of RB bytes made of 16-byte chunks.  A 128-bit LDS read is
+// served 16 lanes at a time over 64 four-byte banks (256 bytes), so the 16
+// rows a fragment read touches must put their chunks in 16 distinct slots of
+// a 256-byte window: chunk c of `row` is stored at position
+// c ^ ((row / max(1, 256/RB)) & (min(RB/16, 16) - 1)).
+template <int RB>
+__device__ __forceinline__ int swz(int row, int c) {
+  constexpr int W = RB >= 256 ? 1 : 256 / RB;
+  constexpr int CPR = RB / 16;
+  constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+  return c ^ ((row / W) & MASK);
+}
+
 // ------------------------------------------------------------------ wave / block reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

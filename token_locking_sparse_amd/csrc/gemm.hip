@@ -21,23 +21,58 @@
 namespace sl {
 
 constexpr int kGemmThreads = 256;
-constexpr int kRowBytes = 128;   // bytes of K per row per stage (64 bf16 / 32 fp32)
 
-template <typename T, int BM, int BN, int WM, int WN>
+// Tile geometry.  RB = bytes of K per row per k-tile (64 or 128); a k-tile is
+// staged in LDS as BM + BN rows of RB bytes, chunks placed by swz<RB> so the
+// 16 rows of every fragment read hit 16 distinct bank slots.
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S>
 struct GemmCfg {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int ALoads = BM * 8 / kGemmThreads;
-  static constexpr int BLoads = BN * 8 / kGemmThreads;
-  static constexpr int StageBytes = (BM + BN) * kRowBytes;
+  static constexpr int CPR = RB / 16;                 // chunks per row
+  static constexpr int KS = RB / 32;                  // MFMA k-steps per k-tile (32 bytes each)
+  static constexpr int ADma = BM * CPR / kGemmThreads;  // direct loads per thread per k-tile
+  static constexpr int BDma = BN * CPR / kGemmThreads;
+  static constexpr int StageBytes = (BM + BN) * RB;
+  static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(WM * WN == 4, "four waves");
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
-  static_assert(ALoads >= 1 && BLoads >= 1, "load split");
+  static_assert(ADma >= 1 && BDma >= 1 && BM * CPR % kGemmThreads == 0 && BN * CPR % kGemmThreads == 0, "load split");
+  static_assert(S >= 2 && S * StageBytes <= 150 * 1024, "LDS budget");
+  static_assert((S - 2) * (ADma + BDma) < 64, "vmcnt range");
 };
 
-__device__ __forceinline__ int gswz(int row, int c) { return c ^ (row & 7); }
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after the wave-uniform LDS base.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; others left at "no wait").
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() adds a release
+// fence, which makes the compiler drain every outstanding global load first
+// (vmcnt(0)), including the direct loads of later k-tiles that are meant to
+// stay in flight.  The main loop orders its LDS traffic itself: the stage it
+// overwrites was last read by ds_reads whose results the MFMAs have consumed,
+// and the tile it reads was waited for with wait_vmcnt before the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <typename T, int EPI>
 __device__ __forceinline__ const char* w_row_ptr(const GemmArgs& a, int vrow, int TN) {
@@ -57,14 +92,130 @@ __device__ __forceinline__ const char* w_row_ptr(const GemmArgs& a, int vrow, in
   return (const char*)a.w0 + (size_t)vrow * rb;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
-__global__ void __launch_bounds__(kGemmThreads)
+// 8 consecutive outputs of the storage type (one 16-byte store for bf16).
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float* y) {
+  if (sizeof(T) == 2) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16 lo = (bf16)y[2 * i], hi = (bf16)y[2 * i + 1];
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    st16(dst, w);
+  } else {
+    st16(dst, u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])});
+    st16((float*)dst + 4, u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])});
+  }
+}
+
+__device__ __forceinline__ void lds8(const float* p, float* y) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { y[i] = a[i]; y[4 + i] = b[i]; }
+}
+
+// One pass of the epilogue over PR rows of the fp32 tile (rows from mrow0).
+// Paired epilogues: output pair p of the tile takes its first element from
+// tile column (p / (TN/2)) * TN + p % (TN/2) and its partner TN/2 further.
+template <typename T, int EPI, int BN, int TN, int LDW, int PR>
+__device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int mrow0, int n0) {
+  const int tid = threadIdx.x;
+  if (EPI == EPI_RESID) {
+    if (a.split_k > 1) {
+      // fp32 atomics, consecutive lanes on consecutive floats of a row
+      for (int id = tid; id < PR * BN; id += kGemmThreads) {
+        const int r = id / BN, c = id % BN;
+        const int m = mrow0 + r;
+        if (m < a.M) unsafeAtomicAdd((float*)a.out0 + (size_t)m * a.Nv + n0 + c, tile[r * LDW + c]);
+      }
+    } else {
+      constexpr int CPR = BN / 4;
+      for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+        const int r = id / CPR, c = (id % CPR) * 4;
+        const int m = mrow0 + r;
+        if (m >= a.M) continue;
+        float* h = (float*)a.out0 + (size_t)m * a.Nv + n0 + c;
+        f32x4 y = *(const f32x4*)h;
+        y += *(const f32x4*)(tile + r * LDW + c);
+        *(f32x4*)h = y;
+      }
+    }
+  } else if (EPI == EPI_LOGITS) {
+    constexpr int CPR = BN / 8;
+    for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+      const int r = id / CPR, c = (id % CPR) * 8;
+      const int m = mrow0 + r;
+      if (m >= a.M) continue;
+      const int b = seq_of_row(a.act_off, a.B, m);
+      const size_t g = (size_t)b * a.N + a.act_idx[m];
+      float y[8];
+      lds8(tile + r * LDW + c, y);
+      store8<T>((T*)a.out0 + g * a.Nv + n0 + c, y);
+    }
+  } else {
+    constexpr int CPR = BN / 16;                  // 8-pair runs per row
+    for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+      const int r = id / CPR, p0 = (id % CPR) * 8;
+      const int m = mrow0 + r;
+      if (m >= a.M) continue;
+      const int c1 = (p0 / (TN / 2)) * TN + p0 % (TN / 2);
+      float x1[8], x2[8];
+      lds8(tile + r * LDW + c1, x1);
+      lds8(tile + r * LDW + c1 + TN / 2, x2);
+      const int pair = n0 / 2 + p0;
+      if (EPI == EPI_SWIGLU) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = silu_f(x1[i]) * x2[i];
+        store8<T>((T*)a.out0 + (size_t)m * (a.Nv / 2) + pair, y);
+      } else {
+        const int hd = a.d / 2, hh = a.Dh / 2;          // hh is a power of two
+        const int mat = pair >= 2 * hd ? 2 : (pair >= hd ? 1 : 0);
+        const int gp = pair - mat * hd;
+        const int jj = gp & (hh - 1);
+        const int col = (gp / hh) * a.Dh + jj;
+        const int pos = a.act_idx[m];
+        if (mat < 2) {
+          const float* cs = a.rope + ((size_t)pos * hh + jj) * 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 t = *(const f32x4*)(cs + 4 * q);   // (cos, sin) of pairs 2q, 2q+1
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int i = 2 * q + e;
+              const float c = t[2 * e], sn = t[2 * e + 1];
+              const float u1 = x1[i] * c - x2[i] * sn, u2 = x2[i] * c + x1[i] * sn;
+              x1[i] = u1;
+              x2[i] = u2;
+            }
+          }
+        }
+        T* dst;
+        if (mat == 0) {
+          dst = (T*)a.out0 + (size_t)m * a.d;
+        } else {
+          const int b = seq_of_row(a.act_off, a.B, m);
+          dst = (T*)(mat == 1 ? a.out1 : a.out2) + ((size_t)b * a.N + pos) * a.d;
+        }
+        store8<T>(dst + col, x1);
+        store8<T>(dst + col + hh, x2);
+      }
+    }
+  }
+}
+
+// A wave's direct load fills 1 KB = 1024/RB consecutive rows: lane l lands at
+// row l/CPR, stored chunk l%CPR, so it fetches the logical chunk that the
+// swizzle stores there.  S-stage pipeline: tile kt+S-1 is requested while tile
+// kt is multiplied; one barrier per k-tile.
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
-  using C = GemmCfg<T, BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::StageBytes];
-  __shared__ int s_pos[BM];
-  __shared__ int s_glob[BM];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  using C = GemmCfg<T, BM, BN, WM, WN, RB, S>;
+  __shared__ __attribute__((aligned(1024))) char smem[S * C::StageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int wm = wid / WN, wn = wid % WN;
 
   // workgroup -> tile; tiles sharing a weight tile are consecutive and sit on one XCD
@@ -74,58 +225,38 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   const int bm = lid % MT, bn = lid / MT;
   const int m0 = bm * BM, n0 = bn * BN;
   const int split = blockIdx.z;
-  const int KI = a.K * (int)sizeof(T) / kRowBytes;
+  const int KI = a.K * (int)sizeof(T) / RB;
   const int kt0 = split * k_iters_per_split;
   const int kt1 = min(KI, kt0 + k_iters_per_split);
 
-  if (EPI == EPI_QKV || EPI == EPI_LOGITS) {
-    for (int r = tid; r < BM; r += kGemmThreads) {
-      const int m = min(m0 + r, a.M - 1);
-      const int b = seq_of_row(a.act_off, a.B, m);
-      const int pos = a.act_idx[m];
-      s_pos[r] = pos;
-      s_glob[r] = b * a.N + pos;
-    }
-  }
-
-  // global source pointers of this thread's 16-byte chunks
-  const char* ap[C::ALoads];
-  const char* bp[C::BLoads];
+  // global sources of this thread's direct loads: lane l lands at tile row
+  // r = group*(1024/RB) + l/CPR, stored position l%CPR, holding the logical
+  // chunk that swz<RB> puts there (swz is an involution in the chunk index)
+  const int lrow = lane / C::CPR, lpos = lane % C::CPR;
   const size_t arb = (size_t)a.K * sizeof(T);
+  uint32_t aoff[C::ADma];
+  const char* bp[C::BDma];
 #pragma unroll
-  for (int i = 0; i < C::ALoads; ++i) {
-    const int id = tid + i * kGemmThreads;
-    const int r = id >> 3, c = id & 7;
-    ap[i] = (const char*)a.A + (size_t)min(m0 + r, a.M - 1) * arb + c * 16;
+  for (int i = 0; i < C::ADma; ++i) {
+    const int r = (i * 4 + wid) * (1024 / RB) + lrow;
+    aoff[i] = (uint32_t)((size_t)min(m0 + r, a.M - 1) * arb) + swz<RB>(r, lpos) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < C::BLoads; ++i) {
-    const int id = tid + i * kGemmThreads;
-    const int r = id >> 3, c = id & 7;
-    bp[i] = w_row_ptr<T, EPI>(a, n0 + r, C::TN) + c * 16;
+  for (int i = 0; i < C::BDma; ++i) {
+    const int r = (i * 4 + wid) * (1024 / RB) + lrow;
+    bp[i] = w_row_ptr<T, EPI>(a, n0 + r, C::TN) + swz<RB>(r, lpos) * 16;
   }
-  u32x4 ra[C::ALoads], rb[C::BLoads];
-  auto gload = [&](int kt) {
-    const size_t off = (size_t)kt * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < C::ALoads; ++i) ra[i] = ld16(ap[i] + off);
-#pragma unroll
-    for (int i = 0; i < C::BLoads; ++i) rb[i] = ld16(bp[i] + off);
-  };
-  auto lstore = [&](int stage) {
+  const char* abase = (const char*)a.A;
+  // direct loads j in [j0, j1) of k-tile kt into `stage` (A loads first, then B)
+  auto issue = [&](int kt, int stage, int j0, int j1) {
     char* as = smem + stage * C::StageBytes;
-    char* bs = as + BM * kRowBytes;
+    char* bs = as + BM * RB;
+    const size_t off = (size_t)kt * RB;
 #pragma unroll
-    for (int i = 0; i < C::ALoads; ++i) {
-      const int id = tid + i * kGemmThreads;
-      const int r = id >> 3, c = id & 7;
-      st16(as + r * kRowBytes + gswz(r, c) * 16, ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < C::BLoads; ++i) {
-      const int id = tid + i * kGemmThreads;
-      const int r = id >> 3, c = id & 7;
-      st16(bs + r * kRowBytes + gswz(r, c) * 16, rb[i]);
+    for (int j = 0; j < C::ADma + C::BDma; ++j) {
+      if (j < j0 || j >= j1) continue;
+      if (j < C::ADma) dma16(abase + aoff[j] + off, as + (j * 4 + wid) * 1024);
+      else dma16(bp[j - C::ADma] + off, bs + ((j - C::ADma) * 4 + wid) * 1024);
     }
   };
 
@@ -137,147 +268,182 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (kt0 < kt1) {
-    gload(kt0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int stage = (kt - kt0) & 1;
-    if (kt + 1 < kt1) gload(kt + 1);
-    const char* as = smem + stage * C::StageBytes;
-    const char* bs = as + BM * kRowBytes;
+  // LDS byte offsets of this lane's fragment rows (chunk added per k-step)
+  int arow[C::FM], brow[C::FN];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 fa[C::FM], fb[C::FN];
+  for (int i = 0; i < C::FM; ++i) arow[i] = wm * C::TM + i * 32 + l32;
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) brow[j] = wn * C::TN + j * 32 + l32;
+
+  constexpr int NDMA = C::ADma + C::BDma;
+  constexpr int DPS = (NDMA + C::KS - 1) / C::KS;   // direct loads issued per k-step
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (kt0 + st < kt1) issue(kt0 + st, st, 0, NDMA);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    // tile kt has landed when at most the (S-2) later tiles are still in flight
+    if (kt + S - 2 < kt1) wait_vmcnt<(S - 2) * NDMA>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    const bool pre = kt + S - 1 < kt1;
+    const int pre_stage = (kt + S - 1 - kt0) % S;
+    const char* as = smem + ((kt - kt0) % S) * C::StageBytes;
+    const char* bs = as + BM * RB;
+    u32x4 fa[2][C::FM], fb[2][C::FN];
+    auto frags = [&](int ks, int buf) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * C::TM + i * 32 + l32;
-        fa[i] = *(const u32x4*)(as + r * kRowBytes + gswz(r, 2 * ks + hl) * 16);
+        const int r = arow[i];
+        fa[buf][i] = *(const u32x4*)(as + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        const int r = wn * C::TN + j * 32 + l32;
-        fb[j] = *(const u32x4*)(bs + r * kRowBytes + gswz(r, 2 * ks + hl) * 16);
+        const int r = brow[j];
+        fb[buf][j] = *(const u32x4*)(bs + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
       }
+    };
+    frags(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      // this step's share of the next tile's direct loads, and the fragments of the
+      // next k-step, are spread between this step's MFMAs
+      if (pre) issue(kt + S - 1, pre_stage, ks * DPS, (ks + 1) * DPS);
+      if (ks + 1 < C::KS) frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
-    }
-    if (kt + 1 < kt1) lstore(stage ^ 1);
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- epilogues
+        for (int j = 0; j < C::FN; ++j) Mfma<T>::run(acc[i][j], fa[ks & 1][i], fb[ks & 1][j]);
+      if (ks + 1 < C::KS) {
+        // the direct loads go out first; the next step's fragment reads are spread
+        // between this step's MFMAs
+        constexpr int NRD = C::FM + C::FN;
+        constexpr int NM = C::FM * C::FN * (sizeof(T) == 2 ? 1 : 4);
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int lr = wm * C::TM + i * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
-      const int m = m0 + lr;
-      if (m >= a.M) continue;
-      if (EPI == EPI_RESID) {
-        float* h = (float*)a.out0 + (size_t)m * a.Nv + n0 + wn * C::TN + l32;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          if (a.split_k > 1) unsafeAtomicAdd(h + j * 32, acc[i][j][v]);
-          else h[j * 32] += acc[i][j][v];
-        }
-      } else if (EPI == EPI_LOGITS) {
-        T* o = (T*)a.out0 + (size_t)s_glob[lr] * a.Nv + n0 + wn * C::TN + l32;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) o[j * 32] = from_f32<T>(acc[i][j][v]);
-      } else {
-        const int pbase = (n0 + wn * C::TN) / 2 + l32;
-#pragma unroll
-        for (int j = 0; j < C::FN / 2; ++j) {
-          const float x1 = acc[i][j][v], x2 = acc[i][j + C::FN / 2][v];
-          const int pair = pbase + j * 32;
-          if (EPI == EPI_SWIGLU) {
-            const int F = a.Nv / 2;
-            ((T*)a.out0)[(size_t)m * F + pair] = from_f32<T>(silu_f(x1) * x2);
-          } else {
-            const int hd = a.d / 2, hh = a.Dh / 2;
-            const int mat = pair / hd, gp = pair % hd;
-            const int jj = gp % hh;
-            const int col = (gp / hh) * a.Dh + jj;
-            float y1 = x1, y2 = x2;
-            if (mat < 2) {
-              const float2 cs = *(const float2*)(a.rope + ((size_t)s_pos[lr] * hh + jj) * 2);
-              y1 = x1 * cs.x - x2 * cs.y;
-              y2 = x2 * cs.x + x1 * cs.y;
-            }
-            T* dst;
-            if (mat == 0) dst = (T*)a.out0 + (size_t)m * a.d;
-            else dst = (T*)(mat == 1 ? a.out1 : a.out2) + (size_t)s_glob[lr] * a.d;
-            dst[col] = from_f32<T>(y1);
-            dst[col + hh] = from_f32<T>(y2);
-          }
+        for (int g = 0; g < NRD; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NM / NRD > 0 ? NM / NRD : 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  __syncthreads();   // every wave is done with the pipeline's LDS
+
+  // ---------------------------------------------------------------- epilogue
+  // The accumulators go through LDS (an fp32 tile, rows padded to BN+8 floats so
+  // that both half-waves of an MFMA store hit different banks), in row passes
+  // when the tile is larger than the pipeline's LDS; then every thread handles
+  // runs of 8 (4 for the residual) consecutive outputs with 16-byte accesses.
+  constexpr int LDW = BN + 8;
+  constexpr int SMEM = S * C::StageBytes;
+  constexpr int PR = (BM * LDW * 4 <= SMEM) ? BM : (BM / 2 * LDW * 4 <= SMEM) ? BM / 2 : (BM / 4 * LDW * 4 <= SMEM) ? BM / 4 : 32;
+  static_assert(PR >= 32 && PR % 32 == 0 && BM % PR == 0 && PR * LDW * 4 <= SMEM, "epilogue pass");
+  float* tile = (float*)smem;
+  for (int r_lo = 0; r_lo < BM; r_lo += PR) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int rb = wm * C::TM + i * 32 - r_lo;   // first tile row of this MFMA block in the pass
+      if (rb < 0 || rb >= PR) continue;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          tile[(rb + (v >> 2) * 8 + 4 * hl + (v & 3)) * LDW + wn * C::TN + j * 32 + l32] = acc[i][j][v];
+    }
+    __syncthreads();
+    epilogue_pass<T, EPI, BN, C::TN, LDW, PR>(a, tile, m0 + r_lo, n0);
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ dispatch
-struct TileCfg { int BM, BN; };
-
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S>
 static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int split) {
   const int MT = (a.M + BM - 1) / BM, NT = a.Nv / BN;
-  const int KI = a.K * (int)sizeof(T) / kRowBytes;
+  const int KI = a.K * (int)sizeof(T) / RB;
   const int kps = (KI + split - 1) / split;
   const int nsplit = (KI + kps - 1) / kps;
   GemmArgs b = a;
   b.split_k = nsplit;
   const dim3 grid(MT * NT, 1, nsplit), block(kGemmThreads);
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI_QKV>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI_RESID>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI_SWIGLU>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI_LOGITS>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_QKV>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_SWIGLU>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS>), grid, block, 0, s, b, MT, NT, kps); break;
   }
   return hipGetLastError();
 }
 
-// Tile shapes: 0 = 256x256 (wave 128x128), 1 = 128x128 (64x64), 2 = 128x64 (32x64, waves 4x1).
-static const TileCfg kCfgs[3] = {{256, 256}, {128, 128}, {128, 64}};
+// Tile shapes (all 4 waves; RB = k-tile row bytes; S = stages) and their
+// measured sustained rate per CU in multiply-adds per microsecond (bf16,
+// K = 4096 tiles on MI355X).  One workgroup per CU (LDS bound).
+struct TileCfg { int BM, BN, RB, S; float rate; };
+static const TileCfg kCfgs[6] = {
+    {256, 256, 64, 4, 2.40e6f},   // 0: wave tile 128x128
+    {128, 256, 128, 3, 2.10e6f},  // 1: wave tile 64x128
+    {256, 128, 128, 3, 1.85e6f},  // 2: wave tile 128x64
+    {128, 128, 128, 3, 1.30e6f},  // 3: wave tile 64x64
+    {128, 64, 128, 4, 1.25e6f},   // 4: waves 4x1, wave tile 32x64
+    {128, 64, 128, 6, 1.20e6f},   // 5: same, deeper pipeline for weight streaming
+};
+constexpr int kCUs = 256;
+constexpr float kStreamBytesPerUs = 5.5e6f;   // sustained weight streaming, bytes/us
+constexpr float kAtomicBytesPerUs = 2.0e6f;   // fp32 atomic adds of split-K partials
 
-static int pick_cfg(const GemmArgs& a) {
-  // largest tile that still gives >= 256 workgroups; else the one with the most tiles
-  int best = -1;
-  for (int c = 0; c < 3; ++c) {
-    if (a.Nv % kCfgs[c].BN) continue;
-    const long tiles = (long)((a.M + kCfgs[c].BM - 1) / kCfgs[c].BM) * (a.Nv / kCfgs[c].BN);
-    if (tiles >= 256) return c;
-    best = c;
+// Estimated time of a launch: compute over full waves of tiles, or streaming
+// the weights (plus A re-reads) from HBM, whichever is longer; split-K adds its
+// atomic traffic.
+static float est_us(const GemmArgs& a, int eb, int c, int split) {
+  const TileCfg& g = kCfgs[c];
+  const long MT = (a.M + g.BM - 1) / g.BM, NT = a.Nv / g.BN;
+  const long blocks = MT * NT * split;
+  const long waves = (blocks + kCUs - 1) / kCUs;
+  const float comp = (float)waves * g.BM * g.BN * ((float)a.K / split) / g.rate;
+  const float conc = blocks < kCUs ? (float)blocks / kCUs : 1.f;
+  const float bytes = (float)a.Nv * a.K * eb + (float)MT * 0 + (float)NT * a.M * a.K * eb * 0.25f;
+  const float mem = bytes / (kStreamBytesPerUs * conc);
+  const float atom = split > 1 ? (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs : 0.f;
+  return (comp > mem ? comp : mem) + atom;
+}
+
+static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& split) {
+  float best = 3.4e38f;
+  cfg = -1; split = 1;
+  for (int c = 0; c < 6; ++c) {
+    const TileCfg& g = kCfgs[c];
+    if (a.Nv % g.BN || (a.K * eb) % g.RB) continue;
+    const int KI = a.K * eb / g.RB;
+    for (int sp = 1; sp <= 8; sp *= 2) {
+      if (sp > 1 && (epi != EPI_RESID || KI / sp < 8)) break;
+      const float t = est_us(a, eb, c, sp);
+      if (t < best) { best = t; cfg = c; split = sp; }
+    }
   }
-  return best;
 }
 
 int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh) {
   const int eb = dtype == 0 ? 2 : 4;
-  if ((K * eb) % kRowBytes) return 0;
-  if (Nv % 64) return 0;
+  if ((K * eb) % 128) return 0;   // every config then has a valid k-tile
+  if (Nv % 64) return 0;          // config 4 then tiles the columns
   if (epi == EPI_QKV && (d % 128 || Dh % 2)) return 0;
   return 1;
 }
 
 template <typename T>
 static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
-  const int c = pick_cfg(a);
-  if (c < 0) return hipErrorInvalidValue;
-  const int BM = kCfgs[c].BM, BN = kCfgs[c].BN;
-  const long tiles = (long)((a.M + BM - 1) / BM) * (a.Nv / BN);
-  int split = 1;
-  if (epi == EPI_RESID) {
-    const int KI = a.K * (int)sizeof(T) / kRowBytes;
-    while (tiles * split * 2 <= 512 && KI / (split * 2) >= 8) split *= 2;
+  int c, split;
+  pick_cfg(a, epi, (int)sizeof(T), c, split);
+  switch (c) {
+    case 0: return run_cfg<T, 256, 256, 2, 2, 64, 4>(epi, a, s, split);
+    case 1: return run_cfg<T, 128, 256, 2, 2, 128, 3>(epi, a, s, split);
+    case 2: return run_cfg<T, 256, 128, 2, 2, 128, 3>(epi, a, s, split);
+    case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3>(epi, a, s, split);
+    case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4>(epi, a, s, split);
+    case 5: return run_cfg<T, 128, 64, 4, 1, 128, 6>(epi, a, s, split);
   }
-  if (c == 0) return run_cfg<T, 256, 256, 2, 2>(epi, a, s, split);
-  if (c == 1) return run_cfg<T, 128, 128, 2, 2>(epi, a, s, split);
-  return run_cfg<T, 128, 64, 4, 1>(epi, a, s, split);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s) {
