@@ -46,6 +46,10 @@ template <> struct Chunk<float> {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming read of data used once (non-temporal hint: do not keep it in the caches).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // ------------------------------------------------------------------ MFMA traits
 // A 16-byte fragment per lane per operand.  For bf16 one fragment feeds one
@@ -98,6 +102,48 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// DPP wave primitives (no LDS round trip).  Within each row of 16 lanes the
+// row_shr:1,2,4,8 steps form an inclusive scan; row_bcast:15 then adds row 0's
+// (row 2's) total to row 1 (row 3), and row_bcast:31 adds lane 31's running
+// total to rows 2 and 3.  Lanes whose source lies outside the row keep `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<kRowShr1, 0xf>(0, v);
+  v += dpp_i<kRowShr2, 0xf>(0, v);
+  v += dpp_i<kRowShr4, 0xf>(0, v);
+  v += dpp_i<kRowShr8, 0xf>(0, v);
+  v += dpp_i<kRowBcast15, 0xa>(0, v);
+  v += dpp_i<kRowBcast31, 0xc>(0, v);
+  return v;
+}
+// Minimum / maximum over the 64 lanes, returned to every lane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const int id = (int)0xffffffffu;
+  v = min(v, (uint32_t)dpp_i<kRowShr1, 0xf>(id, (int)v));
+  v = min(v, (uint32_t)dpp_i<kRowShr2, 0xf>(id, (int)v));
+  v = min(v, (uint32_t)dpp_i<kRowShr4, 0xf>(id, (int)v));
+  v = min(v, (uint32_t)dpp_i<kRowShr8, 0xf>(id, (int)v));
+  v = min(v, (uint32_t)dpp_i<kRowBcast15, 0xa>(id, (int)v));
+  v = min(v, (uint32_t)dpp_i<kRowBcast31, 0xc>(id, (int)v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kRowShr1, 0xf>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kRowShr2, 0xf>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kRowShr4, 0xf>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kRowShr8, 0xf>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kRowBcast15, 0xa>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kRowBcast31, 0xc>(0, (int)v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Row of a compact active list -> its sequence: largest b with act_off[b] <= m.

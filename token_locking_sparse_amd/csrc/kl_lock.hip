@@ -22,37 +22,62 @@ constexpr int kPartWords = 8;
 constexpr int kTailThreads = 1024;
 
 // ------------------------------------------------------------------ compaction
-// Ascending positions with locked == 0 of B sequences of N, written with the
-// whole workgroup: per round every thread tests one position, a wave ballot and
-// mbcnt give the rank inside the wave, and the per-wave counts are prefix-summed
-// through LDS.  s_w: LDS scratch of blockDim/64 ints.
+// Ascending positions with locked == 0 of B sequences of N.  Every thread tests
+// 16 consecutive positions (one 16-byte load of the mask), the per-thread
+// counts are prefix-summed across the workgroup (wave shuffle scan, then the
+// wave totals through LDS), and each thread writes its run of active
+// positions.  s_w: LDS scratch of blockDim/64 ints.
+constexpr int kCompactPer = 16;
+
+__device__ __forceinline__ int block_excl_scan(int c, int& total, int* s_w) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
+  const int inc = wave_incl_scan(c);
+  if (lane == 63) s_w[wid] = inc;
+  __syncthreads();
+  int wpre = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = s_w[w];
+    wpre += (w < wid) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();   // s_w is reused by the next round
+  total = tot;
+  return wpre + inc - c;
+}
+
 __device__ void block_compact(const uint8_t* locked, int B, int N, int32_t* act_idx,
                               int32_t* act_off, int* s_w) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x;
   const int total = B * N;
+  const bool aligned = ((uintptr_t)locked & 15) == 0;
   int base = 0;
-  for (int r0 = 0; r0 < total; r0 += blockDim.x) {
-    const int i = r0 + tid;
-    const bool act = (i < total) && (locked[i] == 0);
-    const uint64_t bal = __ballot(act);
-    const int lane_pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (lane == 0) s_w[wid] = __popcll(bal);
-    __syncthreads();
-    int wpre = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int c = s_w[w];
-      wpre += (w < wid) ? c : 0;
-      tot += c;
+  for (int r0 = 0; r0 < total; r0 += kCompactPer * blockDim.x) {
+    const int i0 = r0 + kCompactPer * tid;
+    uint32_t w[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // past the end: locked
+    if (aligned && i0 + kCompactPer <= total) {
+      const u32x4 v = ld16(locked + i0);
+      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    } else {
+      for (int j = 0; j < kCompactPer; ++j) {
+        const uint32_t x = (i0 + j < total) ? (uint32_t)locked[i0 + j] : 0xffu;
+        w[j >> 2] = (w[j >> 2] & ~(0xffu << (8 * (j & 3)))) | (x << (8 * (j & 3)));
+      }
     }
-    const int pos = base + wpre + lane_pre;
-    if (i < total) {
-      const int q = i / N, rr = i - q * N;
-      if (act) act_idx[pos] = rr;
-      if (rr == 0) act_off[q] = pos;
+    uint32_t am = 0;   // bit j: position i0 + j is active
+#pragma unroll
+    for (int j = 0; j < kCompactPer; ++j)
+      am |= (((w[j >> 2] >> (8 * (j & 3))) & 0xffu) == 0u ? 1u : 0u) << j;
+    int tot;
+    int pos = base + block_excl_scan(__popc(am), tot, s_w);
+    if (i0 < total) {
+      int q = i0 / N, rr = i0 - q * N;
+      for (int j = 0; j < kCompactPer && i0 + j < total; ++j) {
+        if (rr == 0) act_off[q] = pos;
+        if ((am >> j) & 1u) act_idx[pos++] = rr;
+        if (++rr == N) { rr = 0; ++q; }
+      }
     }
     base += tot;
-    __syncthreads();
   }
   if (tid == 0) act_off[B] = base;
 }
@@ -72,84 +97,179 @@ hipError_t launch_compact(const uint8_t* locked, int B, int N, int32_t* act_idx,
 // ------------------------------------------------------------------ tail
 struct TailShared {
   int w[16];
-  uint32_t hist[256];
-  int sel[2];
+  uint32_t hist[3][256];   // radix-select histograms, used round-robin
+  uint32_t mm[32];         // per-wave min / max of the select's values
   float fv[16];
   int iv[32];
 };
 
-// k-th smallest (0-based) of the non-negative floats u[o0..o1), exact, by a
-// 4-pass 8-bit radix select on their bit patterns (monotone for x >= 0).
-__device__ float block_select_kth(const float* u, int o0, int o1, int k, TailShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  uint32_t prefix = 0, pmask = 0;
-  int kk = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
-    __syncthreads();
+// Up to kRegSel values of a sequence per thread are held in registers; longer
+// sequences are read from global memory on every pass.
+constexpr int kRegSel = 4;
+constexpr uint32_t kNoValue = 0xffffffffu;   // not a non-negative float's pattern
+
+// One 8-bit digit of the radix select, run by every wave on the complete
+// histogram h: find the bucket holding the kk-th value, extend the prefix and
+// rebase kk.  All waves reach the same answer, so nothing is broadcast.
+__device__ __forceinline__ void radix_digit(const uint32_t* h, int& kk, int shift, uint32_t& prefix,
+                                            uint32_t& pmask) {
+  const int lane = threadIdx.x & 63;
+  int c[4], ls = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { c[j] = (int)h[4 * lane + j]; ls += c[j]; }
+  const int inc = wave_incl_scan(ls);
+  const int ex = inc - ls;
+  const bool mine = ex <= kk && kk < inc;   // exactly one lane
+  int run = ex, j = 0;
+  if (mine)
+    while (j < 3 && run + c[j] <= kk) { run += c[j]; ++j; }
+  const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+  const int bucket = __builtin_amdgcn_readlane(4 * lane + j, src);
+  const int rem = __builtin_amdgcn_readlane(kk - run, src);
+  prefix |= ((uint32_t)bucket) << shift;
+  pmask |= 255u << shift;
+  kk = rem;
+}
+
+// k-th smallest (0-based) of non-negative floats, exact, by a radix select on
+// their bit patterns (monotone for x >= 0).  The values are either v[]
+// (kNoValue = absent) or, when from_regs is false, u[o0..o1).  The high bits
+// shared by the smallest and largest value are fixed first, so the 8-bit
+// digit passes start at the first bit where the values differ (this also
+// spreads the first histogram when the values cluster, as 1 - max p does).
+// One barrier per pass: pass q counts into hist[q % 3] while clearing
+// hist[(q + 1) % 3], whose last readers finished before the previous barrier.
+__device__ float block_select_kth(const uint32_t (&v)[kRegSel], bool from_regs, const float* u, int o0,
+                                  int o1, int k, TailShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
+  __syncthreads();   // earlier readers of sh.hist / sh.mm are done
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  if (from_regs) {
+#pragma unroll
+    for (int i = 0; i < kRegSel; ++i)
+      if (v[i] != kNoValue) { lo = min(lo, v[i]); hi = max(hi, v[i]); }
+  } else {
     for (int m = o0 + tid; m < o1; m += blockDim.x) {
-      const uint32_t v = __float_as_uint(u[m]);
-      if ((v & pmask) == prefix) atomicAdd(&sh.hist[(v >> shift) & 255u], 1u);
+      const uint32_t x = __float_as_uint(u[m]);
+      lo = min(lo, x); hi = max(hi, x);
     }
-    __syncthreads();
-    if (tid < 64) {
-      int c[4], ls = 0;
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) { sh.mm[wid] = lo; sh.mm[16 + wid] = hi; }
+  for (int i = tid; i < 256; i += blockDim.x) sh.hist[0][i] = 0;
+  __syncthreads();
+  lo = 0xffffffffu; hi = 0u;
+  for (int w = 0; w < nw; ++w) { lo = min(lo, sh.mm[w]); hi = max(hi, sh.mm[16 + w]); }
+  if (lo == hi) return __uint_as_float(lo);
+  const int free_bits = 32 - __clz((int)(lo ^ hi));   // bits below the shared prefix
+  uint32_t pmask = free_bits >= 32 ? 0u : ~((1u << free_bits) - 1u);
+  uint32_t prefix = lo & pmask;
+  int kk = k;
+  int shift = free_bits > 8 ? free_bits - 8 : 0;
+  for (int q = 0;; ++q) {
+    uint32_t* h = sh.hist[q % 3];
+    if (from_regs) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = (int)sh.hist[4 * lane + j]; ls += c[j]; }
-      int inc = ls;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += t;
+      for (int i = 0; i < kRegSel; ++i) {
+        bool act = v[i] != kNoValue && (v[i] & pmask) == prefix;
+        const uint32_t d = (v[i] >> shift) & 255u;
+        // lanes sharing the first active lane's digit add once (values cluster)
+        const unsigned long long m = __ballot(act);
+        if (m != 0ull) {
+          const int leader = __ffsll(m) - 1;
+          const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+          const unsigned long long same = __ballot(act && d == dl);
+          if (lane == leader) atomicAdd(&h[dl], (uint32_t)__popcll(same));
+          act = act && d != dl;
+        }
+        if (act) atomicAdd(&h[d], 1u);
       }
-      int ex = inc - ls;
-      if (ex <= kk && kk < inc) {
-        int run = ex, j = 0;
-        while (run + c[j] <= kk) { run += c[j]; ++j; }
-        sh.sel[0] = 4 * lane + j;
-        sh.sel[1] = kk - run;
+    } else {
+      for (int m = o0 + tid; m < o1; m += blockDim.x) {
+        const uint32_t x = __float_as_uint(u[m]);
+        if ((x & pmask) == prefix) atomicAdd(&h[(x >> shift) & 255u], 1u);
       }
     }
+    for (int i = tid; i < 256; i += blockDim.x) sh.hist[(q + 1) % 3][i] = 0;
     __syncthreads();
-    prefix |= ((uint32_t)sh.sel[0]) << shift;
-    pmask |= 255u << shift;
-    kk = sh.sel[1];
-    __syncthreads();
+    radix_digit(h, kk, shift, prefix, pmask);
+    if (shift == 0) break;
+    shift = shift > 8 ? shift - 8 : 0;
   }
   return __uint_as_float(prefix);
 }
 
 // Gate quantile, lock update, optional sampler, compaction — one workgroup.
+// A sequence of at most kRegSel * blockDim active rows is read once into
+// registers (positions, u, KL, then the candidate flags) and its select and
+// lock update run from there.
 __device__ void tail_phase(const TailParams& p, TailShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
+  const int bd = blockDim.x;
   const bool gate = p.gate_q >= 0.f;
   const bool can_lock = p.eps > 0.f && p.have_prev;
   for (int b = 0; b < p.B; ++b) {
     const int o0 = p.act_off[b], o1 = p.act_off[b + 1];
     const int n = o1 - o0;
+    const bool regs = n <= kRegSel * bd;
+    uint32_t uv[kRegSel];
+    float kv[kRegSel];
+    int pv[kRegSel];
+#pragma unroll
+    for (int i = 0; i < kRegSel; ++i) {
+      const int m = o0 + tid + i * bd;
+      const bool in = regs && m < o1;
+      uv[i] = in ? __float_as_uint(p.u[m]) : kNoValue;
+      kv[i] = in ? p.kl[m] : INFINITY;
+      pv[i] = in ? p.act_idx[m] : -1;
+    }
     float thr = INFINITY;
     if (gate && n > 0) {
       const int k = (int)floor((double)p.gate_q * (double)(n - 1));
-      thr = block_select_kth(p.u, o0, o1, k, sh);
+      thr = block_select_kth(uv, regs, p.u, o0, o1, k, sh);
     }
     if (tid == 0 && p.gate_thr) p.gate_thr[b] = thr;
     if (can_lock) {
-      for (int m = o0 + tid; m < o1; m += blockDim.x) {
-        const int64_t g = (int64_t)b * p.N + p.act_idx[m];
-        bool ok = (p.cand == nullptr) || (p.cand[g] != 0);
-        ok = ok && (p.kl[m] <= p.eps);
-        if (gate) ok = ok && (p.u[m] <= thr);
-        if (ok) {
-          p.locked[g] = 1;
-          if (p.lock_step) p.lock_step[g] = p.t;
+      const int64_t gb = (int64_t)b * p.N;
+      if (regs) {
+        bool ok[kRegSel];
+#pragma unroll
+        for (int i = 0; i < kRegSel; ++i) {
+          ok[i] = pv[i] >= 0 && kv[i] <= p.eps;
+          if (gate) ok[i] = ok[i] && (__uint_as_float(uv[i]) <= thr);
+        }
+        if (p.cand) {
+#pragma unroll
+          for (int i = 0; i < kRegSel; ++i) ok[i] = ok[i] && (p.cand[gb + (ok[i] ? pv[i] : 0)] != 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kRegSel; ++i) {
+          if (ok[i]) {
+            p.locked[gb + pv[i]] = 1;
+            if (p.lock_step) p.lock_step[gb + pv[i]] = p.t;
+          }
+        }
+      } else {
+        for (int m = o0 + tid; m < o1; m += bd) {
+          const int64_t g = gb + p.act_idx[m];
+          bool ok = (p.cand == nullptr) || (p.cand[g] != 0);
+          ok = ok && (p.kl[m] <= p.eps);
+          if (gate) ok = ok && (p.u[m] <= thr);
+          if (ok) {
+            p.locked[g] = 1;
+            if (p.lock_step) p.lock_step[g] = p.t;
+          }
         }
       }
     }
     // Sampler: the unmask_k most confident [MASK] positions take their argmax.
+    // It runs after the lock update, which reads the candidate flags it sets.
+    __syncthreads();
     for (int r = 0; r < p.unmask_k; ++r) {
       float bc = -1.f;
       int bp = INT_MAX, bm = -1;
-      for (int m = o0 + tid; m < o1; m += blockDim.x) {
+      for (int m = o0 + tid; m < o1; m += bd) {
         const int pos = p.act_idx[m];
         const int64_t g = (int64_t)b * p.N + pos;
         if (p.tok[g] != p.mask_id) continue;
@@ -209,35 +329,88 @@ __device__ __forceinline__ Part combine(const Part& x, const Part& y) {
   return r;
 }
 
-__device__ __forceinline__ Part shfl_part(const Part& x, int o) {
-  Part r;
-  r.ma = __shfl_xor(x.ma, o, 64); r.sa = __shfl_xor(x.sa, o, 64); r.ta = __shfl_xor(x.ta, o, 64);
-  r.mb = __shfl_xor(x.mb, o, 64); r.sb = __shfl_xor(x.sb, o, 64);
-  r.best = __shfl_xor(x.best, o, 64); r.bidx = __shfl_xor(x.bidx, o, 64);
-  return r;
+// Lane (l - shift) within the row of 16, or the identity partial where that
+// lane lies outside the row / the row is masked off (DPP, no LDS round trip).
+template <int CTRL, int RM>
+__device__ __forceinline__ Part dpp_part(const Part& x) {
+  const int ninf = __float_as_int(-INFINITY);
+  Part y;
+  y.ma = __int_as_float(dpp_i<CTRL, RM>(ninf, __float_as_int(x.ma)));
+  y.sa = __int_as_float(dpp_i<CTRL, RM>(0, __float_as_int(x.sa)));
+  y.ta = __int_as_float(dpp_i<CTRL, RM>(0, __float_as_int(x.ta)));
+  y.mb = __int_as_float(dpp_i<CTRL, RM>(ninf, __float_as_int(x.mb)));
+  y.sb = __int_as_float(dpp_i<CTRL, RM>(0, __float_as_int(x.sb)));
+  y.best = __int_as_float(dpp_i<CTRL, RM>(ninf, __float_as_int(x.best)));
+  y.bidx = dpp_i<CTRL, RM>(INT_MAX, x.bidx);
+  return y;
 }
 
-// Row statistics from a (combined) partial: with S_a = sum e^(a - max a),
-// A = max a + ln S_a, max p = 1/S_a, KL = sum p (a - b) - A + B.
-template <typename T, bool PREV>
-__device__ void finish_row(const KLRowParams& rp, const Part& t, const char* crow, int C, int mask_id, int r) {
+// Combine the partials of the 64 lanes (the same steps as wave_incl_scan);
+// lane 63 ends with the wave's total, which is returned to every lane.
+__device__ __forceinline__ Part wave_reduce_part(Part p) {
+  p = combine(p, dpp_part<kRowShr1, 0xf>(p));
+  p = combine(p, dpp_part<kRowShr2, 0xf>(p));
+  p = combine(p, dpp_part<kRowShr4, 0xf>(p));
+  p = combine(p, dpp_part<kRowShr8, 0xf>(p));
+  p = combine(p, dpp_part<kRowBcast15, 0xa>(p));
+  p = combine(p, dpp_part<kRowBcast31, 0xc>(p));
+  Part t;
+  t.ma = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.ma), 63));
+  t.sa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.sa), 63));
+  t.ta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.ta), 63));
+  t.mb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.mb), 63));
+  t.sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.sb), 63));
+  t.best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.best), 63));
+  t.bidx = __builtin_amdgcn_readlane(p.bidx, 63);
+  return t;
+}
+
+// Exact argmax inside the 16-byte chunk `c` whose raw bits are `raw`: the
+// lowest id equal to `best` that is not the mask, or INT_MAX when c < 0 (no
+// finite maximum was seen).
+template <typename T>
+__device__ __forceinline__ int resolve_argmax(const u32x4& raw, int c, float best, int mask_id) {
   constexpr int E = Chunk<T>::kElems;
+  if (c < 0 || c == INT_MAX) return INT_MAX;
+  float a[E];
+  Chunk<T>::unpack(raw, a);
+  int am = INT_MAX;
+#pragma unroll
+  for (int j = E - 1; j >= 0; --j)
+    if (a[j] == best && c * E + j != mask_id) am = c * E + j;
+  return am;
+}
+
+// Row statistics from a (combined) partial whose `bidx` is the exact argmax
+// (INT_MAX: none): with S_a = sum e^(a - max a), A = max a + ln S_a,
+// max p = 1/S_a, KL = sum p (a - b) - A + B.
+template <bool PREV>
+__device__ void finish_row(const KLRowParams& rp, const Part& t, int r) {
   const float A = t.ma + logf(t.sa);
   rp.lse[r] = A;
   rp.u[r] = 1.f - 1.f / t.sa;
   if (PREV) rp.kl[r] = t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb);
   else rp.kl[r] = INFINITY;
-  // exact argmax inside the winning chunk (lowest id equal to the max, not the mask)
-  int am = 0;
-  if (t.bidx >= 0 && t.bidx < C) {   // always true for finite logits
-    float a[E];
-    Chunk<T>::unpack(ld16(crow + (size_t)t.bidx * 16), a);
-    am = t.bidx * E;
-    for (int j = E - 1; j >= 0; --j)
-      if (a[j] == t.best && t.bidx * E + j != mask_id) am = t.bidx * E + j;
-  }
-  if (rp.argmax) rp.argmax[r] = am;
+  if (rp.argmax) rp.argmax[r] = t.bidx == INT_MAX ? 0 : t.bidx;
   if (rp.conf) rp.conf[r] = __expf(t.best - t.ma) / t.sa;
+}
+
+// Segment partials: 8 words per (segment, row), segment-major, so the tail
+// reads one segment of consecutive rows with consecutive lanes.
+__device__ __forceinline__ void store_part(float* pp, const Part& t) {
+  f32x4 x0, x1;
+  x0[0] = t.ma; x0[1] = t.sa; x0[2] = t.ta; x0[3] = t.mb;
+  x1[0] = t.sb; x1[1] = t.best; x1[2] = __int_as_float(t.bidx); x1[3] = 0.f;
+  reinterpret_cast<f32x4*>(pp)[0] = x0;
+  reinterpret_cast<f32x4*>(pp)[1] = x1;
+}
+__device__ __forceinline__ Part load_part(const float* pp) {
+  const f32x4 x0 = reinterpret_cast<const f32x4*>(pp)[0];
+  const f32x4 x1 = reinterpret_cast<const f32x4*>(pp)[1];
+  Part t;
+  t.ma = x0[0]; t.sa = x0[1]; t.ta = x0[2]; t.mb = x0[3];
+  t.sb = x1[0]; t.best = x1[1]; t.bidx = __float_as_int(x1[2]);
+  return t;
 }
 
 // Row pass: workgroup (row r, segment) streams its slice of the current and
@@ -260,29 +433,99 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
   const int c0 = seg * seg_chunks;
   const int c1 = min(C, c0 + seg_chunks);
   const int mask_id = tp.mask_id;
+  // chunk holding the [MASK] id (never matches when there is none): it is left
+  // out of the argmax tracking in the streaming loops and folded in afterwards
+  const int mask_chunk = mask_id >= 0 ? mask_id / E : -1;
 
   Part acc;
   acc.ma = -INFINITY; acc.sa = 0.f; acc.ta = 0.f;
   acc.mb = -INFINITY; acc.sb = 0.f;
   acc.best = -INFINITY; acc.bidx = INT_MAX;
 
-  for (int c = c0 + tid; c < c1; c += kKLThreads) {
+  // Groups of U chunks per thread (strided by the workgroup size, so every load
+  // instruction of the workgroup covers a contiguous 4 KB): U loads of each row
+  // in flight, one running-max rescale per group.
+  constexpr int U = 4;
+  u32x4 braw = {0u, 0u, 0u, 0u};   // raw bits of chunk acc.bidx
+  int c = c0 + tid;
+  for (; c + (U - 1) * kKLThreads < c1; c += U * kKLThreads) {
+    u32x4 ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ra[u] = ld16_stream(crow + (uint32_t)(c + u * kKLThreads) * 16u);
+    if (PREV) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) rb[u] = ld16_stream(prow + (uint32_t)(c + u * kKLThreads) * 16u);
+    }
+    float a[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) Chunk<T>::unpack(ra[u], a[u]);
+    float cm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cm[u] = a[u][0];
+#pragma unroll
+      for (int j = 1; j < E; ++j) cm[u] = __builtin_fmaxf(cm[u], a[u][j]);
+    }
+    const float gm = __builtin_fmaxf(__builtin_fmaxf(cm[0], cm[1]), __builtin_fmaxf(cm[2], cm[3]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // selects, not branches; lowest chunk wins ties
+      const float cx = (c + u * kKLThreads == mask_chunk) ? -INFINITY : cm[u];
+      const bool gt = cx > acc.best;
+      acc.bidx = gt ? c + u * kKLThreads : acc.bidx;
+      acc.best = gt ? cx : acc.best;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) braw[q] = gt ? ra[u][q] : braw[q];
+    }
+    const float mnew = __builtin_fmaxf(acc.ma, gm);
+    const float sc = scale_to(acc.ma, mnew);
+    acc.sa *= sc;
+    acc.ta *= sc;
+    acc.ma = mnew;
+    const float ml = mnew * kLog2e;
+    if (PREV) {
+      float b[U][E];
+#pragma unroll
+      for (int u = 0; u < U; ++u) Chunk<T>::unpack(rb[u], b[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(a[u][j], kLog2e, -ml));
+          acc.sa += e;
+          acc.ta = fmaf(e, a[u][j] - b[u][j], acc.ta);
+        }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E; ++j) bm = __builtin_fmaxf(bm, b[u][j]);
+      const float mbn = __builtin_fmaxf(acc.mb, bm);
+      acc.sb *= scale_to(acc.mb, mbn);
+      acc.mb = mbn;
+      const float mbl = mbn * kLog2e;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(b[u][j], kLog2e, -mbl));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc.sa += __builtin_amdgcn_exp2f(fmaf(a[u][j], kLog2e, -ml));
+    }
+  }
+  // remaining chunks one at a time
+  for (; c < c1; c += kKLThreads) {
     float a[E], bb[E];
-    Chunk<T>::unpack(ld16(crow + (size_t)c * 16), a);
-    if (PREV) Chunk<T>::unpack(ld16(prow + (size_t)c * 16), bb);
+    const u32x4 rc = ld16_stream(crow + (uint32_t)c * 16u);
+    Chunk<T>::unpack(rc, a);
+    if (PREV) Chunk<T>::unpack(ld16_stream(prow + (uint32_t)c * 16u), bb);
     float cm = a[0];
 #pragma unroll
-    for (int j = 1; j < E; ++j) cm = fmaxf(cm, a[j]);
-    float cmn = cm;
-    const int e0 = c * E;
-    if ((unsigned)(mask_id - e0) < (unsigned)E) {
-      cmn = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e0 + j != mask_id) cmn = fmaxf(cmn, a[j]);
-    }
-    if (cmn > acc.best) { acc.best = cmn; acc.bidx = c; }
-    const float mnew = fmaxf(acc.ma, cm);
+    for (int j = 1; j < E; ++j) cm = __builtin_fmaxf(cm, a[j]);
+    const float cx = (c == mask_chunk) ? -INFINITY : cm;
+    if (cx > acc.best) { acc.best = cx; acc.bidx = c; braw = rc; }
+    const float mnew = __builtin_fmaxf(acc.ma, cm);
     const float sc = scale_to(acc.ma, mnew);
     acc.sa *= sc;
     acc.ta *= sc;
@@ -297,8 +540,8 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
     if (PREV) {
       float bm = bb[0];
 #pragma unroll
-      for (int j = 1; j < E; ++j) bm = fmaxf(bm, bb[j]);
-      const float mbn = fmaxf(acc.mb, bm);
+      for (int j = 1; j < E; ++j) bm = __builtin_fmaxf(bm, bb[j]);
+      const float mbn = __builtin_fmaxf(acc.mb, bm);
       acc.sb *= scale_to(acc.mb, mbn);
       acc.mb = mbn;
       const float mbl = mbn * kLog2e;
@@ -306,47 +549,61 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
       for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(bb[j], kLog2e, -mbl));
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc = combine(acc, shfl_part(acc, o));
+  // the [MASK] chunk, if this thread streamed it: best over its other ids
+  if (mask_chunk >= c0 && mask_chunk < c1 && (mask_chunk - c0) % kKLThreads == tid) {
+    float a[E];
+    const u32x4 rm = ld16(crow + (size_t)mask_chunk * 16);
+    Chunk<T>::unpack(rm, a);
+    float cmn = -INFINITY;
+    for (int j = 0; j < E; ++j)
+      if (mask_chunk * E + j != mask_id) cmn = __builtin_fmaxf(cmn, a[j]);
+    if (cmn > acc.best || (cmn == acc.best && mask_chunk < acc.bidx)) {
+      acc.best = cmn; acc.bidx = mask_chunk; braw = rm;
+    }
+  }
+  acc.bidx = resolve_argmax<T>(braw, acc.bidx, acc.best, mask_id);   // chunk -> exact id
+  acc = wave_reduce_part(acc);
   if (lane == 0) s_part[wid] = acc;
   __syncthreads();
   if (tid == 0) {
     Part t = s_part[0];
     for (int w = 1; w < kKLThreads / 64; ++w) t = combine(t, s_part[w]);
-    if (n_seg == 1) {
-      finish_row<T, PREV>(rp, t, crow, C, mask_id, r);
-    } else {
-      float* pp = part + ((size_t)r * n_seg + seg) * kPartWords;
-      pp[0] = t.ma; pp[1] = t.sa; pp[2] = t.ta; pp[3] = t.mb; pp[4] = t.sb; pp[5] = t.best;
-      pp[6] = __int_as_float(t.bidx);
-    }
+    if (n_seg == 1) finish_row<PREV>(rp, t, r);
+    else store_part(part + ((size_t)seg * tp.M_tot + r) * kPartWords, t);
   }
 }
 
 // Tail kernel (one workgroup): merge the segment partials of every row (when a
 // row was split), then gate quantile, lock update, sampler and compaction.
+// The merge takes kMergeRows rows per thread per round and issues every
+// partial load of the round before combining.
+constexpr int kMaxSeg = 4;
+constexpr int kMergeRows = 2;
+
 template <typename T, bool PREV>
 __global__ void __launch_bounds__(kTailThreads)
 kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   __shared__ TailShared sh;
-  if (n_seg > 1) {
-    const int C = rp.V / Chunk<T>::kElems;
-    const size_t rowbytes = (size_t)rp.V * sizeof(T);
-    for (int r = threadIdx.x; r < tp.M_tot; r += blockDim.x) {
-      const float* q = part + (size_t)r * n_seg * kPartWords;
-      Part x;
-      x.ma = q[0]; x.sa = q[1]; x.ta = q[2]; x.mb = q[3]; x.sb = q[4]; x.best = q[5];
-      x.bidx = __float_as_int(q[6]);
-      for (int s2 = 1; s2 < n_seg; ++s2) {
-        const float* qs = q + s2 * kPartWords;
-        Part y;
-        y.ma = qs[0]; y.sa = qs[1]; y.ta = qs[2]; y.mb = qs[3]; y.sb = qs[4]; y.best = qs[5];
-        y.bidx = __float_as_int(qs[6]);
-        x = combine(x, y);
+  if (n_seg > 1 && tp.M_tot > 0) {
+    const int bd = blockDim.x;
+    for (int r0 = 0; r0 < tp.M_tot; r0 += kMergeRows * bd) {
+      Part x[kMergeRows][kMaxSeg];
+#pragma unroll
+      for (int k = 0; k < kMergeRows; ++k) {
+        const int r = min(r0 + (int)threadIdx.x + k * bd, tp.M_tot - 1);   // clamped: loads stay in bounds
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSeg; ++s2)
+          if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * tp.M_tot + r) * kPartWords);
       }
-      const int b = seq_of_row(tp.act_off, tp.B, r);
-      const int64_t g = (int64_t)b * tp.N + tp.act_idx[r];
-      finish_row<T, PREV>(rp, x, (const char*)rp.cur + g * rowbytes, C, tp.mask_id, r);
+#pragma unroll
+      for (int k = 0; k < kMergeRows; ++k) {
+        Part t = x[k][0];
+#pragma unroll
+        for (int s2 = 1; s2 < kMaxSeg; ++s2)
+          if (s2 < n_seg) t = combine(t, x[k][s2]);
+        const int r = r0 + (int)threadIdx.x + k * bd;
+        if (r < tp.M_tot) finish_row<PREV>(rp, t, r);
+      }
     }
     __syncthreads();
   }
@@ -356,9 +613,10 @@ kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
 static int kl_nseg(int M_tot, int V, int elem_bytes) {
   const int C = V * elem_bytes / 16;
   if (M_tot <= 0) return 1;
-  const int want = (4096 + M_tot - 1) / M_tot;
+  const int want = (2048 + M_tot - 1) / M_tot;   // about 2048 workgroups or more
   const int maxseg = C / (kKLThreads * 4) > 1 ? C / (kKLThreads * 4) : 1;
   int n = want < maxseg ? want : maxseg;
+  n = n < kMaxSeg ? n : kMaxSeg;
   return n < 1 ? 1 : n;
 }
 
