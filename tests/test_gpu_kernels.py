@@ -192,6 +192,8 @@ ATTN_CASES = [
     # dtype, Dh, H, N, Ms
     ("bf16", 128, 2, 256, [256, 37]),
     ("bf16", 128, 3, 1024, [5]),          # few query tiles: split over keys + merge
+    ("bf16", 128, 8, 512, [300, 1, 77]),  # heads a multiple of 8 (XCD placement), ragged
+    ("bf16", 128, 16, 1024, [640]),       # several query tiles per head, no split
     ("bf16", 64, 2, 128, [1, 128, 70]),
     ("bf16", 32, 4, 64, [64]),
     ("f32", 32, 4, 64, [64, 3]),

@@ -74,9 +74,23 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
   constexpr int E = C::E;
   __shared__ __attribute__((aligned(16))) char smem[C::Smem];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.y, split = blockIdx.z;
+  // Flat grid of slots * H * nsplit workgroups.  Workgroups are dealt to the 8
+  // XCDs round-robin; when H % 8 == 0 every (slot, split) of a head is placed
+  // on the same XCD, so that head's K/V is fetched from HBM once per XCD and
+  // then served from that XCD's L2.
+  const int per_head = gridDim.x / H;   // slots * nsplit
+  int h, rest;
+  if ((H & 7) == 0) {
+    const int bid = blockIdx.x, xcd = bid & 7, k = bid >> 3;
+    h = xcd + 8 * (k / per_head);
+    rest = k % per_head;
+  } else {
+    h = blockIdx.x / per_head;
+    rest = blockIdx.x % per_head;
+  }
+  const int split = rest % nsplit, slot = rest / nsplit;
   int row0 = 0, row_end = 0;
-  const int b = find_tile(act_off, B, blockIdx.x, row0, row_end);
+  const int b = find_tile(act_off, B, slot, row0, row_end);
   if (b < 0) return;
   const int n_tiles_total = N / kBKV;
   const int t_begin = split * tiles_per_split;
@@ -297,6 +311,257 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
   }
 }
 
+// ------------------------------------------------------------------ bf16, Dh = 128
+// Same decomposition (4 waves x 32 queries, 64-key tiles, S^T = K Q^T, online
+// softmax per lane, O^T = V^T P^T), but K and V reach LDS by direct
+// global->LDS loads in their natural [key][d] layout, double-buffered with one
+// barrier per tile, and the V^T operand is read with the LDS transpose read
+// (ds_read_b64_tr_b16).  In each 16-lane group that instruction hands lane i,
+// element j, the (i % 4)-th 16-bit value read by lane 4 j + i / 4; so when lane
+// s of the group reads the 4 values V[kb + s / 4][d0 + 4 (s % 4) ...], lane i
+// receives V[kb .. kb + 3][d0 + i]: four consecutive keys of one column, as
+// the MFMA A operand wants.  Two such reads give a lane its 8 k-slots; their
+// key bases follow the key order of the S^T accumulator (lane half hl holds
+// keys 16 m + 4 hl + {0..3} and 16 m + 8 + 4 hl + {0..3} of k-step m), so P^T
+// goes from the score registers to the B operand unpermuted.
+// LDS layouts (row = one key, 16 chunks of 16 bytes): K chunk c at position
+// c ^ (row & 15) (conflict-free 16-byte fragment reads); V chunk c at position
+// c ^ 4 (row & 3), which spreads the 16 (row, chunk) pairs one half-wave of a
+// transpose read touches over the 16 positions.
+constexpr int kTrDh = 128;
+constexpr int kTrBKV = 64;                       // keys per tile
+constexpr int kTrS = 2;                          // LDS stages: loads run kTrS - 1 tiles ahead
+constexpr int kTrRB = kTrDh * 2;                 // bytes per key row
+constexpr int kTrTile = kTrBKV * kTrRB;          // 8 KB per K or V tile
+constexpr int kTrStage = 2 * kTrTile;
+constexpr int kTrEpi = 4 * 32 * (kTrDh + 1) * 4;
+constexpr int kTrSmem = (kTrS * kTrStage > kTrEpi) ? kTrS * kTrStage : kTrEpi;
+constexpr int kTrDma = kTrTile / (kAttnThreads * 16);   // direct loads per thread per K (or V) tile
+constexpr int kTrLoads = 2 * kTrDma;                   // per thread per tile (K and V)
+static_assert(kTrDma >= 1 && kBKV % kTrBKV == 0 && kTrBKV % 32 == 0, "tile split");
+static_assert((kTrS - 2) * kTrLoads < 16, "vmcnt immediate");
+
+typedef __attribute__((address_space(3))) void attn_lds_t;
+typedef __attribute__((address_space(1))) void attn_glb_t;
+typedef short attn_v4s __attribute__((ext_vector_type(4)));
+typedef attn_v4s __attribute__((address_space(3))) attn_lds_v4s;
+
+__device__ __forceinline__ int vswz(int row, int c) { return c ^ (4 * (row & 3)); }
+
+__device__ __forceinline__ uint2 lds_tr16(const char* p) {
+  const attn_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn_lds_v4s*)(attn_lds_t*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+               const int32_t* __restrict__ act_off, int B, int N, int H, float scale_log2, int nsplit,
+               int tiles_per_split, bf16* __restrict__ out, float* __restrict__ part_o,
+               float* __restrict__ part_ml, int M_tot) {
+  constexpr int Dh = kTrDh, E = 8, nKK = Dh / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[kTrSmem];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int per_head = gridDim.x / H;
+  int h, rest;
+  if ((H & 7) == 0) {   // all workgroups of a head on one XCD (see attn_kernel)
+    const int bid = blockIdx.x, xcd = bid & 7, k = bid >> 3;
+    h = xcd + 8 * (k / per_head);
+    rest = k % per_head;
+  } else {
+    h = blockIdx.x / per_head;
+    rest = blockIdx.x % per_head;
+  }
+  const int split = rest % nsplit, slot = rest / nsplit;
+  int row0 = 0, row_end = 0;
+  const int b = find_tile(act_off, B, slot, row0, row_end);
+  if (b < 0) return;
+  // the split plan counts 64-key tiles; this kernel walks 32-key tiles
+  constexpr int TR = kBKV / kTrBKV;
+  const int t_begin = split * tiles_per_split * TR;
+  const int t_end = min(N / kBKV, (split + 1) * tiles_per_split) * TR;
+  const int HD = H * Dh;
+
+  const int wrow0 = row0 + wid * 32;
+  const bool wave_live = wrow0 < row_end;
+  const int my_row = min(wrow0 + l32, row_end - 1);
+  u32x4 qf[nKK];
+  {
+    const char* qr = (const char*)(q + (size_t)my_row * HD + (size_t)h * Dh);
+#pragma unroll
+    for (int kk = 0; kk < nKK; ++kk) qf[kk] = ld16(qr + (2 * kk + hl) * 16);
+  }
+
+  // direct-load sources: load j of this wave fills LDS bytes [(4 j + wid) KB, +1 KB)
+  // of a tile = key rows 4 (4 j + wid) + lane / 16, stored position lane % 16
+  const size_t krow = (size_t)HD * 2;
+  const char* kb0 = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
+  const char* vb0 = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
+  uint32_t koff[kTrDma], voff[kTrDma];
+#pragma unroll
+  for (int j = 0; j < kTrDma; ++j) {
+    const int r = 4 * (4 * j + wid) + (lane >> 4), pos = lane & 15;
+    koff[j] = (uint32_t)(r * krow) + swz<kTrRB>(r, pos) * 16;
+    voff[j] = (uint32_t)(r * krow) + vswz(r, pos) * 16;
+  }
+  auto issue = [&](int tile, int stage) {
+    char* ks = smem + stage * kTrStage;
+    char* vs = ks + kTrTile;
+    const size_t t0 = (size_t)tile * kTrBKV * krow;
+#pragma unroll
+    for (int j = 0; j < kTrDma; ++j)
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(kb0 + t0 + koff[j]), (attn_lds_t*)(ks + (4 * j + wid) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kTrDma; ++j)
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(vb0 + t0 + voff[j]), (attn_lds_t*)(vs + (4 * j + wid) * 1024), 16, 0, 0);
+  };
+
+  // transpose-read offsets inside a V tile (per d-tile dt and k-step m add
+  // dt / m dependent terms): this lane of its 16-lane group reads key row
+  // kb + s / 4 at column d0 + 4 (s % 4)
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_dhalf = 16 * (g16 & 1);            // d0 within the 32-wide d-tile
+  const int tr_khalf = 4 * (g16 >> 1);            // 4 hl
+  f32x16 oacc[Dh / 32];
+#pragma unroll
+  for (int i = 0; i < Dh / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < kTrS - 1; ++i)
+    if (t_begin + i < t_end) issue(t_begin + i, i);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int stage = (t - t_begin) % kTrS;
+    // tile t has landed once at most the loads of the tiles after it are
+    // outstanding (2 K + 2 V loads per tile; older Q loads are done by then)
+    const int after = min(kTrS - 2, t_end - 1 - t);
+    if (kTrS >= 4 && after >= 2) __builtin_amdgcn_s_waitcnt(((2 * kTrLoads) & 15) | (7 << 4) | (15 << 8));
+    else if (kTrS >= 3 && after >= 1) __builtin_amdgcn_s_waitcnt((kTrLoads & 15) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();   // everyone's tile t landed; the stage of tile t - 1 is free
+    asm volatile("" ::: "memory");
+    if (t + kTrS - 1 < t_end) issue(t + kTrS - 1, (t + kTrS - 1 - t_begin) % kTrS);
+    if (!wave_live) continue;
+    const char* ks = smem + stage * kTrStage;
+    const char* vs = ks + kTrTile;
+    constexpr int NS = kTrBKV / 32;   // 32-key subtiles
+    f32x16 sc[NS];
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[sub][v] = 0.f;
+      const int kr = sub * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < nKK; ++kk) {
+        const u32x4 a = *(const u32x4*)(ks + kr * kTrRB + swz<kTrRB>(kr, 2 * kk + hl) * 16);
+        Mfma<bf16>::run(sc[sub], a, qf[kk]);
+      }
+    }
+    // Online softmax with a lazily moved reference: the row's reference m_run
+    // only moves when the tile max exceeds it by more than kLazy (log2 units),
+    // so P <= 2^kLazy and the accumulators are rescaled only on those tiles.
+    constexpr float kLazy = 8.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[sub][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    const bool move = mx > m_run + kLazy;          // also true on the first tile
+    const float m_new = move ? mx : m_run;
+    const float alpha = (move && m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    if (__ballot(move && m_run > -INFINITY)) {     // wave-uniform: rare after the first tiles
+#pragma unroll
+      for (int i = 0; i < Dh / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+    }
+    m_run = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[sub][v], scale_log2, -m_new));
+        sc[sub][v] = pv;
+        ls += pv;
+      }
+    l_run = l_run * alpha + ls;
+    // O^T += V^T P^T, k-step m covers keys 16 m .. 16 m + 15 of the tile
+#pragma unroll
+    for (int m = 0; m < kTrBKV / 16; ++m) {
+      const int sub = m >> 1, r0 = (m & 1) * 8;
+      u32x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = pack_bf16x2(sc[sub][r0 + 2 * i], sc[sub][r0 + 2 * i + 1]);
+      const int kr0 = 16 * m + tr_khalf + (s16 >> 2);   // key row of the first read
+      const int kr1 = kr0 + 8;
+#pragma unroll
+      for (int dt = 0; dt < Dh / 32; ++dt) {
+        const int d = 32 * dt + tr_dhalf + 4 * (s16 & 3);
+        const int c = d >> 3, cb = (d & 7) * 2;
+        const uint2 x0 = lds_tr16(vs + kr0 * kTrRB + vswz(kr0, c) * 16 + cb);
+        const uint2 x1 = lds_tr16(vs + kr1 * kTrRB + vswz(kr1, c) * 16 + cb);
+        u32x4 a;
+        a[0] = x0.x; a[1] = x0.y; a[2] = x1.x; a[3] = x1.y;
+        Mfma<bf16>::run(oacc[dt], a, pb);
+      }
+    }
+  }
+  __syncthreads();   // stages free for the epilogue staging
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const bool final_out = (nsplit == 1);
+  const float inv = (final_out && l_tot > 0.f) ? 1.f / l_tot : 1.f;
+  float* ep = (float*)smem + wid * 32 * (Dh + 1);
+#pragma unroll
+  for (int dt = 0; dt < Dh / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
+      ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
+    }
+  __syncthreads();
+  if (wave_live) {
+    const int nrow = min(32, row_end - wrow0);
+    if (final_out) {
+      constexpr int CPR = Dh / E;
+      for (int id = lane; id < 32 * CPR; id += 64) {
+        const int rr = id / CPR, c = id % CPR;
+        if (rr < nrow) {
+          const float* src = ep + rr * (Dh + 1) + c * E;
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16 lo = (bf16)src[2 * i], hi = (bf16)src[2 * i + 1];
+            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          st16((char*)(out + (size_t)(wrow0 + rr) * HD + (size_t)h * Dh) + c * 16, w);
+        }
+      }
+    } else {
+      constexpr int CPR = Dh / 4;
+      for (int id = lane; id < 32 * CPR; id += 64) {
+        const int rr = id / CPR, c = id % CPR;
+        if (rr < nrow) {
+          const float* src = ep + rr * (Dh + 1) + c * 4;
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(src[i]);
+          st16(part_o + (((size_t)split * M_tot + wrow0 + rr) * H + h) * Dh + c * 4, w);
+        }
+      }
+      if (hl == 0 && l32 < nrow) {
+        float* ml = part_ml + (((size_t)split * M_tot + wrow0 + l32) * H + h) * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+  }
+}
+
 // Merge the split-KV partial softmaxes: one wave per (row, head).
 template <typename T, int Dh>
 __global__ void __launch_bounds__(256)
@@ -334,8 +599,11 @@ static void attn_plan(int B, int N, int M_tot, int H, int& slots, int& nsplit, i
   slots = (M_tot + kBQ - 1) / kBQ + B;
   const int tiles = N / kBKV;
   const int blocks = ((M_tot + kBQ - 1) / kBQ) * H;   // useful workgroups without a split
+  // Splitting the keys costs a second pass over fp32 partials (several us), so
+  // it is used only when the query tiles alone leave most of the chip idle.
   nsplit = 1;
-  while (blocks * nsplit < 512 && nsplit * 2 <= tiles / 2) nsplit *= 2;
+  if (blocks < 64)
+    while (blocks * nsplit < 256 && nsplit * 2 <= tiles / 2) nsplit *= 2;
   tps = (tiles + nsplit - 1) / nsplit;
 }
 
@@ -355,9 +623,14 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
   float* part_o = (float*)ws;
   float* part_ml = part_o + (size_t)nsplit * M_tot * H * Dh;
   const float sl2 = scale * kLog2e;
-  hipLaunchKernelGGL((attn_kernel<T, Dh>), dim3(slots, H, nsplit), dim3(kAttnThreads), 0, s,
-                     (const T*)q, (const T*)kc, (const T*)vc, act_off, B, N, H, sl2, nsplit, tps,
-                     (T*)out, part_o, part_ml, M_tot);
+  if (sizeof(T) == 2 && Dh == kTrDh)
+    hipLaunchKernelGGL(attn_tr_kernel, dim3(slots * H * nsplit), dim3(kAttnThreads), 0, s,
+                       (const bf16*)q, (const bf16*)kc, (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps,
+                       (bf16*)out, part_o, part_ml, M_tot);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, Dh>), dim3(slots * H * nsplit), dim3(kAttnThreads), 0, s,
+                       (const T*)q, (const T*)kc, (const T*)vc, act_off, B, N, H, sl2, nsplit, tps,
+                       (T*)out, part_o, part_ml, M_tot);
   if (nsplit > 1) {
     const int waves = M_tot * H;
     hipLaunchKernelGGL((attn_combine_kernel<T, Dh>), dim3((waves + 3) / 4), dim3(256), 0, s, part_o,
