@@ -378,32 +378,38 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
 
 // Tile shapes (all 4 waves; RB = k-tile row bytes; S = stages) and their
 // measured sustained rate per CU in multiply-adds per microsecond (bf16,
-// K = 4096 tiles on MI355X).  One workgroup per CU (LDS bound).
+// one workgroup per CU, calibrated on the 4096 / 12288 projections at
+// M = 64 .. 1024 on MI355X).
 struct TileCfg { int BM, BN, RB, S; float rate; };
-static const TileCfg kCfgs[6] = {
-    {256, 256, 64, 4, 2.40e6f},   // 0: wave tile 128x128
-    {128, 256, 128, 3, 2.10e6f},  // 1: wave tile 64x128
-    {256, 128, 128, 3, 1.85e6f},  // 2: wave tile 128x64
-    {128, 128, 128, 3, 1.30e6f},  // 3: wave tile 64x64
+constexpr int kNumCfgs = 8;
+static const TileCfg kCfgs[kNumCfgs] = {
+    {256, 256, 64, 4, 2.10e6f},   // 0: wave tile 128x128
+    {128, 256, 128, 3, 2.05e6f},  // 1: wave tile 64x128
+    {256, 128, 128, 3, 2.10e6f},  // 2: wave tile 128x64
+    {128, 128, 128, 3, 1.55e6f},  // 3: wave tile 64x64
     {128, 64, 128, 4, 1.25e6f},   // 4: waves 4x1, wave tile 32x64
-    {128, 64, 128, 6, 1.20e6f},   // 5: same, deeper pipeline for weight streaming
+    {128, 64, 128, 6, 1.22e6f},   // 5: same, deeper pipeline for weight streaming
+    {256, 192, 64, 4, 1.90e6f},   // 6: wave tile 128x96 (256 tiles at M = 1024, N = 12288)
+    {128, 384, 64, 4, 1.87e6f},   // 7: wave tile 64x192
 };
 constexpr int kCUs = 256;
-constexpr float kStreamBytesPerUs = 5.5e6f;   // sustained weight streaming, bytes/us
-constexpr float kAtomicBytesPerUs = 2.0e6f;   // fp32 atomic adds of split-K partials
+constexpr float kWgStreamBytesPerUs = 6.0e4f;   // what one workgroup's loads sustain
+constexpr float kStreamCapBytesPerUs = 5.5e6f;  // weight streaming from HBM, whole chip
+constexpr float kAtomicBytesPerUs = 1.5e6f;     // fp32 atomic adds of split-K partials
 
 // Estimated time of a launch: compute over full waves of tiles, or streaming
-// the weights (plus A re-reads) from HBM, whichever is longer; split-K adds its
-// atomic traffic.
+// the weights, whichever is longer.  Few workgroups stream slower (each moves
+// about kWgStreamBytesPerUs, of which the weight tile's share is BN/(BM+BN));
+// split-K adds its atomic traffic.
 static float est_us(const GemmArgs& a, int eb, int c, int split) {
   const TileCfg& g = kCfgs[c];
   const long MT = (a.M + g.BM - 1) / g.BM, NT = a.Nv / g.BN;
   const long blocks = MT * NT * split;
   const long waves = (blocks + kCUs - 1) / kCUs;
   const float comp = (float)waves * g.BM * g.BN * ((float)a.K / split) / g.rate;
-  const float conc = blocks < kCUs ? (float)blocks / kCUs : 1.f;
-  const float bytes = (float)a.Nv * a.K * eb + (float)MT * 0 + (float)NT * a.M * a.K * eb * 0.25f;
-  const float mem = bytes / (kStreamBytesPerUs * conc);
+  float bw = (float)blocks * kWgStreamBytesPerUs * g.BN / (g.BM + g.BN);
+  if (bw > kStreamCapBytesPerUs) bw = kStreamCapBytesPerUs;
+  const float mem = (float)a.Nv * a.K * eb / bw;
   const float atom = split > 1 ? (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs : 0.f;
   return (comp > mem ? comp : mem) + atom;
 }
@@ -411,7 +417,7 @@ static float est_us(const GemmArgs& a, int eb, int c, int split) {
 static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& split) {
   float best = 3.4e38f;
   cfg = -1; split = 1;
-  for (int c = 0; c < 6; ++c) {
+  for (int c = 0; c < kNumCfgs; ++c) {
     const TileCfg& g = kCfgs[c];
     if (a.Nv % g.BN || (a.K * eb) % g.RB) continue;
     const int KI = a.K * eb / g.RB;
@@ -442,6 +448,8 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
     case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3>(epi, a, s, split);
     case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4>(epi, a, s, split);
     case 5: return run_cfg<T, 128, 64, 4, 1, 128, 6>(epi, a, s, split);
+    case 6: return run_cfg<T, 256, 192, 2, 2, 64, 4>(epi, a, s, split);
+    case 7: return run_cfg<T, 128, 384, 2, 2, 64, 4>(epi, a, s, split);
   }
   return hipErrorInvalidValue;
 }
