@@ -51,6 +51,35 @@ def kl_bytes(M, N=N_KL, V=V_KL):
     return 2.0 * M * V * 2 + 2.0 * N + 16.0 * M + 4.0 * (N + 2)
 
 
+# HBM traffic of the two roofline kernels from rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) of `python3 bench.py --profile-kernels`, each scaled by
+# what the counter reads for a plain device copy of known size in the same run.  Valid
+# only for the kernel sources they were taken on (sha256 of the listed files); otherwise
+# the report says null.
+TRAFFIC = {
+    "gemm": {"files": ["token_locking_sparse_amd/csrc/gemm.hip"],
+             "sha256": "e6e6cf2c0bf82d8edd878495c2d8e92d0251495f437972aa56f59b7c50eec60c", "bytes": 428020045},
+    "kl": {"files": ["token_locking_sparse_amd/csrc/kl_lock.hip"],
+           "sha256": "09c478114c226effec93327ec7e49f64d58f0c399e75f799d2209ecfe4d71e72", "bytes": 829614215},
+}
+
+
+def _sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(key):
+    t = TRAFFIC[key]
+    if t["bytes"] is None or t["sha256"] != _sources_sha(t["files"]):
+        return None
+    return t["bytes"]
+
+
 def gpu_part(args):
     import numpy as np
     import torch
@@ -194,6 +223,7 @@ def gpu_part(args):
     tot_ms = sum(ms_M.values())
     kb = kl_bytes(M_kl)
     fl_gu = 4.0 * Mg * D * F
+    gu_plan = sl.sl_gemm_plan(bf, sl.SL_EPI_SWIGLU, Mg, D, 2 * F)
     out = {
         "value": round(tot_fl / (tot_ms * 1e-3) / 1e12, 3),
         "ms_per_step": round(wall / args.steps * 1e3, 4),
@@ -201,16 +231,60 @@ def gpu_part(args):
         "kl_lock": {"ms": round(ms_kl, 4), "gbs": round(kb / (ms_kl * 1e-3) / 1e9, 1), "bytes": kb, "M": M_kl,
                     "M_after": M_after, "frac_hbm_peak": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_ms_M1024": {k: round(v, 4) for k, v in br.items()},
-        "roofline": {"kernel": "gemm_kernel<bf16,128x256,...,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_kernel<bf16,%dx%d,split %d,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)" % gu_plan,
+                     "bound": "mfma",
                      "achieved": round(fl_gu / (ms_gu * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fl_gu / (ms_gu * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(fl_gu / (ms_gu * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for("gemm"),
                      "flops_per_launch": fl_gu, "avg_launch_ms": round(ms_gu, 4)},
-        "roofline_kl": {"kernel": "kl_rows_kernel<bf16,true> (KL-lock pass, M=1639, V=126464)", "bound": "hbm",
+        "roofline_kl": {"kernel": "kl_rows_kernel + kl_tail_kernel <bf16> (KL-lock pass, M=1639, V=126464)", "bound": "hbm",
                         "achieved": round(kb / (ms_kl * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                        "frac": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic_for("kl"),
                         "bytes_per_launch": kb, "avg_launch_ms": round(ms_kl, 4)},
     }
     return out
+
+
+def profile_kernels():
+    """Launch only the two roofline kernels and a plain copy of known size, 3 times each
+    (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; the copy calibrates the counters)."""
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import workloads as W
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    Mg = 1024
+    x = (torch.randn((Mg, D), generator=g, device=dev) * 1.0).to(bf)
+    wg = (torch.randn((F, D), generator=g, device=dev) * 0.02).to(bf)
+    wu = (torch.randn((F, D), generator=g, device=dev) * 0.02).to(bf)
+    act = torch.empty(Mg, F, dtype=bf, device=dev)
+    locked_np, act_idx_np, act_off_np = W.kl_lock_mask(N_KL, 1, 0.6, 0)
+    M_kl = int(act_off_np[-1])
+    cur = (torch.randn((N_KL, V_KL), generator=g, device=dev) * 2.0).to(bf)
+    prev = (cur.float() + 0.05 * torch.randn((N_KL, V_KL), generator=g, device=dev)).to(bf)
+    locked = torch.from_numpy(locked_np).to(dev)
+    ai = torch.from_numpy(act_idx_np).to(dev)
+    ao = torch.from_numpy(act_off_np).to(dev)
+    o = {k: torch.empty(M_kl, device=dev) for k in ("kl", "u", "lse", "conf")}
+    am = torch.empty(M_kl, dtype=torch.int32, device=dev)
+    thr = torch.empty(1, device=dev)
+    nai = torch.empty(N_KL, dtype=torch.int32, device=dev)
+    nao = torch.empty(2, dtype=torch.int32, device=dev)
+    ws = torch.empty(sl.sl_kl_lock_workspace_size(1, N_KL, M_kl, V_KL), dtype=torch.uint8, device=dev)
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        sl.sl_gemm(sl.SL_EPI_SWIGLU, x, Mg, D, 2 * F, wg, wu, out0=act)
+        sl.sl_kl_lock(cur, prev, V_KL, ai, ao, 1, N_KL, M_kl, None, EPS_KL, GATE_KL, -1, True, locked, o["kl"],
+                      o["u"], o["lse"], am, o["conf"], thr, nai, nao, ws)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profiled: gate/up GEMM M=%d plan %s, KL-lock pass M=%d, copy of %d bytes" %
+          (Mg, sl.sl_gemm_plan(bf, sl.SL_EPI_SWIGLU, Mg, D, 2 * F), M_kl, src.numel()), flush=True)
 
 
 def cpu_part(seconds: float):
@@ -253,7 +327,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="only launch the roofline kernels and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
+    if args.profile_kernels:
+        profile_kernels()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the SureLock path here is built and measured on a single MI355X "

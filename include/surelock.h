@@ -184,6 +184,14 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
                   const float* rope, int d, int head_dim, const int32_t* act_idx,
                   const int32_t* act_off, int B, int N, sl_stream stream);
 
+/*
+ * sl_gemm_plan — the launch sl_gemm would make for this shape: workgroup tile
+ * rows x columns and the split-K factor (the residual epilogue alone splits K),
+ * chosen by the library's cost model.  Writes nothing on error.  No device work.
+ */
+sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* tile_m, int* tile_n,
+                       int* split_k);
+
 /* One layer's weights, each stored [out_features][in_features] row-major. */
 typedef struct {
   const void* wq; /* [d][d] */

@@ -66,3 +66,22 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.replace("oracle of", ""), "%s mentions the oracle" % f
+
+
+def test_gemm_plan_tiles_divide_and_only_residual_splits():
+    import torch
+
+    import token_locking_sparse_amd.surelock as S
+    d, f, v = 4096, 12288, 126464
+    shapes = [(S.SL_EPI_QKV_ROPE, d, 3 * d), (S.SL_EPI_RESIDUAL, d, d), (S.SL_EPI_SWIGLU, d, 2 * f),
+              (S.SL_EPI_RESIDUAL, f, d), (S.SL_EPI_LOGITS, d, v)]
+    for epi, K, n in shapes:
+        for M in (1, 64, 256, 512, 1024, 3000):
+            tm, tn, sk = S.sl_gemm_plan(torch.bfloat16, epi, M, K, n)
+            assert n % tn == 0 and tm in (128, 256) and tn % 64 == 0
+            assert sk >= 1 and (sk == 1 or epi == S.SL_EPI_RESIDUAL)
+            assert (K * 2 // 128) // sk >= 1
+    # residual projections with few row tiles split K to fill the chip
+    assert S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_RESIDUAL, 64, f, d)[2] > 1
+    with pytest.raises(S.SureLockError):
+        S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_SWIGLU, 64, 4096, 100)   # n_out % 64 != 0

@@ -246,6 +246,20 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
   return SL_OK;
 }
 
+sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* tile_m, int* tile_n,
+                       int* split_k) {
+  g_err[0] = 0;
+  sl_status st = check_dtype(dtype);
+  if (st != SL_OK) return st;
+  SL_REQUIRE(tile_m && tile_n && split_k, SL_ERR_INVALID, "NULL output pointer");
+  SL_REQUIRE(epilogue >= SL_EPI_QKV_ROPE && epilogue <= SL_EPI_LOGITS, SL_ERR_INVALID, "bad epilogue %d", epilogue);
+  SL_REQUIRE(M > 0 && K > 0 && n_out > 0, SL_ERR_INVALID, "bad size");
+  SL_REQUIRE(sl::gemm_supported(dtype, (sl::EpiKind)epilogue, n_out, K, 128, 2), SL_ERR_UNSUPPORTED,
+             "unsupported GEMM shape (K=%d, n_out=%d)", K, n_out);
+  sl::gemm_plan(dtype, (sl::EpiKind)epilogue, M, K, n_out, tile_m, tile_n, split_k);
+  return SL_OK;
+}
+
 size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot) {
   if (!model) return 0;
   return StepLayout(model, B, N, M_tot).total;

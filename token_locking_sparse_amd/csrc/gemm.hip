@@ -454,6 +454,16 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split) {
+  GemmArgs a{};
+  a.M = M; a.K = K; a.Nv = Nv;
+  int c, sp;
+  pick_cfg(a, epi, dtype == 0 ? 2 : 4, c, sp);
+  *bm = c >= 0 ? kCfgs[c].BM : 0;
+  *bn = c >= 0 ? kCfgs[c].BN : 0;
+  *split = c >= 0 ? sp : 0;
+}
+
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   return dtype == 0 ? launch_t<bf16>(epi, a, s) : launch_t<float>(epi, a, s);

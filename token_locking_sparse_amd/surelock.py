@@ -59,7 +59,7 @@ class sl_step_params(C.Structure):
 
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
-           "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_gemm")
+           "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_gemm", "sl_gemm_plan")
 
 _lib = None
 
@@ -88,6 +88,7 @@ def lib():
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
         "sl_gemm": (i, [i, i, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp, vp, i, i, vp]),
+        "sl_gemm_plan": (i, [i, i, i, i, i, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -221,6 +222,14 @@ def sl_step(model: sl_model, state: sl_state, params: sl_step_params, ws, stream
 
 
 SL_EPI_QKV_ROPE, SL_EPI_RESIDUAL, SL_EPI_SWIGLU, SL_EPI_LOGITS = 0, 1, 2, 3
+
+
+def sl_gemm_plan(dtype, epilogue, M, K, n_out):
+    """(tile rows, tile columns, split-K) that sl_gemm launches for this shape."""
+    tm, tn, sk = C.c_int(0), C.c_int(0), C.c_int(0)
+    st = lib().sl_gemm_plan(dtype_code(dtype), int(epilogue), M, K, n_out, C.byref(tm), C.byref(tn), C.byref(sk))
+    _check("sl_gemm_plan", st)
+    return tm.value, tn.value, sk.value
 
 
 def sl_gemm(epilogue, A, M, K, n_out, w0, w1=None, w2=None, out0=None, out1=None, out2=None, rope=None,
