@@ -187,6 +187,51 @@ def test_kl_lock_full_size():
         int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
 
 
+@pytest.mark.slow
+def test_kl_lock_batched_full_size():
+    """The KL-lock pass at the batched ragged shape: 8 sequences x N=2048, V=126464, active fraction
+    per sequence uniform on [0.05, 0.8], eps=0.05, gate 0.5 per sequence."""
+    say("kl_lock batched full size")
+    B, N = 8, 2048
+    lf = 1.0 - W.ragged_fracs(B, key=B * N)
+    case = W.kl_lock_case(N=N, V=126464, B=B, locked_frac=lf, key=B * N)
+    g = _run_kl(case, 0.05, 0.5, -1, True)
+    st, lr = _oracle_kl(case, 0.05, 0.5, -1, True)
+    nd = _compare_kl(case, g, st, lr, 0.05, 0.5, True)
+    say("batched KL-lock: M=%d, new locks gpu %d oracle %d, exempt mismatches %d" % (
+        case.M_tot, int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
+
+
+# ------------------------------------------------------------------ LM head at full vocabulary
+@pytest.mark.slow
+def test_lm_head_full_vocabulary():
+    """Logits of the active rows at d=4096, V=126464, written at rows b*N+pos of the posterior buffer;
+    every other row stays untouched.  Max-abs 2e-2 against the float64 product."""
+    sl = _sl()
+    say("lm head full vocabulary")
+    dm = W.LLADA_LAYER
+    B, N, Ms = 2, 512, [300, 77]
+    g = W.rng(W.SEED_SETS, 4242)
+    acts = [np.sort(g.permutation(N)[:M]).astype(np.int32) for M in Ms]
+    off = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int32)
+    act_idx = np.concatenate(acts)
+    M = int(off[-1])
+    x = W.to_storage(W.normal(W.rng(W.SEED_ACT, 4242), (M, dm.d), 1.0), "bf16")
+    head = W.lm_head_weights(dm)
+    out = torch.full((B * N, dm.vocab), 7.0, dtype=torch.bfloat16, device="cuda")
+    sl.sl_gemm(sl.SL_EPI_LOGITS, dev(x, "bf16"), M, dm.d, dm.vocab, dev(head, "bf16"), out0=out,
+               act_idx=torch.from_numpy(act_idx).cuda(), act_off=torch.from_numpy(off).cuda(), B=B, N=N)
+    torch.cuda.synchronize()
+    glob = O.seq_of_rows(off) * N + act_idx.astype(np.int64)
+    ref = O.widen(x, "bf16") @ O.widen(head, "bf16").T
+    got = host64(out)
+    err = np.max(np.abs(got[glob] - ref))
+    say("lm head max |err| %.3e" % err)
+    assert err <= 2e-2
+    others = np.setdiff1d(np.arange(B * N), glob)
+    assert np.all(got[others] == 7.0)
+
+
 # ------------------------------------------------------------------ attention
 ATTN_CASES = [
     # dtype, Dh, H, N, Ms

@@ -115,6 +115,15 @@ def test_layer_step_full_llada_shape(M):
     _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M, tol=TOL["bf16"])
 
 
+@pytest.mark.slow
+def test_layer_step_batched_full_shape():
+    """The LLaDA-8B-shaped layer on 8 sequences x N=2048 with ragged active sets (fraction per
+    sequence uniform on [0.05, 0.8]): attention within each sequence only."""
+    Ms = W.ragged_ms(8, 2048, key=8 * 2048)
+    say("batched full layer step", Ms)
+    _layer_case_run(W.LLADA_LAYER, 2048, Ms, key=8 * 2048, tol=TOL["bf16"])
+
+
 # ------------------------------------------------------------------ tiny fp32 sampler loop (teacher-forced)
 def _tiny_setup(dm, B, N, n_prompt):
     layers = [W.layer_weights(dm, l) for l in range(dm.n_layers)]

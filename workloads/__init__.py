@@ -156,15 +156,17 @@ class KLLockCase:
         return int(self.act_off[-1])
 
 
-def kl_lock_mask(N: int, B: int = 1, locked_frac: float = 0.6, key: int = 0):
+def kl_lock_mask(N: int, B: int = 1, locked_frac=0.6, key: int = 0):
     """floor(locked_frac*N) positions per sequence locked by a seeded permutation.
 
+    locked_frac is one fraction for every sequence or a sequence of B of them.
     Returns (locked uint8 [B*N], act_idx int32 [M_tot], act_off int32 [B+1])."""
+    fr = np.broadcast_to(np.asarray(locked_frac, dtype=np.float64), (B,))
     locked = np.zeros(B * N, dtype=np.uint8)
     acts, offs = [], [0]
     for b in range(B):
         perm = rng(SEED_SETS, key, b).permutation(N)
-        nl = int(np.floor(locked_frac * N))
+        nl = int(np.floor(fr[b] * N))
         locked[b * N + perm[:nl]] = 1
         act = np.sort(perm[nl:]).astype(np.int32)
         acts.append(act)
@@ -173,7 +175,7 @@ def kl_lock_mask(N: int, B: int = 1, locked_frac: float = 0.6, key: int = 0):
     return locked, act_idx, np.asarray(offs, dtype=np.int32)
 
 
-def kl_lock_case(N: int = 4096, V: int = 126464, B: int = 1, locked_frac: float = 0.6,
+def kl_lock_case(N: int = 4096, V: int = 126464, B: int = 1, locked_frac=0.6,
                  spike_frac: float = 0.7, spike: float = 8.0, std: float = 2.0,
                  drift: float = 0.05, dtype: str = "bf16", cand_frac: float | None = None,
                  key: int = 0) -> KLLockCase:
