@@ -85,3 +85,13 @@ def test_gemm_plan_tiles_divide_and_only_residual_splits():
     assert S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_RESIDUAL, 64, f, d)[2] > 1
     with pytest.raises(S.SureLockError):
         S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_SWIGLU, 64, 4096, 100)   # n_out % 64 != 0
+
+
+def test_gemm_parity_cases_cover_every_tile():
+    """The GPU GEMM parity cases reach every tile shape the launcher can pick (checked on the host)."""
+    import torch
+
+    import token_locking_sparse_amd.surelock as S
+    from tests.test_gpu_kernels import ALL_TILES, GEMM_CASES
+    epi = {"resid": S.SL_EPI_RESIDUAL, "swiglu": S.SL_EPI_SWIGLU, "qkv": S.SL_EPI_QKV_ROPE, "logits": S.SL_EPI_LOGITS}
+    assert {S.sl_gemm_plan(torch.bfloat16, epi[e], M, K, n)[:2] for e, M, K, n in GEMM_CASES} == ALL_TILES

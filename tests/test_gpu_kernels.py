@@ -232,6 +232,94 @@ def test_lm_head_full_vocabulary():
     assert np.all(got[others] == 7.0)
 
 
+# ------------------------------------------------------------------ gathered-row GEMM, every tile shape
+# (epilogue, M, K, n_out): shapes on which the launcher's cost model picks each of its tile
+# shapes (and split-K for the residual); the union is checked to cover every tile.
+GEMM_CASES = [
+    ("resid", 16, 512, 768), ("resid", 16, 1024, 768), ("swiglu", 130, 512, 12288),
+    ("resid", 16, 1024, 12288), ("resid", 16, 2048, 12288), ("swiglu", 300, 512, 12288),
+    ("resid", 130, 4096, 6144), ("swiglu", 700, 512, 12288), ("swiglu", 128, 512, 36864),
+    ("swiglu", 640, 512, 18432), ("swiglu", 768, 512, 18432), ("qkv", 300, 512, 1536),
+    ("qkv", 700, 1024, 3072), ("logits", 130, 512, 6144), ("logits", 600, 1024, 12288),
+]
+ALL_TILES = {(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (256, 192), (128, 384)}
+
+
+def test_gemm_cases_cover_every_tile():
+    sl = _sl()
+    epi = {"resid": sl.SL_EPI_RESIDUAL, "swiglu": sl.SL_EPI_SWIGLU, "qkv": sl.SL_EPI_QKV_ROPE,
+           "logits": sl.SL_EPI_LOGITS}
+    tiles = {sl.sl_gemm_plan(torch.bfloat16, epi[e], M, K, n)[:2] for e, M, K, n in GEMM_CASES}
+    assert tiles == ALL_TILES
+
+
+@pytest.mark.parametrize("kind,M,K,n_out", GEMM_CASES)
+def test_gemm_parity(kind, M, K, n_out):
+    """sl_gemm against the float64 product of the same bf16 inputs, per epilogue."""
+    sl = _sl()
+    say("gemm", kind, M, K, n_out, sl.sl_gemm_plan(torch.bfloat16, {"resid": 1, "swiglu": 2, "qkv": 0, "logits": 3}[kind],
+                                                   M, K, n_out))
+    g = W.rng(W.SEED_ACT, 9000 + M + K + n_out)
+    A = W.to_storage(W.normal(g, (M, K), 1.0), "bf16")
+    A64 = O.widen(A, "bf16")
+    if kind == "swiglu":
+        F = n_out // 2
+        w0 = W.to_storage(W.normal(g, (F, K), 0.02), "bf16")
+        w1 = W.to_storage(W.normal(g, (F, K), 0.02), "bf16")
+        out = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+        sl.sl_gemm(sl.SL_EPI_SWIGLU, dev(A, "bf16"), M, K, n_out, dev(w0, "bf16"), dev(w1, "bf16"), out0=out)
+        ref = O.silu(A64 @ O.widen(w0, "bf16").T) * (A64 @ O.widen(w1, "bf16").T)
+        got = host64(out)
+        assert np.max(np.abs(got - ref) / (1e-2 + np.abs(ref))) <= 1.0, "swiglu mismatch"
+        assert np.max(np.abs(got - ref)) <= 2e-2
+        return
+    if kind == "resid":
+        w0 = W.to_storage(W.normal(g, (n_out, K), 0.02), "bf16")
+        h0 = W.normal(g, (M, n_out), 1.0).astype(np.float32)
+        out = torch.from_numpy(h0.copy()).cuda()
+        sl.sl_gemm(sl.SL_EPI_RESIDUAL, dev(A, "bf16"), M, K, n_out, dev(w0, "bf16"), out0=out)
+        ref = h0.astype(np.float64) + A64 @ O.widen(w0, "bf16").T
+        np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-4, atol=2e-3)
+        return
+    # row-to-position maps over two ragged sequences
+    B, N = 2, max(512, M)
+    m0 = M // 3
+    acts = [np.sort(g.permutation(N)[:m0]), np.sort(g.permutation(N)[:M - m0])]
+    off = np.array([0, m0, M], dtype=np.int32)
+    act_idx = np.concatenate(acts).astype(np.int32)
+    glob = O.seq_of_rows(off) * N + act_idx.astype(np.int64)
+    ai, ao = torch.from_numpy(act_idx).cuda(), torch.from_numpy(off).cuda()
+    if kind == "logits":
+        w0 = W.to_storage(W.normal(g, (n_out, K), 0.02), "bf16")
+        out = torch.full((B * N, n_out), 3.0, dtype=torch.bfloat16, device="cuda")
+        sl.sl_gemm(sl.SL_EPI_LOGITS, dev(A, "bf16"), M, K, n_out, dev(w0, "bf16"), out0=out, act_idx=ai,
+                   act_off=ao, B=B, N=N)
+        got = host64(out)
+        assert np.max(np.abs(got[glob] - A64 @ O.widen(w0, "bf16").T)) <= 2e-2
+        assert np.all(np.delete(got, glob, axis=0) == 3.0)
+        return
+    # QKV + RoPE + cache scatter
+    d, Dh = K, 64
+    H = d // Dh
+    ws = [W.to_storage(W.normal(g, (d, d), 0.02), "bf16") for _ in range(3)]
+    rope = torch.empty(N, Dh // 2, 2, dtype=torch.float32, device="cuda")
+    sl.sl_rope_table(N, Dh, 1e4, rope)
+    q = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    kc = torch.full((B, N, d), 5.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((B, N, d), 5.0, dtype=torch.bfloat16, device="cuda")
+    sl.sl_gemm(sl.SL_EPI_QKV_ROPE, dev(A, "bf16"), M, d, 3 * d, *[dev(w, "bf16") for w in ws], out0=q, out1=kc,
+               out2=vc, rope=rope, d=d, head_dim=Dh, act_idx=ai, act_off=ao, B=B, N=N)
+    W64 = [O.widen(w, "bf16") for w in ws]
+    rq = O.rope((A64 @ W64[0].T).reshape(M, H, Dh), act_idx, 1e4).reshape(M, d)
+    rk = O.rope((A64 @ W64[1].T).reshape(M, H, Dh), act_idx, 1e4).reshape(M, d)
+    rv = A64 @ W64[2].T
+    assert np.max(np.abs(host64(q) - rq)) <= 2e-2
+    gk, gv = host64(kc).reshape(B * N, d), host64(vc).reshape(B * N, d)
+    assert np.max(np.abs(gk[glob] - rk)) <= 2e-2
+    assert np.max(np.abs(gv[glob] - rv)) <= 2e-2
+    assert np.all(np.delete(gk, glob, axis=0) == 5.0) and np.all(np.delete(gv, glob, axis=0) == 5.0)
+
+
 # ------------------------------------------------------------------ attention
 ATTN_CASES = [
     # dtype, Dh, H, N, Ms

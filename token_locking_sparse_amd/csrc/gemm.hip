@@ -20,7 +20,6 @@
 
 namespace sl {
 
-constexpr int kGemmThreads = 256;
 
 // Tile geometry.  RB = bytes of K per row per k-tile (64 or 128); a k-tile is
 // staged in LDS as BM + BN rows of RB bytes, chunks placed by swz<RB> so the
@@ -31,13 +30,14 @@ struct GemmCfg {
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int CPR = RB / 16;                 // chunks per row
   static constexpr int KS = RB / 32;                  // MFMA k-steps per k-tile (32 bytes each)
-  static constexpr int ADma = BM * CPR / kGemmThreads;  // direct loads per thread per k-tile
-  static constexpr int BDma = BN * CPR / kGemmThreads;
+  static constexpr int NW = WM * WN, NT = 64 * NW;     // waves and threads per workgroup
+  static constexpr int ADma = BM * CPR / NT;            // direct loads per thread per k-tile
+  static constexpr int BDma = BN * CPR / NT;
   static constexpr int StageBytes = (BM + BN) * RB;
   static_assert(RB == 64 || RB == 128, "row bytes");
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
-  static_assert(ADma >= 1 && BDma >= 1 && BM * CPR % kGemmThreads == 0 && BN * CPR % kGemmThreads == 0, "load split");
+  static_assert(ADma >= 1 && BDma >= 1 && BM * CPR % NT == 0 && BN * CPR % NT == 0, "load split");
   static_assert(S >= 2 && S * StageBytes <= 150 * 1024, "LDS budget");
   static_assert((S - 2) * (ADma + BDma) < 64, "vmcnt range");
 };
@@ -118,20 +118,20 @@ __device__ __forceinline__ void lds8(const float* p, float* y) {
 // One pass of the epilogue over PR rows of the fp32 tile (rows from mrow0).
 // Paired epilogues: output pair p of the tile takes its first element from
 // tile column (p / (TN/2)) * TN + p % (TN/2) and its partner TN/2 further.
-template <typename T, int EPI, int BN, int TN, int LDW, int PR>
+template <typename T, int EPI, int BN, int TN, int LDW, int PR, int NT>
 __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int mrow0, int n0) {
   const int tid = threadIdx.x;
   if (EPI == EPI_RESID) {
     if (a.split_k > 1) {
       // fp32 atomics, consecutive lanes on consecutive floats of a row
-      for (int id = tid; id < PR * BN; id += kGemmThreads) {
+      for (int id = tid; id < PR * BN; id += NT) {
         const int r = id / BN, c = id % BN;
         const int m = mrow0 + r;
         if (m < a.M) unsafeAtomicAdd((float*)a.out0 + (size_t)m * a.Nv + n0 + c, tile[r * LDW + c]);
       }
     } else {
       constexpr int CPR = BN / 4;
-      for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+      for (int id = tid; id < PR * CPR; id += NT) {
         const int r = id / CPR, c = (id % CPR) * 4;
         const int m = mrow0 + r;
         if (m >= a.M) continue;
@@ -143,7 +143,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     }
   } else if (EPI == EPI_LOGITS) {
     constexpr int CPR = BN / 8;
-    for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+    for (int id = tid; id < PR * CPR; id += NT) {
       const int r = id / CPR, c = (id % CPR) * 8;
       const int m = mrow0 + r;
       if (m >= a.M) continue;
@@ -155,7 +155,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     }
   } else {
     constexpr int CPR = BN / 16;                  // 8-pair runs per row
-    for (int id = tid; id < PR * CPR; id += kGemmThreads) {
+    for (int id = tid; id < PR * CPR; id += NT) {
       const int r = id / CPR, p0 = (id % CPR) * 8;
       const int m = mrow0 + r;
       if (m >= a.M) continue;
@@ -210,7 +210,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 // swizzle stores there.  S-stage pipeline: tile kt+S-1 is requested while tile
 // kt is multiplied; one barrier per k-tile.
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, 2)))
 gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   using C = GemmCfg<T, BM, BN, WM, WN, RB, S>;
   __shared__ __attribute__((aligned(1024))) char smem[S * C::StageBytes];
@@ -238,12 +238,12 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   const char* bp[C::BDma];
 #pragma unroll
   for (int i = 0; i < C::ADma; ++i) {
-    const int r = (i * 4 + wid) * (1024 / RB) + lrow;
+    const int r = (i * C::NW + wid) * (1024 / RB) + lrow;
     aoff[i] = (uint32_t)((size_t)min(m0 + r, a.M - 1) * arb) + swz<RB>(r, lpos) * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::BDma; ++i) {
-    const int r = (i * 4 + wid) * (1024 / RB) + lrow;
+    const int r = (i * C::NW + wid) * (1024 / RB) + lrow;
     bp[i] = w_row_ptr<T, EPI>(a, n0 + r, C::TN) + swz<RB>(r, lpos) * 16;
   }
   const char* abase = (const char*)a.A;
@@ -255,8 +255,8 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 #pragma unroll
     for (int j = 0; j < C::ADma + C::BDma; ++j) {
       if (j < j0 || j >= j1) continue;
-      if (j < C::ADma) dma16(abase + aoff[j] + off, as + (j * 4 + wid) * 1024);
-      else dma16(bp[j - C::ADma] + off, bs + ((j - C::ADma) * 4 + wid) * 1024);
+      if (j < C::ADma) dma16(abase + aoff[j] + off, as + (j * C::NW + wid) * 1024);
+      else dma16(bp[j - C::ADma] + off, bs + ((j - C::ADma) * C::NW + wid) * 1024);
     }
   };
 
@@ -352,7 +352,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
           tile[(rb + (v >> 2) * 8 + 4 * hl + (v & 3)) * LDW + wn * C::TN + j * 32 + l32] = acc[i][j][v];
     }
     __syncthreads();
-    epilogue_pass<T, EPI, BN, C::TN, LDW, PR>(a, tile, m0 + r_lo, n0);
+    epilogue_pass<T, EPI, BN, C::TN, LDW, PR, C::NT>(a, tile, m0 + r_lo, n0);
     __syncthreads();
   }
 }
@@ -366,7 +366,7 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
   const int nsplit = (KI + kps - 1) / kps;
   GemmArgs b = a;
   b.split_k = nsplit;
-  const dim3 grid(MT * NT, 1, nsplit), block(kGemmThreads);
+  const dim3 grid(MT * NT, 1, nsplit), block(64 * WM * WN);
   switch (epi) {
     case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_QKV>), grid, block, 0, s, b, MT, NT, kps); break;
     case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID>), grid, block, 0, s, b, MT, NT, kps); break;
@@ -376,21 +376,21 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
   return hipGetLastError();
 }
 
-// Tile shapes (all 4 waves; RB = k-tile row bytes; S = stages) and their
+// Tile shapes (4 or 8 waves; RB = k-tile row bytes; S = stages) and their
 // measured sustained rate per CU in multiply-adds per microsecond (bf16,
 // one workgroup per CU, calibrated on the 4096 / 12288 projections at
 // M = 64 .. 1024 on MI355X).
 struct TileCfg { int BM, BN, RB, S; float rate; };
 constexpr int kNumCfgs = 8;
 static const TileCfg kCfgs[kNumCfgs] = {
-    {256, 256, 64, 4, 2.10e6f},   // 0: wave tile 128x128
-    {128, 256, 128, 3, 2.05e6f},  // 1: wave tile 64x128
-    {256, 128, 128, 3, 2.10e6f},  // 2: wave tile 128x64
-    {128, 128, 128, 3, 1.55e6f},  // 3: wave tile 64x64
-    {128, 64, 128, 4, 1.25e6f},   // 4: waves 4x1, wave tile 32x64
+    {256, 256, 64, 4, 2.35e6f},   // 0: eight waves 2x4, wave tile 128x64
+    {256, 128, 128, 3, 2.17e6f},  // 1: eight waves 4x2, wave tile 64x64
+    {128, 256, 128, 3, 2.13e6f},  // 2: eight waves 2x4, wave tile 64x64
+    {128, 128, 128, 3, 1.55e6f},  // 3: four waves, wave tile 64x64
+    {128, 64, 128, 4, 1.25e6f},   // 4: four waves 4x1, wave tile 32x64
     {128, 64, 128, 6, 1.22e6f},   // 5: same, deeper pipeline for weight streaming
-    {256, 192, 64, 4, 1.90e6f},   // 6: wave tile 128x96 (256 tiles at M = 1024, N = 12288)
-    {128, 384, 64, 4, 1.87e6f},   // 7: wave tile 64x192
+    {256, 192, 64, 4, 1.90e6f},   // 6: four waves, wave tile 128x96 (256 tiles at M = 1024, N = 12288)
+    {128, 384, 64, 4, 1.87e6f},   // 7: four waves, wave tile 64x192
 };
 constexpr int kCUs = 256;
 constexpr float kWgStreamBytesPerUs = 6.0e4f;   // what one workgroup's loads sustain
@@ -442,9 +442,9 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
   int c, split;
   pick_cfg(a, epi, (int)sizeof(T), c, split);
   switch (c) {
-    case 0: return run_cfg<T, 256, 256, 2, 2, 64, 4>(epi, a, s, split);
-    case 1: return run_cfg<T, 128, 256, 2, 2, 128, 3>(epi, a, s, split);
-    case 2: return run_cfg<T, 256, 128, 2, 2, 128, 3>(epi, a, s, split);
+    case 0: return run_cfg<T, 256, 256, 2, 4, 64, 4>(epi, a, s, split);
+    case 1: return run_cfg<T, 256, 128, 4, 2, 128, 3>(epi, a, s, split);
+    case 2: return run_cfg<T, 128, 256, 2, 4, 128, 3>(epi, a, s, split);
     case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3>(epi, a, s, split);
     case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4>(epi, a, s, split);
     case 5: return run_cfg<T, 128, 64, 4, 1, 128, 6>(epi, a, s, split);
