@@ -330,16 +330,19 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
 // transpose read touches over the 16 positions.
 constexpr int kTrDh = 128;
 constexpr int kTrBKV = 64;                       // keys per tile
-constexpr int kTrS = 2;                          // LDS stages: loads run kTrS - 1 tiles ahead
+constexpr int kTrGroups = 2;                     // key groups: waves 4g .. 4g+3 take the tiles t = g (mod 2)
+constexpr int kTrThreads = 256 * kTrGroups;
+constexpr int kTrS = 2;                          // LDS stages per group: loads run one tile ahead
 constexpr int kTrRB = kTrDh * 2;                 // bytes per key row
-constexpr int kTrTile = kTrBKV * kTrRB;          // 8 KB per K or V tile
-constexpr int kTrStage = 2 * kTrTile;
+constexpr int kTrTile = kTrBKV * kTrRB;          // 16 KB per K or V tile
+constexpr int kTrStage = 2 * kTrTile;            // K + V of one group's tile
 constexpr int kTrEpi = 4 * 32 * (kTrDh + 1) * 4;
-constexpr int kTrSmem = (kTrS * kTrStage > kTrEpi) ? kTrS * kTrStage : kTrEpi;
-constexpr int kTrDma = kTrTile / (kAttnThreads * 16);   // direct loads per thread per K (or V) tile
-constexpr int kTrLoads = 2 * kTrDma;                   // per thread per tile (K and V)
-static_assert(kTrDma >= 1 && kBKV % kTrBKV == 0 && kTrBKV % 32 == 0, "tile split");
-static_assert((kTrS - 2) * kTrLoads < 16, "vmcnt immediate");
+constexpr int kTrMergeWave = 64 * (kTrDh / 2) + 2 * 64;   // floats a group-1 wave hands over: O^T, m, l
+constexpr int kTrMerge = 4 * kTrMergeWave * 4;
+constexpr int kTrPipe = kTrS * kTrGroups * kTrStage;
+constexpr int kTrSmem = kTrPipe > kTrEpi ? (kTrPipe > kTrMerge ? kTrPipe : kTrMerge) : (kTrEpi > kTrMerge ? kTrEpi : kTrMerge);
+constexpr int kTrDma = kTrTile / (256 * 16);     // direct loads per thread per K (or V) tile
+static_assert(kTrDma >= 1 && kBKV == kTrBKV && kTrS == 2, "tile split");
 
 typedef __attribute__((address_space(3))) void attn_lds_t;
 typedef __attribute__((address_space(1))) void attn_glb_t;
@@ -353,7 +356,7 @@ __device__ __forceinline__ uint2 lds_tr16(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kTrThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
                const int32_t* __restrict__ act_off, int B, int N, int H, float scale_log2, int nsplit,
                int tiles_per_split, bf16* __restrict__ out, float* __restrict__ part_o,
@@ -361,6 +364,7 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   constexpr int Dh = kTrDh, E = 8, nKK = Dh / 16;
   __shared__ __attribute__((aligned(1024))) char smem[kTrSmem];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int grp = wid >> 2, wq = wid & 3;   // key group; query block of the wave
   const int per_head = gridDim.x / H;
   int h, rest;
   if ((H & 7) == 0) {   // all workgroups of a head on one XCD (see attn_kernel)
@@ -374,14 +378,12 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   const int split = rest % nsplit, slot = rest / nsplit;
   int row0 = 0, row_end = 0;
   const int b = find_tile(act_off, B, slot, row0, row_end);
-  if (b < 0) return;
-  // the split plan counts 64-key tiles; this kernel walks 32-key tiles
-  constexpr int TR = kBKV / kTrBKV;
-  const int t_begin = split * tiles_per_split * TR;
-  const int t_end = min(N / kBKV, (split + 1) * tiles_per_split) * TR;
+  if (b < 0) return;   // uniform over the workgroup
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(N / kBKV, t_begin + tiles_per_split);
   const int HD = H * Dh;
 
-  const int wrow0 = row0 + wid * 32;
+  const int wrow0 = row0 + wq * 32;
   const bool wave_live = wrow0 < row_end;
   const int my_row = min(wrow0 + l32, row_end - 1);
   u32x4 qf[nKK];
@@ -391,33 +393,33 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     for (int kk = 0; kk < nKK; ++kk) qf[kk] = ld16(qr + (2 * kk + hl) * 16);
   }
 
-  // direct-load sources: load j of this wave fills LDS bytes [(4 j + wid) KB, +1 KB)
-  // of a tile = key rows 4 (4 j + wid) + lane / 16, stored position lane % 16
+  // direct-load sources: load j of wave wq of a group fills LDS bytes [(4 j + wq) KB, +1 KB)
+  // of its tile = key rows 4 (4 j + wq) + lane / 16, stored position lane % 16
   const size_t krow = (size_t)HD * 2;
   const char* kb0 = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
   const char* vb0 = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
   uint32_t koff[kTrDma], voff[kTrDma];
 #pragma unroll
   for (int j = 0; j < kTrDma; ++j) {
-    const int r = 4 * (4 * j + wid) + (lane >> 4), pos = lane & 15;
+    const int r = 4 * (4 * j + wq) + (lane >> 4), pos = lane & 15;
     koff[j] = (uint32_t)(r * krow) + swz<kTrRB>(r, pos) * 16;
     voff[j] = (uint32_t)(r * krow) + vswz(r, pos) * 16;
   }
+  auto stage_base = [&](int stage) { return smem + (stage * kTrGroups + grp) * kTrStage; };
   auto issue = [&](int tile, int stage) {
-    char* ks = smem + stage * kTrStage;
+    char* ks = stage_base(stage);
     char* vs = ks + kTrTile;
     const size_t t0 = (size_t)tile * kTrBKV * krow;
 #pragma unroll
     for (int j = 0; j < kTrDma; ++j)
-      __builtin_amdgcn_global_load_lds((attn_glb_t*)(kb0 + t0 + koff[j]), (attn_lds_t*)(ks + (4 * j + wid) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(kb0 + t0 + koff[j]), (attn_lds_t*)(ks + (4 * j + wq) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < kTrDma; ++j)
-      __builtin_amdgcn_global_load_lds((attn_glb_t*)(vb0 + t0 + voff[j]), (attn_lds_t*)(vs + (4 * j + wid) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(vb0 + t0 + voff[j]), (attn_lds_t*)(vs + (4 * j + wq) * 1024), 16, 0, 0);
   };
 
-  // transpose-read offsets inside a V tile (per d-tile dt and k-step m add
-  // dt / m dependent terms): this lane of its 16-lane group reads key row
-  // kb + s / 4 at column d0 + 4 (s % 4)
+  // transpose-read offsets inside a V tile: this lane of its 16-lane group reads
+  // key row kb + s / 4 at column d0 + 4 (s % 4)
   const int g16 = lane >> 4, s16 = lane & 15;
   const int tr_dhalf = 16 * (g16 & 1);            // d0 within the 32-wide d-tile
   const int tr_khalf = 4 * (g16 >> 1);            // 4 hl
@@ -428,23 +430,19 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-#pragma unroll
-  for (int i = 0; i < kTrS - 1; ++i)
-    if (t_begin + i < t_end) issue(t_begin + i, i);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int stage = (t - t_begin) % kTrS;
-    // tile t has landed once at most the loads of the tiles after it are
-    // outstanding (2 K + 2 V loads per tile; older Q loads are done by then)
-    const int after = min(kTrS - 2, t_end - 1 - t);
-    if (kTrS >= 4 && after >= 2) __builtin_amdgcn_s_waitcnt(((2 * kTrLoads) & 15) | (7 << 4) | (15 << 8));
-    else if (kTrS >= 3 && after >= 1) __builtin_amdgcn_s_waitcnt((kTrLoads & 15) | (7 << 4) | (15 << 8));
-    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  // iteration it: group g takes tile t_begin + 2 it + g (if inside the range)
+  const int n_it = (t_end - t_begin + kTrGroups - 1) / kTrGroups;
+  auto own_tile = [&](int it) { return t_begin + it * kTrGroups + grp; };
+  if (n_it > 0 && own_tile(0) < t_end) issue(own_tile(0), 0);
+  for (int it = 0; it < n_it; ++it) {
+    const int stage = it & 1;
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): this thread's loads of the tile landed
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();   // everyone's tile t landed; the stage of tile t - 1 is free
+    __builtin_amdgcn_s_barrier();                  // everyone's landed; the other stage is free again
     asm volatile("" ::: "memory");
-    if (t + kTrS - 1 < t_end) issue(t + kTrS - 1, (t + kTrS - 1 - t_begin) % kTrS);
-    if (!wave_live) continue;
-    const char* ks = smem + stage * kTrStage;
+    if (it + 1 < n_it && own_tile(it + 1) < t_end) issue(own_tile(it + 1), stage ^ 1);
+    if (!wave_live || own_tile(it) >= t_end) continue;
+    const char* ks = stage_base(stage);
     const char* vs = ks + kTrTile;
     constexpr int NS = kTrBKV / 32;   // 32-key subtiles
     f32x16 sc[NS];
@@ -510,21 +508,49 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
       }
     }
   }
-  __syncthreads();   // stages free for the epilogue staging
+  __syncthreads();   // stages free
+
+  // group 1 hands its partial (O^T registers, m, l; lane and register order) to the
+  // group-0 wave of the same queries, which merges the two online softmaxes
+  float* mg = (float*)smem + wq * kTrMergeWave;
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < Dh / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mg[(dt * 16 + v) * 64 + lane] = oacc[dt][v];
+    mg[64 * (Dh / 2) + lane] = m_run;
+    mg[64 * (Dh / 2) + 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m_o = mg[64 * (Dh / 2) + lane], l_o = mg[64 * (Dh / 2) + 64 + lane];
+    const float m_new = fmaxf(m_run, m_o);
+    const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f;
+    const float a1 = m_o > -INFINITY ? __builtin_amdgcn_exp2f(m_o - m_new) : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < Dh / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][v] = oacc[dt][v] * a0 + mg[(dt * 16 + v) * 64 + lane] * a1;
+    l_run = l_run * a0 + l_o * a1;
+    m_run = m_new;
+  }
+  __syncthreads();   // merge area free for the output staging
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const bool final_out = (nsplit == 1);
   const float inv = (final_out && l_tot > 0.f) ? 1.f / l_tot : 1.f;
-  float* ep = (float*)smem + wid * 32 * (Dh + 1);
+  float* ep = (float*)smem + wq * 32 * (Dh + 1);
+  if (grp == 0) {
 #pragma unroll
-  for (int dt = 0; dt < Dh / 32; ++dt)
+    for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
-      ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
-    }
+      for (int v = 0; v < 16; ++v) {
+        const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
+        ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
+      }
+  }
   __syncthreads();
-  if (wave_live) {
+  if (grp == 0 && wave_live) {
     const int nrow = min(32, row_end - wrow0);
     if (final_out) {
       constexpr int CPR = Dh / E;
@@ -534,10 +560,7 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
           const float* src = ep + rr * (Dh + 1) + c * E;
           u32x4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16 lo = (bf16)src[2 * i], hi = (bf16)src[2 * i + 1];
-            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
+          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(src[2 * i], src[2 * i + 1]);
           st16((char*)(out + (size_t)(wrow0 + rr) * HD + (size_t)h * Dh) + c * 16, w);
         }
       }
@@ -624,7 +647,7 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
   float* part_ml = part_o + (size_t)nsplit * M_tot * H * Dh;
   const float sl2 = scale * kLog2e;
   if (sizeof(T) == 2 && Dh == kTrDh)
-    hipLaunchKernelGGL(attn_tr_kernel, dim3(slots * H * nsplit), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL(attn_tr_kernel, dim3(slots * H * nsplit), dim3(kTrThreads), 0, s,
                        (const bf16*)q, (const bf16*)kc, (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps,
                        (bf16*)out, part_o, part_ml, M_tot);
   else
