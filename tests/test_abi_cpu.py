@@ -78,7 +78,7 @@ def test_gemm_plan_tiles_divide_and_only_residual_splits():
     for epi, K, n in shapes:
         for M in (1, 64, 256, 512, 1024, 3000):
             tm, tn, sk = S.sl_gemm_plan(torch.bfloat16, epi, M, K, n)
-            assert n % tn == 0 and tm in (128, 256) and tn % 64 == 0
+            assert n % tn == 0 and tm in (64, 128, 256) and tn % 64 == 0
             assert sk >= 1 and (sk == 1 or epi == S.SL_EPI_RESIDUAL)
             assert (K * 2 // 128) // sk >= 1
     # residual projections with few row tiles split K to fill the chip

@@ -241,8 +241,9 @@ GEMM_CASES = [
     ("resid", 130, 4096, 6144), ("swiglu", 700, 512, 12288), ("swiglu", 128, 512, 36864),
     ("swiglu", 640, 512, 18432), ("swiglu", 768, 512, 18432), ("qkv", 300, 512, 1536),
     ("qkv", 700, 1024, 3072), ("logits", 130, 512, 6144), ("logits", 600, 1024, 12288),
+    ("swiglu", 16, 512, 24576), ("swiglu", 16, 512, 768),
 ]
-ALL_TILES = {(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (256, 192), (128, 384)}
+ALL_TILES = {(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (256, 192), (128, 384), (64, 128), (64, 64)}
 
 
 def test_gemm_cases_cover_every_tile():

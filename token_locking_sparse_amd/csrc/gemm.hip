@@ -378,40 +378,42 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
 
 // Tile shapes (4 or 8 waves; RB = k-tile row bytes; S = stages) and their
 // measured sustained rate per CU in multiply-adds per microsecond (bf16,
-// one workgroup per CU, calibrated on the 4096 / 12288 projections at
-// M = 64 .. 1024 on MI355X).
+// calibrated on the 4096 / 12288 projections at M = 64 .. 1024 on MI355X,
+// weights rotated over copies larger than the Infinity Cache).
 struct TileCfg { int BM, BN, RB, S; float rate; };
-constexpr int kNumCfgs = 8;
+constexpr int kNumCfgs = 9;
 static const TileCfg kCfgs[kNumCfgs] = {
     {256, 256, 64, 4, 2.35e6f},   // 0: eight waves 2x4, wave tile 128x64
     {256, 128, 128, 3, 2.17e6f},  // 1: eight waves 4x2, wave tile 64x64
     {128, 256, 128, 3, 2.13e6f},  // 2: eight waves 2x4, wave tile 64x64
     {128, 128, 128, 3, 1.55e6f},  // 3: four waves, wave tile 64x64
     {128, 64, 128, 4, 1.25e6f},   // 4: four waves 4x1, wave tile 32x64
-    {128, 64, 128, 6, 1.22e6f},   // 5: same, deeper pipeline for weight streaming
-    {256, 192, 64, 4, 1.90e6f},   // 6: four waves, wave tile 128x96 (256 tiles at M = 1024, N = 12288)
-    {128, 384, 64, 4, 1.87e6f},   // 7: four waves, wave tile 64x192
+    {256, 192, 64, 4, 1.90e6f},   // 5: four waves, wave tile 128x96 (256 tiles at M = 1024, N = 12288)
+    {128, 384, 64, 4, 1.87e6f},   // 6: four waves, wave tile 64x192
+    {64, 128, 128, 6, 1.06e6f},   // 7: four waves 1x4, wave tile 64x32: weight streaming at small M
+    {64, 64, 128, 8, 0.82e6f},    // 8: four waves 2x2, wave tile 32x32: weight streaming at small M
 };
 constexpr int kCUs = 256;
-constexpr float kWgStreamBytesPerUs = 6.0e4f;   // what one workgroup's loads sustain
-constexpr float kStreamCapBytesPerUs = 5.5e6f;  // weight streaming from HBM, whole chip
+constexpr float kStreamCapBytesPerUs = 5.0e6f;  // weight streaming from HBM, whole chip
+constexpr float kLoadLatencyUs = 1.0f;          // what a workgroup's S-1 tiles in flight amortise
 constexpr float kAtomicBytesPerUs = 1.5e6f;     // fp32 atomic adds of split-K partials
+constexpr float kLaunchUs = 2.0f;
 
 // Estimated time of a launch: compute over full waves of tiles, or streaming
-// the weights, whichever is longer.  Few workgroups stream slower (each moves
-// about kWgStreamBytesPerUs, of which the weight tile's share is BN/(BM+BN));
-// split-K adds its atomic traffic.
+// the weights, whichever is longer.  A workgroup keeps (S-1) weight tiles
+// (BN x RB bytes each) in flight, so few workgroups stream slower than the chip
+// can; split-K adds its atomic traffic.
 static float est_us(const GemmArgs& a, int eb, int c, int split) {
   const TileCfg& g = kCfgs[c];
   const long MT = (a.M + g.BM - 1) / g.BM, NT = a.Nv / g.BN;
   const long blocks = MT * NT * split;
   const long waves = (blocks + kCUs - 1) / kCUs;
   const float comp = (float)waves * g.BM * g.BN * ((float)a.K / split) / g.rate;
-  float bw = (float)blocks * kWgStreamBytesPerUs * g.BN / (g.BM + g.BN);
+  float bw = (float)blocks * (g.S - 1) * g.BN * g.RB / kLoadLatencyUs;
   if (bw > kStreamCapBytesPerUs) bw = kStreamCapBytesPerUs;
   const float mem = (float)a.Nv * a.K * eb / bw;
   const float atom = split > 1 ? (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs : 0.f;
-  return (comp > mem ? comp : mem) + atom;
+  return (comp > mem ? comp : mem) + atom + kLaunchUs;
 }
 
 static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& split) {
@@ -447,9 +449,10 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
     case 2: return run_cfg<T, 128, 256, 2, 4, 128, 3>(epi, a, s, split);
     case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3>(epi, a, s, split);
     case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4>(epi, a, s, split);
-    case 5: return run_cfg<T, 128, 64, 4, 1, 128, 6>(epi, a, s, split);
-    case 6: return run_cfg<T, 256, 192, 2, 2, 64, 4>(epi, a, s, split);
-    case 7: return run_cfg<T, 128, 384, 2, 2, 64, 4>(epi, a, s, split);
+    case 5: return run_cfg<T, 256, 192, 2, 2, 64, 4>(epi, a, s, split);
+    case 6: return run_cfg<T, 128, 384, 2, 2, 64, 4>(epi, a, s, split);
+    case 7: return run_cfg<T, 64, 128, 1, 4, 128, 6>(epi, a, s, split);
+    case 8: return run_cfg<T, 64, 64, 2, 2, 128, 8>(epi, a, s, split);
   }
   return hipErrorInvalidValue;
 }
