@@ -11,37 +11,100 @@
 
 namespace sl {
 
-// One wave per row.  The residual stream h32 is fp32; x = h / sqrt(mean(h^2)+eps)
-// is stored in the GEMM operand type.
-template <typename T>
-__global__ void __launch_bounds__(256)
-gather_norm_kernel(const T* __restrict__ h_in, const T* __restrict__ embed, const int32_t* __restrict__ tok,
-                   const int32_t* __restrict__ act_idx, const int32_t* __restrict__ act_off, int B, int N,
-                   int M_tot, int d, float eps, float* __restrict__ h32, T* __restrict__ x) {
-  constexpr int E = 16 / (int)sizeof(T);
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M_tot) return;
-  const int b = seq_of_row(act_off, B, m);
-  const int64_t g = (int64_t)b * N + act_idx[m];
-  const T* src = h_in ? h_in + g * d : embed + (int64_t)tok[g] * d;
+// One wave per row: x = h / sqrt(mean(h^2) + eps) in the GEMM operand type TO,
+// from a row of TI (the fp32 residual stream, or the storage-type input of the
+// gather, which is also copied into the fp32 residual stream).  A row of up to
+// kRowElems elements is read once into registers (all loads in flight
+// together); wider rows are read twice.
+constexpr int kRowElems = 8192;
+
+// 4 or 8 floats -> the output type with one or two 16-byte (or one 8-byte) stores
+__device__ __forceinline__ void store_x(bf16* dst, const float* f, int n) {
+  if (n == 8) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    st16(dst, w);
+  } else {
+    uint2 w;
+    w.x = pack_bf16x2(f[0], f[1]);
+    w.y = pack_bf16x2(f[2], f[3]);
+    *reinterpret_cast<uint2*>(dst) = w;
+  }
+}
+__device__ __forceinline__ void store_x(float* dst, const float* f, int n) {
+  st16(dst, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])});
+  if (n == 8)
+    st16(dst + 4, u32x4{__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])});
+}
+
+template <typename TI, typename TO, bool H32>
+__device__ __forceinline__ void norm_row(const TI* __restrict__ src, int d, float eps, float* __restrict__ h32row,
+                                         TO* __restrict__ xrow, int lane) {
+  constexpr int E = Chunk<TI>::kElems;
+  constexpr int kRowChunks = kRowElems / (64 * E);   // 16-byte chunks per lane
   const int nc = d / E;
+  if (nc <= 64 * kRowChunks) {
+    u32x4 v[kRowChunks];
+#pragma unroll
+    for (int k = 0; k < kRowChunks; ++k)
+      if (lane + 64 * k < nc) v[k] = ld16(src + (lane + 64 * k) * E);
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRowChunks; ++k)
+      if (lane + 64 * k < nc) {
+        float f[E];
+        Chunk<TI>::unpack(v[k], f);
+#pragma unroll
+        for (int j = 0; j < E; ++j) ss = fmaf(f[j], f[j], ss);
+      }
+    ss = wave_sum(ss);
+    const float r = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int k = 0; k < kRowChunks; ++k)
+      if (lane + 64 * k < nc) {
+        const int c = lane + 64 * k;
+        float f[E], y[E];
+        Chunk<TI>::unpack(v[k], f);
+        if (H32) store_x(h32row + c * E, f, E);
+#pragma unroll
+        for (int j = 0; j < E; ++j) y[j] = f[j] * r;
+        store_x(xrow + c * E, y, E);
+      }
+    return;
+  }
   float ss = 0.f;
   for (int c = lane; c < nc; c += 64) {
     float f[E];
-    Chunk<T>::unpack(ld16(src + c * E), f);
+    Chunk<TI>::unpack(ld16(src + c * E), f);
 #pragma unroll
     for (int j = 0; j < E; ++j) ss = fmaf(f[j], f[j], ss);
   }
   ss = wave_sum(ss);
   const float r = 1.f / sqrtf(ss / (float)d + eps);
   for (int c = lane; c < nc; c += 64) {
-    float f[E];
-    Chunk<T>::unpack(ld16(src + c * E), f);
-    float* hp = h32 + (size_t)m * d + c * E;
-    T* xp = x + (size_t)m * d + c * E;
+    float f[E], y[E];
+    Chunk<TI>::unpack(ld16(src + c * E), f);
+    if (H32) store_x(h32row + c * E, f, E);
 #pragma unroll
-    for (int j = 0; j < E; ++j) { hp[j] = f[j]; xp[j] = from_f32<T>(f[j] * r); }
+    for (int j = 0; j < E; ++j) y[j] = f[j] * r;
+    store_x(xrow + c * E, y, E);
   }
+}
+
+// Gather of the layer-0 input of the active rows (embedding of the current
+// token, or a given hidden row) into the fp32 residual stream, plus its RMSNorm.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gather_norm_kernel(const T* __restrict__ h_in, const T* __restrict__ embed, const int32_t* __restrict__ tok,
+                   const int32_t* __restrict__ act_idx, const int32_t* __restrict__ act_off, int B, int N,
+                   int M_tot, int d, float eps, float* __restrict__ h32, T* __restrict__ x) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M_tot) return;
+  const int b = seq_of_row(act_off, B, m);
+  const int64_t g = (int64_t)b * N + act_idx[m];
+  const T* src = h_in ? h_in + g * d : embed + (int64_t)tok[g] * d;
+  norm_row<T, T, true>(src, d, eps, h32 + (size_t)m * d, x + (size_t)m * d, lane);
 }
 
 template <typename T>
@@ -49,22 +112,7 @@ __global__ void __launch_bounds__(256)
 norm_kernel(const float* __restrict__ h32, int M_tot, int d, float eps, T* __restrict__ x) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (m >= M_tot) return;
-  const float* hp = h32 + (size_t)m * d;
-  const int nc = d / 4;
-  float ss = 0.f;
-  for (int c = lane; c < nc; c += 64) {
-    const f32x4 v = *(const f32x4*)(hp + 4 * c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ss = fmaf(v[j], v[j], ss);
-  }
-  ss = wave_sum(ss);
-  const float r = 1.f / sqrtf(ss / (float)d + eps);
-  T* xp = x + (size_t)m * d;
-  for (int c = lane; c < nc; c += 64) {
-    const f32x4 v = *(const f32x4*)(hp + 4 * c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xp[4 * c + j] = from_f32<T>(v[j] * r);
-  }
+  norm_row<float, T, false>(h32 + (size_t)m * d, d, eps, nullptr, x + (size_t)m * d, lane);
 }
 
 hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, const int32_t* tok,
