@@ -328,6 +328,8 @@ ATTN_CASES = [
     ("bf16", 128, 3, 1024, [5]),          # few query tiles: split over keys + merge
     ("bf16", 128, 8, 512, [300, 1, 77]),  # heads a multiple of 8 (XCD placement), ragged
     ("bf16", 128, 16, 1024, [640]),       # several query tiles per head, no split
+    ("bf16", 128, 32, 1024, [1024]),      # 128-query workgroups (two key groups)
+    ("bf16", 128, 32, 1024, [600, 500]),  # same, ragged tails in both sequences
     ("bf16", 64, 2, 128, [1, 128, 70]),
     ("bf16", 32, 4, 64, [64]),
     ("f32", 32, 4, 64, [64, 3]),

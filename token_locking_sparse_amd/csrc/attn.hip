@@ -53,12 +53,13 @@ __device__ __forceinline__ int vpos(int k) {
 
 // Locate query tile `slot` of the ragged sequences: returns b (or -1) and the
 // first row of the tile.
-__device__ __forceinline__ int find_tile(const int32_t* act_off, int B, int slot, int& row0, int& row_end) {
+__device__ __forceinline__ int find_tile(const int32_t* act_off, int B, int slot, int& row0, int& row_end,
+                                         int bq = kBQ) {
   int s = slot;
   for (int b = 0; b < B; ++b) {
     const int o0 = act_off[b], o1 = act_off[b + 1];
-    const int nt = (o1 - o0 + kBQ - 1) / kBQ;
-    if (s < nt) { row0 = o0 + s * kBQ; row_end = o1; return b; }
+    const int nt = (o1 - o0 + bq - 1) / bq;
+    if (s < nt) { row0 = o0 + s * bq; row_end = o1; return b; }
     s -= nt;
   }
   return -1;
@@ -329,20 +330,27 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
 // c ^ 4 (row & 3), which spreads the 16 (row, chunk) pairs one half-wave of a
 // transpose read touches over the 16 positions.
 constexpr int kTrDh = 128;
-constexpr int kTrBKV = 64;                       // keys per tile
-constexpr int kTrGroups = 2;                     // key groups: waves 4g .. 4g+3 take the tiles t = g (mod 2)
-constexpr int kTrThreads = 256 * kTrGroups;
-constexpr int kTrS = 2;                          // LDS stages per group: loads run one tile ahead
 constexpr int kTrRB = kTrDh * 2;                 // bytes per key row
-constexpr int kTrTile = kTrBKV * kTrRB;          // 16 KB per K or V tile
-constexpr int kTrStage = 2 * kTrTile;            // K + V of one group's tile
-constexpr int kTrEpi = 4 * 32 * (kTrDh + 1) * 4;
-constexpr int kTrMergeWave = 64 * (kTrDh / 2) + 2 * 64;   // floats a group-1 wave hands over: O^T, m, l
-constexpr int kTrMerge = 4 * kTrMergeWave * 4;
-constexpr int kTrPipe = kTrS * kTrGroups * kTrStage;
-constexpr int kTrSmem = kTrPipe > kTrEpi ? (kTrPipe > kTrMerge ? kTrPipe : kTrMerge) : (kTrEpi > kTrMerge ? kTrEpi : kTrMerge);
-constexpr int kTrDma = kTrTile / (256 * 16);     // direct loads per thread per K (or V) tile
-static_assert(kTrDma >= 1 && kBKV == kTrBKV && kTrS == 2, "tile split");
+constexpr int kTrMergeWave = 64 * (kTrDh / 2) + 2 * 64;   // floats a wave hands over: O^T, m, l
+
+// Shape of one workgroup of the bf16 / Dh = 128 kernel: QW query waves (32
+// queries each) x G key groups (group g takes the BKV-key tiles t = g mod G),
+// double-buffered per group.
+template <int QW, int G, int BKV>
+struct TrCfg {
+  static constexpr int kThreads = 64 * QW * G;
+  static constexpr int kBQ = 32 * QW;
+  static constexpr int kTile = BKV * kTrRB;            // one K or V tile
+  static constexpr int kStage = 2 * kTile;             // K + V of one group's tile
+  static constexpr int kPipe = 2 * G * kStage;
+  static constexpr int kMerge = (G - 1) * QW * kTrMergeWave * 4;
+  static constexpr int kEpi = QW * 32 * (kTrDh + 1) * 4;
+  static constexpr int kSmem = kPipe > kMerge ? (kPipe > kEpi ? kPipe : kEpi) : (kMerge > kEpi ? kMerge : kEpi);
+  static constexpr int kDma = kTile / (64 * QW * 16);  // direct loads per thread per K (or V) tile
+  static_assert(kThreads == 512 && kDma >= 1 && kTile % (64 * QW * 16) == 0 && BKV % 32 == 0, "shape");
+  static_assert(kBKV % BKV == 0, "split plan counts kBKV-key tiles");
+  static_assert(kSmem <= 160 * 1024, "LDS");
+};
 
 typedef __attribute__((address_space(3))) void attn_lds_t;
 typedef __attribute__((address_space(1))) void attn_glb_t;
@@ -356,15 +364,17 @@ __device__ __forceinline__ uint2 lds_tr16(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-__global__ void __launch_bounds__(kTrThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int QW, int G, int BKV>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
                const int32_t* __restrict__ act_off, int B, int N, int H, float scale_log2, int nsplit,
                int tiles_per_split, bf16* __restrict__ out, float* __restrict__ part_o,
                float* __restrict__ part_ml, int M_tot) {
+  using C = TrCfg<QW, G, BKV>;
   constexpr int Dh = kTrDh, E = 8, nKK = Dh / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[kTrSmem];
+  __shared__ __attribute__((aligned(1024))) char smem[C::kSmem];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
-  const int grp = wid >> 2, wq = wid & 3;   // key group; query block of the wave
+  const int grp = wid / QW, wq = wid % QW;   // key group; query block of the wave
   const int per_head = gridDim.x / H;
   int h, rest;
   if ((H & 7) == 0) {   // all workgroups of a head on one XCD (see attn_kernel)
@@ -377,10 +387,12 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   }
   const int split = rest % nsplit, slot = rest / nsplit;
   int row0 = 0, row_end = 0;
-  const int b = find_tile(act_off, B, slot, row0, row_end);
+  const int b = find_tile(act_off, B, slot, row0, row_end, C::kBQ);
   if (b < 0) return;   // uniform over the workgroup
-  const int t_begin = split * tiles_per_split;
-  const int t_end = min(N / kBKV, t_begin + tiles_per_split);
+  // the split plan counts kBKV-key tiles; this kernel walks BKV-key tiles
+  constexpr int TR = kBKV / BKV;
+  const int t_begin = split * tiles_per_split * TR;
+  const int t_end = min(N / kBKV, (split + 1) * tiles_per_split) * TR;
   const int HD = H * Dh;
 
   const int wrow0 = row0 + wq * 32;
@@ -393,29 +405,29 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     for (int kk = 0; kk < nKK; ++kk) qf[kk] = ld16(qr + (2 * kk + hl) * 16);
   }
 
-  // direct-load sources: load j of wave wq of a group fills LDS bytes [(4 j + wq) KB, +1 KB)
-  // of its tile = key rows 4 (4 j + wq) + lane / 16, stored position lane % 16
+  // direct-load sources: load j of wave wq of a group fills LDS bytes [(QW j + wq) KB, +1 KB)
+  // of its tile = key rows 4 (QW j + wq) + lane / 16, stored position lane % 16
   const size_t krow = (size_t)HD * 2;
   const char* kb0 = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
   const char* vb0 = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
-  uint32_t koff[kTrDma], voff[kTrDma];
+  uint32_t koff[C::kDma], voff[C::kDma];
 #pragma unroll
-  for (int j = 0; j < kTrDma; ++j) {
-    const int r = 4 * (4 * j + wq) + (lane >> 4), pos = lane & 15;
+  for (int j = 0; j < C::kDma; ++j) {
+    const int r = 4 * (QW * j + wq) + (lane >> 4), pos = lane & 15;
     koff[j] = (uint32_t)(r * krow) + swz<kTrRB>(r, pos) * 16;
     voff[j] = (uint32_t)(r * krow) + vswz(r, pos) * 16;
   }
-  auto stage_base = [&](int stage) { return smem + (stage * kTrGroups + grp) * kTrStage; };
+  auto stage_base = [&](int stage) { return smem + (stage * G + grp) * C::kStage; };
   auto issue = [&](int tile, int stage) {
     char* ks = stage_base(stage);
-    char* vs = ks + kTrTile;
-    const size_t t0 = (size_t)tile * kTrBKV * krow;
+    char* vs = ks + C::kTile;
+    const size_t t0 = (size_t)tile * BKV * krow;
 #pragma unroll
-    for (int j = 0; j < kTrDma; ++j)
-      __builtin_amdgcn_global_load_lds((attn_glb_t*)(kb0 + t0 + koff[j]), (attn_lds_t*)(ks + (4 * j + wq) * 1024), 16, 0, 0);
+    for (int j = 0; j < C::kDma; ++j)
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(kb0 + t0 + koff[j]), (attn_lds_t*)(ks + (QW * j + wq) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < kTrDma; ++j)
-      __builtin_amdgcn_global_load_lds((attn_glb_t*)(vb0 + t0 + voff[j]), (attn_lds_t*)(vs + (4 * j + wq) * 1024), 16, 0, 0);
+    for (int j = 0; j < C::kDma; ++j)
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)(vb0 + t0 + voff[j]), (attn_lds_t*)(vs + (QW * j + wq) * 1024), 16, 0, 0);
   };
 
   // transpose-read offsets inside a V tile: this lane of its 16-lane group reads
@@ -431,8 +443,8 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   float m_run = -INFINITY, l_run = 0.f;
 
   // iteration it: group g takes tile t_begin + 2 it + g (if inside the range)
-  const int n_it = (t_end - t_begin + kTrGroups - 1) / kTrGroups;
-  auto own_tile = [&](int it) { return t_begin + it * kTrGroups + grp; };
+  const int n_it = (t_end - t_begin + G - 1) / G;
+  auto own_tile = [&](int it) { return t_begin + it * G + grp; };
   if (n_it > 0 && own_tile(0) < t_end) issue(own_tile(0), 0);
   for (int it = 0; it < n_it; ++it) {
     const int stage = it & 1;
@@ -443,8 +455,8 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     if (it + 1 < n_it && own_tile(it + 1) < t_end) issue(own_tile(it + 1), stage ^ 1);
     if (!wave_live || own_tile(it) >= t_end) continue;
     const char* ks = stage_base(stage);
-    const char* vs = ks + kTrTile;
-    constexpr int NS = kTrBKV / 32;   // 32-key subtiles
+    const char* vs = ks + C::kTile;
+    constexpr int NS = BKV / 32;   // 32-key subtiles
     f32x16 sc[NS];
 #pragma unroll
     for (int sub = 0; sub < NS; ++sub) {
@@ -489,7 +501,7 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     l_run = l_run * alpha + ls;
     // O^T += V^T P^T, k-step m covers keys 16 m .. 16 m + 15 of the tile
 #pragma unroll
-    for (int m = 0; m < kTrBKV / 16; ++m) {
+    for (int m = 0; m < BKV / 16; ++m) {
       const int sub = m >> 1, r0 = (m & 1) * 8;
       u32x4 pb;
 #pragma unroll
@@ -510,10 +522,10 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   }
   __syncthreads();   // stages free
 
-  // group 1 hands its partial (O^T registers, m, l; lane and register order) to the
-  // group-0 wave of the same queries, which merges the two online softmaxes
-  float* mg = (float*)smem + wq * kTrMergeWave;
-  if (grp == 1) {
+  // groups 1 .. G-1 hand their partials (O^T registers, m, l; lane and register
+  // order) to the group-0 wave of the same queries, which merges the online softmaxes
+  if (grp > 0) {
+    float* mg = (float*)smem + ((grp - 1) * QW + wq) * kTrMergeWave;
 #pragma unroll
     for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
@@ -523,16 +535,19 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   }
   __syncthreads();
   if (grp == 0) {
-    const float m_o = mg[64 * (Dh / 2) + lane], l_o = mg[64 * (Dh / 2) + 64 + lane];
-    const float m_new = fmaxf(m_run, m_o);
-    const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f;
-    const float a1 = m_o > -INFINITY ? __builtin_amdgcn_exp2f(m_o - m_new) : 0.f;
+    for (int g2 = 1; g2 < G; ++g2) {
+      const float* mg = (const float*)smem + ((g2 - 1) * QW + wq) * kTrMergeWave;
+      const float m_o = mg[64 * (Dh / 2) + lane], l_o = mg[64 * (Dh / 2) + 64 + lane];
+      const float m_new = fmaxf(m_run, m_o);
+      const float a0 = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f;
+      const float a1 = m_o > -INFINITY ? __builtin_amdgcn_exp2f(m_o - m_new) : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < Dh / 32; ++dt)
+      for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] = oacc[dt][v] * a0 + mg[(dt * 16 + v) * 64 + lane] * a1;
-    l_run = l_run * a0 + l_o * a1;
-    m_run = m_new;
+        for (int v = 0; v < 16; ++v) oacc[dt][v] = oacc[dt][v] * a0 + mg[(dt * 16 + v) * 64 + lane] * a1;
+      l_run = l_run * a0 + l_o * a1;
+      m_run = m_new;
+    }
   }
   __syncthreads();   // merge area free for the output staging
 
@@ -618,21 +633,31 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
   }
 }
 
-static void attn_plan(int B, int N, int M_tot, int H, int& slots, int& nsplit, int& tps) {
-  slots = (M_tot + kBQ - 1) / kBQ + B;
+// Launch plan.  bq = queries per workgroup; shape 1 (bf16, head dim 128 only)
+// = 64-query workgroups with four key groups, for when 128-query workgroups
+// would leave the chip half idle and 64-query ones need no key split.  Splitting the keys over workgroups costs a
+// second pass over fp32 partials (several us), so it is used only when the
+// query tiles alone leave most of the chip idle.
+struct AttnPlan { int bq, shape, slots, nsplit, tps; };
+
+static AttnPlan attn_plan(int B, int N, int M_tot, int H, bool tr) {
+  AttnPlan p{};
   const int tiles = N / kBKV;
-  const int blocks = ((M_tot + kBQ - 1) / kBQ) * H;   // useful workgroups without a split
-  // Splitting the keys costs a second pass over fp32 partials (several us), so
-  // it is used only when the query tiles alone leave most of the chip idle.
-  nsplit = 1;
+  p.bq = kBQ;
+  p.shape = 0;
+  if (tr && ((M_tot + kBQ - 1) / kBQ) * H < 256 && ((M_tot + 63) / 64) * H >= 64) { p.bq = 64; p.shape = 1; }
+  const int blocks = ((M_tot + p.bq - 1) / p.bq) * H;   // useful workgroups without a split
+  p.nsplit = 1;
   if (blocks < 64)
-    while (blocks * nsplit < 256 && nsplit * 2 <= tiles / 2) nsplit *= 2;
-  tps = (tiles + nsplit - 1) / nsplit;
+    while (blocks * p.nsplit < 256 && p.nsplit * 2 <= tiles / 2) p.nsplit *= 2;
+  p.tps = (tiles + p.nsplit - 1) / p.nsplit;
+  p.slots = (M_tot + p.bq - 1) / p.bq + B;
+  return p;
 }
 
 size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh) {
-  int slots, nsplit, tps;
-  attn_plan(B, N, M_tot, H, slots, nsplit, tps);
+  const AttnPlan p0 = attn_plan(B, N, M_tot, H, false), p1 = attn_plan(B, N, M_tot, H, Dh == kTrDh);
+  const int nsplit = p0.nsplit > p1.nsplit ? p0.nsplit : p1.nsplit;
   if (nsplit == 1) return 256;
   return (size_t)nsplit * M_tot * H * (Dh + 2) * 4 + 256;
 }
@@ -641,19 +666,22 @@ template <typename T, int Dh>
 static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, const int32_t* act_off,
                                 int B, int N, int M_tot, int H, float scale, void* out, void* ws,
                                 hipStream_t s) {
-  int slots, nsplit, tps;
-  attn_plan(B, N, M_tot, H, slots, nsplit, tps);
+  const bool tr = sizeof(T) == 2 && Dh == kTrDh;
+  const AttnPlan p = attn_plan(B, N, M_tot, H, tr);
+  const int nsplit = p.nsplit, tps = p.tps;
   float* part_o = (float*)ws;
   float* part_ml = part_o + (size_t)nsplit * M_tot * H * Dh;
   const float sl2 = scale * kLog2e;
-  if (sizeof(T) == 2 && Dh == kTrDh)
-    hipLaunchKernelGGL(attn_tr_kernel, dim3(slots * H * nsplit), dim3(kTrThreads), 0, s,
-                       (const bf16*)q, (const bf16*)kc, (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps,
-                       (bf16*)out, part_o, part_ml, M_tot);
+  const dim3 grid(p.slots * H * nsplit);
+  if (tr && p.shape == 0)
+    hipLaunchKernelGGL((attn_tr_kernel<4, 2, 64>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
+                       (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml, M_tot);
+  else if (tr)
+    hipLaunchKernelGGL((attn_tr_kernel<2, 4, 32>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
+                       (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml, M_tot);
   else
-    hipLaunchKernelGGL((attn_kernel<T, Dh>), dim3(slots * H * nsplit), dim3(kAttnThreads), 0, s,
-                       (const T*)q, (const T*)kc, (const T*)vc, act_off, B, N, H, sl2, nsplit, tps,
-                       (T*)out, part_o, part_ml, M_tot);
+    hipLaunchKernelGGL((attn_kernel<T, Dh>), grid, dim3(kAttnThreads), 0, s, (const T*)q, (const T*)kc,
+                       (const T*)vc, act_off, B, N, H, sl2, nsplit, tps, (T*)out, part_o, part_ml, M_tot);
   if (nsplit > 1) {
     const int waves = M_tot * H;
     hipLaunchKernelGGL((attn_combine_kernel<T, Dh>), dim3((waves + 3) / 4), dim3(256), 0, s, part_o,
