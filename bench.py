@@ -244,6 +244,72 @@ def gpu_part(args):
     return out
 
 
+def e2e_loop(eps_list=(0.0, 0.01, 0.05), steps=128, N=512, n_prompt=128, unmask=3):
+    """The whole sampler loop on a 32-layer LLaDA-8B-shaped model with random-init weights (d=4096,
+    32 heads x 128, SwiGLU 12288, vocab 126464, bf16), batch 1, N=512 = 128 seeded prompt ids + 384
+    [MASK]; 128 steps, 3 unmasks per step by confidence, gate off.  eps = 0 is the dense reference
+    (nothing locks).  Reports per-step time against the active count M_t."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import workloads as W
+
+    dm = W.LLADA_8B
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    bf = torch.bfloat16
+
+    def randn(shape, std):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+
+    shapes = {"wq": (D, D), "wk": (D, D), "wv": (D, D), "wo": (D, D), "wg": (F, D), "wu": (F, D), "wd": (D, F)}
+    layers = [{k: randn(sh, 0.02) for k, sh in shapes.items()} for _ in range(dm.n_layers)]
+    embed = randn((dm.vocab, D), 0.02)
+    head = randn((dm.vocab, D), 0.02)
+    model = sl.DeviceModel(dtype=bf, n_layers=dm.n_layers, d=D, n_heads=H, head_dim=DH, ffn=F, vocab=dm.vocab,
+                           rms_eps=1e-5, rope_theta=1e4, layers=layers, embed=embed, lm_head=head, rope_n=N)
+    tok0 = W.prompt_tokens(dm, 1, N, n_prompt).reshape(-1)
+    out = {}
+    for eps in eps_list:
+        st = sl.DeviceState(model, 1, N, tok=torch.from_numpy(tok0.copy()).to(dev),
+                            cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).to(dev))
+        Ms, ms = [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            Ms.append(st.M_tot)
+            e0.record()
+            st.step(eps, -1.0, dm.mask_id, True, unmask)
+            e1.record()
+            ms.append((e0, e1))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [a.elapsed_time(b) for a, b in ms]
+        per_row = dm.n_layers * (8.0 * D * D + 6.0 * D * F + 4.0 * N * D) + 2.0 * D * dm.vocab
+        fl = per_row * sum(Ms)
+        by_M = {}
+        for M_t, t_ms in zip(Ms, ms):
+            by_M.setdefault(M_t, []).append(t_ms)
+        curve = [[M_t, round(float(np.median(v)), 3)] for M_t, v in sorted(by_M.items(), reverse=True)]
+        if len(curve) > 12:
+            curve = [curve[i] for i in np.linspace(0, len(curve) - 1, 12).round().astype(int)]
+        out["eps=%g" % eps] = {"ms_total": round(wall * 1e3, 2), "ms_per_step_mean": round(wall * 1e3 / steps, 3),
+                               "tokens_per_s": round((N - n_prompt) / wall, 1),
+                               "tflops": round(fl / wall / 1e12, 2), "M_first": Ms[0], "M_last": st.M_tot,
+                               "rows_computed": int(sum(Ms)), "ms_vs_M": curve}
+        del st
+    dense = out.get("eps=0", {}).get("rows_computed")
+    for k, v in out.items():
+        if dense:
+            v["flops_frac_vs_dense"] = round(v["rows_computed"] / dense, 4)
+    del layers, embed, head, model
+    torch.cuda.empty_cache()
+    return out
+
+
 def profile_kernels():
     """Launch only the two roofline kernels and a plain copy of known size, 3 times each
     (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; the copy calibrates the counters)."""
@@ -327,6 +393,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--no-e2e", action="store_true", help="skip the 32-layer sampler loop")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the roofline kernels and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -362,6 +429,7 @@ def main():
         "kernels_ms_M1024": res["kernels_ms_M1024"],
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
+        "e2e_loop": None if args.no_e2e else e2e_loop(),
         "cpu_baseline": None if args.no_cpu else cpu_part(args.cpu_seconds),
     }
     print(json.dumps(line), flush=True)
