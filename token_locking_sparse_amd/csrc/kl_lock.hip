@@ -17,18 +17,18 @@
 
 namespace sl {
 
-constexpr int kKLThreads = 256;
+constexpr int kKLThreads = 512;
 constexpr int kPartWords = 8;
 constexpr int kTailThreads = 1024;
 
 // ------------------------------------------------------------------ compaction
-// Ascending positions with locked == 0 of B sequences of N.  Every thread tests
-// 16 consecutive positions (one 16-byte load of the mask), the per-thread
-// counts are prefix-summed across the workgroup (wave shuffle scan, then the
-// wave totals through LDS), and each thread writes its run of active
-// positions.  s_w: LDS scratch of blockDim/64 ints.
-constexpr int kCompactPer = 16;
-
+// Ascending positions with locked == 0 of B sequences of N.  Each round gives
+// every thread `per` consecutive positions (4, 8 or 16, so that small totals
+// still spread over every wave), read with one load; the per-thread counts are
+// prefix-summed across the workgroup (DPP wave scan, then the wave totals
+// through LDS), and each thread writes its run of active positions.  One
+// division per thread and round locates its first position; later ones step.
+// s_w: LDS scratch of blockDim/64 ints.
 __device__ __forceinline__ int block_excl_scan(int c, int& total, int* s_w) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
   const int inc = wave_incl_scan(c);
@@ -45,33 +45,47 @@ __device__ __forceinline__ int block_excl_scan(int c, int& total, int* s_w) {
   return wpre + inc - c;
 }
 
-__device__ void block_compact(const uint8_t* locked, int B, int N, int32_t* act_idx,
-                              int32_t* act_off, int* s_w) {
-  const int tid = threadIdx.x;
-  const int total = B * N;
-  const bool aligned = ((uintptr_t)locked & 15) == 0;
-  int base = 0;
-  for (int r0 = 0; r0 < total; r0 += kCompactPer * blockDim.x) {
-    const int i0 = r0 + kCompactPer * tid;
-    uint32_t w[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // past the end: locked
-    if (aligned && i0 + kCompactPer <= total) {
-      const u32x4 v = ld16(locked + i0);
-      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-    } else {
-      for (int j = 0; j < kCompactPer; ++j) {
-        const uint32_t x = (i0 + j < total) ? (uint32_t)locked[i0 + j] : 0xffu;
-        w[j >> 2] = (w[j >> 2] & ~(0xffu << (8 * (j & 3)))) | (x << (8 * (j & 3)));
-      }
+// Flags f[i0 .. i0+per) with one load when aligned (per = 4, 8 or 16); bit j of
+// the result: position i0 + j is in range and unlocked.
+__device__ __forceinline__ uint32_t active_bits(const uint8_t* f, int i0, int per, int total) {
+  uint32_t w[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // past the end: locked
+  const bool whole = i0 + per <= total && ((uintptr_t)(f + i0) & (per - 1)) == 0;
+  if (whole && per == 16) {
+    const u32x4 v = ld16(f + i0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if (whole && per == 8) {
+    const uint2 v = *(const uint2*)(f + i0);
+    w[0] = v.x; w[1] = v.y;
+  } else if (whole) {
+    w[0] = *(const uint32_t*)(f + i0);
+  } else {
+    for (int j = 0; j < per; ++j) {
+      const uint32_t x = (i0 + j < total) ? (uint32_t)f[i0 + j] : 0xffu;
+      w[j >> 2] = (w[j >> 2] & ~(0xffu << (8 * (j & 3)))) | (x << (8 * (j & 3)));
     }
-    uint32_t am = 0;   // bit j: position i0 + j is active
+  }
+  uint32_t am = 0;
 #pragma unroll
-    for (int j = 0; j < kCompactPer; ++j)
-      am |= (((w[j >> 2] >> (8 * (j & 3))) & 0xffu) == 0u ? 1u : 0u) << j;
+  for (int j = 0; j < 16; ++j)
+    am |= (((w[j >> 2] >> (8 * (j & 3))) & 0xffu) == 0u ? 1u : 0u) << j;
+  return per == 16 ? am : am & ((1u << per) - 1u);
+}
+
+__device__ __forceinline__ void block_compact(const uint8_t* locked, int B, int N, int32_t* act_idx,
+                                              int32_t* act_off, int* s_w) {
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int total = B * N;
+  const int need = (total + bd - 1) / bd;
+  const int per = need <= 4 ? 4 : (need <= 8 ? 8 : 16);
+  int base = 0;
+  for (int r0 = 0; r0 < total; r0 += per * bd) {
+    const int i0 = r0 + per * tid;
+    const uint32_t am = active_bits(locked, i0, per, total);
     int tot;
     int pos = base + block_excl_scan(__popc(am), tot, s_w);
     if (i0 < total) {
       int q = i0 / N, rr = i0 - q * N;
-      for (int j = 0; j < kCompactPer && i0 + j < total; ++j) {
+      for (int j = 0; j < per && i0 + j < total; ++j) {
         if (rr == 0) act_off[q] = pos;
         if ((am >> j) & 1u) act_idx[pos++] = rr;
         if (++rr == N) { rr = 0; ++q; }
@@ -170,6 +184,8 @@ __device__ float block_select_kth(const uint32_t (&v)[kRegSel], bool from_regs, 
   for (int q = 0;; ++q) {
     uint32_t* h = sh.hist[q % 3];
     if (from_regs) {
+      // values sit densely in the first waves (kRegSel per thread); the rest skip
+      if (wid * 64 * kRegSel < o1 - o0)
 #pragma unroll
       for (int i = 0; i < kRegSel; ++i) {
         bool act = v[i] != kNoValue && (v[i] & pmask) == prefix;
@@ -202,8 +218,8 @@ __device__ float block_select_kth(const uint32_t (&v)[kRegSel], bool from_regs, 
 
 // Gate quantile, lock update, optional sampler, compaction — one workgroup.
 // A sequence of at most kRegSel * blockDim active rows is read once into
-// registers (positions, u, KL, then the candidate flags) and its select and
-// lock update run from there.
+// registers, kRegSel consecutive rows per thread (positions, u, KL, then the
+// candidate flags), and its select and lock update run from there.
 __device__ void tail_phase(const TailParams& p, TailShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
   const int bd = blockDim.x;
@@ -218,7 +234,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
     int pv[kRegSel];
 #pragma unroll
     for (int i = 0; i < kRegSel; ++i) {
-      const int m = o0 + tid + i * bd;
+      const int m = o0 + tid * kRegSel + i;   // dense: only the first waves hold values
       const bool in = regs && m < o1;
       uv[i] = in ? __float_as_uint(p.u[m]) : kNoValue;
       kv[i] = in ? p.kl[m] : INFINITY;
@@ -580,10 +596,117 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
 constexpr int kMaxSeg = 4;
 constexpr int kMergeRows = 2;
 
+// When the lock mask and the active rows fit in LDS, the tail issues every
+// global load it needs (partials or row statistics, positions, lock and
+// candidate flags) at once, and the select, lock update and compaction then
+// run on the LDS copies; the lock mask is written back at the end.  Each
+// dependent round trip to HBM costs microseconds, and the single workgroup
+// would otherwise make four of them.
+constexpr int kTailPos = 16 * kTailThreads;   // B*N held in LDS (16 flags per thread)
+constexpr int kTailRowsPerThread = 8;
+constexpr int kTailRows = kTailRowsPerThread * kTailThreads;
+struct TailLds {
+  uint8_t lk[kTailPos];   // lock flags, updated in place
+  uint8_t cd[kTailPos];   // candidate flags
+  float u[kTailRows];
+  float kl[kTailRows];
+  int32_t ai[kTailRows];
+};
+
+__device__ __forceinline__ u32x4 load_flags16(const uint8_t* f, int p0, int P, uint32_t fill) {
+  if (((uintptr_t)f & 15) == 0 && p0 + 16 <= P) return ld16(f + p0);
+  u32x4 w = {fill, fill, fill, fill};
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t x = p0 + j < P ? (uint32_t)f[p0 + j] : (fill & 0xffu);
+    w[j >> 2] = (w[j >> 2] & ~(0xffu << (8 * (j & 3)))) | (x << (8 * (j & 3)));
+  }
+  return w;
+}
+
+template <typename T, bool PREV>
+__device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n_seg, const float* part,
+                              TailShared& sh, TailLds& ls) {
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int P = tp.B * tp.N, Mt = tp.M_tot;
+  const int p0 = 16 * tid;
+  // every global load first
+  const u32x4 lkv = load_flags16(tp.locked, p0, P, 0x01010101u);
+  const u32x4 cdv = tp.cand ? load_flags16(tp.cand, p0, P, 0u) : u32x4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+  int32_t ai[kTailRowsPerThread];
+  float uu[kTailRowsPerThread], kk[kTailRowsPerThread];
+#pragma unroll
+  for (int j = 0; j < kTailRowsPerThread; ++j) {
+    const int m = tid + j * bd;
+    ai[j] = m < Mt ? tp.act_idx[m] : 0;
+    if (n_seg == 1) {
+      uu[j] = m < Mt ? rp.u[m] : 0.f;
+      kk[j] = m < Mt ? rp.kl[m] : 0.f;
+    }
+  }
+  Part x[kMergeRows][kMaxSeg];
+  if (n_seg > 1) {   // n_seg > 1 only when M_tot < kMergeRows * blockDim: one round
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const int r = min(tid + k * bd, Mt - 1);   // clamped: loads stay in bounds
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSeg; ++s2)
+        if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * Mt + r) * kPartWords);
+    }
+  }
+  // LDS copies
+  if (p0 < kTailPos) {
+    *(u32x4*)(ls.lk + p0) = lkv;
+    *(u32x4*)(ls.cd + p0) = cdv;
+  }
+#pragma unroll
+  for (int j = 0; j < kTailRowsPerThread; ++j) {
+    const int m = tid + j * bd;
+    ls.ai[m] = ai[j];
+    if (n_seg == 1) { ls.u[m] = uu[j]; ls.kl[m] = kk[j]; }
+  }
+  if (n_seg > 1) {
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      Part t = x[k][0];
+#pragma unroll
+      for (int s2 = 1; s2 < kMaxSeg; ++s2)
+        if (s2 < n_seg) t = combine(t, x[k][s2]);
+      const int r = tid + k * bd;
+      if (r < Mt) {
+        finish_row<PREV>(rp, t, r);
+        ls.u[r] = 1.f - 1.f / t.sa;
+        ls.kl[r] = PREV ? t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb) : INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+  TailParams q = tp;
+  q.locked = ls.lk;
+  q.cand = tp.cand ? ls.cd : nullptr;
+  q.u = ls.u;
+  q.kl = ls.kl;
+  q.act_idx = ls.ai;
+  tail_phase(q, sh);
+  __syncthreads();
+  // write the lock mask back
+  if (p0 < P) {
+    if (((uintptr_t)tp.locked & 15) == 0 && p0 + 16 <= P) {
+      st16(tp.locked + p0, *(const u32x4*)(ls.lk + p0));
+    } else {
+      for (int j = 0; j < 16 && p0 + j < P; ++j) tp.locked[p0 + j] = ls.lk[p0 + j];
+    }
+  }
+}
+
 template <typename T, bool PREV>
 __global__ void __launch_bounds__(kTailThreads)
 kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   __shared__ TailShared sh;
+  __shared__ __attribute__((aligned(16))) TailLds ls;
+  if ((long)tp.B * tp.N <= kTailPos && tp.M_tot <= kTailRows && tp.M_tot > 0) {
+    tail_from_lds<T, PREV>(rp, tp, n_seg, part, sh, ls);
+    return;
+  }
   if (n_seg > 1 && tp.M_tot > 0) {
     const int bd = blockDim.x;
     for (int r0 = 0; r0 < tp.M_tot; r0 += kMergeRows * bd) {
