@@ -600,34 +600,60 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   }
 }
 
-// Merge the split-KV partial softmaxes: one wave per (row, head).
+// Merge the split-KV partial softmaxes: one wave per (row, head).  Splits are
+// taken eight at a time, every load of a batch issued before any is used (one
+// memory round trip per batch instead of one per split), with a running max
+// across batches.
+constexpr int kCombineBatch = 8;
+
 template <typename T, int Dh>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit,
                     int M_tot, int H, T* __restrict__ out) {
+  constexpr int PER = (Dh + 63) / 64;   // output elements per lane
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= M_tot * H) return;
   const int m = w / H, h = w % H;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_ml[(((size_t)s * M_tot + m) * H + h) * 2]);
-  float L = 0.f;
-  float acc[(Dh + 63) / 64];
+  const size_t stride_ml = (size_t)M_tot * H * 2, stride_o = (size_t)M_tot * H * Dh;
+  const float* ml0 = part_ml + ((size_t)m * H + h) * 2;
+  const float* po0 = part_o + ((size_t)m * H + h) * Dh;
+  float mx = -INFINITY, L = 0.f;
+  float acc[PER];
 #pragma unroll
-  for (int i = 0; i < (Dh + 63) / 64; ++i) acc[i] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ml = part_ml + (((size_t)s * M_tot + m) * H + h) * 2;
-    const float wgt = (ml[0] > -INFINITY) ? __builtin_amdgcn_exp2f(ml[0] - mx) : 0.f;
-    L += ml[1] * wgt;
-    const float* po = part_o + (((size_t)s * M_tot + m) * H + h) * Dh;
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+    float ms[kCombineBatch], ls[kCombineBatch], os[kCombineBatch][PER];
 #pragma unroll
-    for (int i = 0; i < (Dh + 63) / 64; ++i) {
-      const int d = lane + 64 * i;
-      if (d < Dh) acc[i] += po[d] * wgt;
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int sidx = min(s0 + k, nsplit - 1);   // clamped: loads stay in bounds
+      ms[k] = ml0[sidx * stride_ml];
+      ls[k] = ml0[sidx * stride_ml + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int d = lane + 64 * i;
+        os[k][i] = d < Dh ? po0[sidx * stride_o + d] : 0.f;
+      }
     }
+    float bm = mx;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+      if (s0 + k < nsplit) bm = fmaxf(bm, ms[k]);
+    const float rescale = (mx > -INFINITY) ? __builtin_amdgcn_exp2f(mx - bm) : 0.f;
+    L *= rescale;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] *= rescale;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const float wgt = (s0 + k < nsplit && ms[k] > -INFINITY) ? __builtin_amdgcn_exp2f(ms[k] - bm) : 0.f;
+      L += ls[k] * wgt;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += os[k][i] * wgt;
+    }
+    mx = bm;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int i = 0; i < (Dh + 63) / 64; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int d = lane + 64 * i;
     if (d < Dh) out[(size_t)m * H * Dh + (size_t)h * Dh + d] = from_f32<T>(acc[i] * inv);
   }
