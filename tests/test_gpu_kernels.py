@@ -31,7 +31,8 @@ def _sl():
 
 # ------------------------------------------------------------------ compaction
 @pytest.mark.parametrize("B,N,p", [(1, 1, 0.5), (1, 4096, 0.6), (3, 1000, 0.3), (8, 2048, 0.5),
-                                   (2, 64, 0.0), (2, 64, 1.0), (5, 3001, 0.97), (1, 65536, 0.5)])
+                                   (2, 64, 0.0), (2, 64, 1.0), (5, 3001, 0.97), (1, 65536, 0.5),
+                                   (2, 3000, 0.5), (7, 9999, 0.4)])
 def test_compact_bit_exact(B, N, p):
     sl = _sl()
     say("compact", B, N, p)
@@ -150,6 +151,9 @@ KL_CASES = [
     (64, 1000, 2, 1.0, "bf16", 0.05, 0.5, -1, True, None),            # every row locked: M = 0
     (100, 126464, 1, 0.9, "bf16", 0.01, 0.5, 126463, True, None),     # full vocabulary, ragged chunks
     (4096, 256, 1, 0.2, "bf16", 0.0, 0.5, -1, True, None),            # eps = 0: nothing locks
+    (5000, 256, 1, 0.1, "f32", 0.05, 0.5, 255, True, None),           # tail in LDS, 4500 rows: select over LDS
+    (10000, 256, 2, 0.7, "bf16", 0.05, 0.5, -1, True, 0.8),           # B*N above the tail's LDS copies
+    (20000, 256, 1, 0.3, "bf16", 0.05, 0.5, -1, True, None),          # 14000 rows: tail reads global memory
 ]
 
 
