@@ -20,9 +20,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
-__device__ __forceinline__ float to_f32(float x) { return x; }
-
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
@@ -96,17 +93,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 }
 
 // ------------------------------------------------------------------ wave / block reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
@@ -162,20 +149,6 @@ __device__ __forceinline__ int seq_of_row(const int32_t* act_off, int B, int m) 
     if (act_off[mid] <= m) lo = mid; else hi = mid - 1;
   }
   return lo;
-}
-
-// Agent-scope atomics / loads used for cross-workgroup hand-off.
-__device__ __forceinline__ int atomic_add_agent(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_agent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sl
