@@ -186,11 +186,14 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
 
 /*
  * sl_gemm_plan — the launch sl_gemm would make for this shape: workgroup tile
- * rows x columns and the split-K factor (the residual epilogue alone splits K),
- * chosen by the library's cost model.  Writes nothing on error.  No device work.
+ * rows x columns, the split-K factor (the residual epilogue alone splits K) and
+ * the load path (*through_registers = 1: both operands' tiles go through vector
+ * registers into LDS, used when few rows stream a wide weight matrix; 0: direct
+ * global-to-LDS loads), chosen by the library's cost model.  through_registers
+ * may be NULL.  Writes nothing on error.  No device work.
  */
 sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* tile_m, int* tile_n,
-                       int* split_k);
+                       int* split_k, int* through_registers);
 
 /* One layer's weights, each stored [out_features][in_features] row-major. */
 typedef struct {

@@ -77,10 +77,14 @@ def test_gemm_plan_tiles_divide_and_only_residual_splits():
               (S.SL_EPI_RESIDUAL, f, d), (S.SL_EPI_LOGITS, d, v)]
     for epi, K, n in shapes:
         for M in (1, 64, 256, 512, 1024, 3000):
-            tm, tn, sk = S.sl_gemm_plan(torch.bfloat16, epi, M, K, n)
+            tm, tn, sk, vb = S.sl_gemm_plan(torch.bfloat16, epi, M, K, n, with_path=True)
             assert n % tn == 0 and tm in (64, 128, 256) and tn % 64 == 0
             assert sk >= 1 and (sk == 1 or epi == S.SL_EPI_RESIDUAL)
             assert (K * 2 // 128) // sk >= 1
+            assert vb in (0, 1) and (not vb or sk == 1)   # the register path streams the whole K
+            assert S.sl_gemm_plan(torch.float32, epi, M, K, n, with_path=True)[3] == 0
+    # wide outputs at few rows stream their weights through registers
+    assert S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_LOGITS, 16, d, v, with_path=True)[3] == 1
     # residual projections with few row tiles split K to fill the chip
     assert S.sl_gemm_plan(torch.bfloat16, S.SL_EPI_RESIDUAL, 64, f, d)[2] > 1
     with pytest.raises(S.SureLockError):
@@ -92,6 +96,6 @@ def test_gemm_parity_cases_cover_every_tile():
     import torch
 
     import token_locking_sparse_amd.surelock as S
-    from tests.test_gpu_kernels import ALL_TILES, GEMM_CASES
+    from tests.test_gpu_kernels import ALL_TILES, GEMM_CASES, tile_of
     epi = {"resid": S.SL_EPI_RESIDUAL, "swiglu": S.SL_EPI_SWIGLU, "qkv": S.SL_EPI_QKV_ROPE, "logits": S.SL_EPI_LOGITS}
-    assert {S.sl_gemm_plan(torch.bfloat16, epi[e], M, K, n)[:2] for e, M, K, n in GEMM_CASES} == ALL_TILES
+    assert {tile_of(S, epi[e], M, K, n) for e, M, K, n in GEMM_CASES} == ALL_TILES

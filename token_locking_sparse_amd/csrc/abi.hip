@@ -247,7 +247,7 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
 }
 
 sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* tile_m, int* tile_n,
-                       int* split_k) {
+                       int* split_k, int* through_registers) {
   g_err[0] = 0;
   sl_status st = check_dtype(dtype);
   if (st != SL_OK) return st;
@@ -256,7 +256,7 @@ sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* ti
   SL_REQUIRE(M > 0 && K > 0 && n_out > 0, SL_ERR_INVALID, "bad size");
   SL_REQUIRE(sl::gemm_supported(dtype, (sl::EpiKind)epilogue, n_out, K, 128, 2), SL_ERR_UNSUPPORTED,
              "unsupported GEMM shape (K=%d, n_out=%d)", K, n_out);
-  sl::gemm_plan(dtype, (sl::EpiKind)epilogue, M, K, n_out, tile_m, tile_n, split_k);
+  sl::gemm_plan(dtype, (sl::EpiKind)epilogue, M, K, n_out, tile_m, tile_n, split_k, through_registers);
   return SL_OK;
 }
 

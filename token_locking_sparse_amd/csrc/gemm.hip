@@ -15,6 +15,8 @@
 // and the second half its partner, so both land in the same lane and register.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -205,15 +207,38 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
   }
 }
 
+// Calls f(integral_constant<int, I>) for I in [I0, I1).
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
+
 // A wave's direct load fills 1 KB = 1024/RB consecutive rows: lane l lands at
 // row l/CPR, stored chunk l%CPR, so it fetches the logical chunk that the
 // swizzle stores there.  S-stage pipeline: tile kt+S-1 is requested while tile
 // kt is multiplied; one barrier per k-tile.
-template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI>
+//
+// VB (through registers): when few activation rows stream a large weight matrix
+// once, the direct-to-LDS path is the limit: it moves HBM data to a CU markedly
+// slower than ordinary vector loads (≈ 4.3 against ≈ 6 TB/s chip-wide).  With VB
+// both operands' tiles are fetched with 16-byte vector loads (non-temporal for
+// the weights) into a ring of S-1 register stages, each lane loading the 16
+// bytes its direct load would have placed, and written to one of two LDS stages
+// with ds_write before the k-tile's barrier.  The k-tile loop is unrolled by the
+// ring so every register slot is static, and every load is unconditional (past
+// the end it repeats the last tile into a slot that is never read): a
+// conditional load, or a direct-to-LDS load in the same kernel, makes the
+// compiler drain all loads before a slot is used.  Small LDS and register use
+// let two workgroups share a CU.
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI, bool VB>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, 2)))
 gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   using C = GemmCfg<T, BM, BN, WM, WN, RB, S>;
-  __shared__ __attribute__((aligned(1024))) char smem[S * C::StageBytes];
+  constexpr int kStages = VB ? 2 : S;   // LDS stages
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * C::StageBytes];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int wm = wid / WN, wn = wid % WN;
@@ -277,18 +302,10 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 
   constexpr int NDMA = C::ADma + C::BDma;
   constexpr int DPS = (NDMA + C::KS - 1) / C::KS;   // direct loads issued per k-step
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (kt0 + st < kt1) issue(kt0 + st, st, 0, NDMA);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // tile kt has landed when at most the (S-2) later tiles are still in flight
-    if (kt + S - 2 < kt1) wait_vmcnt<(S - 2) * NDMA>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    const bool pre = kt + S - 1 < kt1;
-    const int pre_stage = (kt + S - 1 - kt0) % S;
-    const char* as = smem + ((kt - kt0) % S) * C::StageBytes;
-    const char* bs = as + BM * RB;
+
+  // Multiply one k-tile held in LDS (A rows at `as`, B rows at `bs`); step(ks)
+  // issues that k-step's share of the loads in flight.
+  auto mma_tile = [&](const char* as, const char* bs, auto&& step) {
     u32x4 fa[2][C::FM], fb[2][C::FN];
     auto frags = [&](int ks, int buf) {
 #pragma unroll
@@ -306,9 +323,9 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      // this step's share of the next tile's direct loads, and the fragments of the
+      // this step's share of the next tile's loads, and the fragments of the
       // next k-step, are spread between this step's MFMAs
-      if (pre) issue(kt + S - 1, pre_stage, ks * DPS, (ks + 1) * DPS);
+      step(ks);
       if (ks + 1 < C::KS) frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
@@ -327,6 +344,58 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if constexpr (!VB) {
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (kt0 + st < kt1) issue(kt0 + st, st, 0, NDMA);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      // tile kt has landed when at most the (S-2) later tiles are still in flight
+      if (kt + S - 2 < kt1) wait_vmcnt<(S - 2) * NDMA>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();
+      const bool pre = kt + S - 1 < kt1;
+      const int pre_stage = (kt + S - 1 - kt0) % S;
+      const char* as = smem + ((kt - kt0) % S) * C::StageBytes;
+      mma_tile(as, as + BM * RB, [&](int ks) {
+        if (pre) issue(kt + S - 1, pre_stage, ks * DPS, (ks + 1) * DPS);
+      });
+    }
+  } else {
+    constexpr int RS = S - 1;   // register stages
+    u32x4 areg[RS][C::ADma], breg[RS][C::BDma];
+    // weights first, then activations, for every tile: "tile kt landed" is one count
+    auto vload = [&](int kt, int slot) {
+#pragma unroll
+      for (int j = 0; j < C::BDma; ++j) breg[slot][j] = ld16_stream(bp[j] + (size_t)kt * RB);
+#pragma unroll
+      for (int j = 0; j < C::ADma; ++j) areg[slot][j] = ld16(abase + aoff[j] + (size_t)kt * RB);
+    };
+    auto vtile = [&](const int kt, auto U) {
+      constexpr int u = decltype(U)::value;
+      wait_vmcnt<(S - 2) * NDMA>();   // tile kt landed; the S-2 later ones may be in flight
+      // stage kt&1 was last read two k-tiles ago, which every wave finished before the
+      // previous barrier
+      char* as = smem + ((kt - kt0) & 1) * C::StageBytes;
+      char* bs = as + BM * RB;
+#pragma unroll
+      for (int j = 0; j < C::ADma; ++j) st16(as + (j * C::NW + wid) * 1024 + lane * 16, areg[u][j]);
+#pragma unroll
+      for (int j = 0; j < C::BDma; ++j) st16(bs + (j * C::NW + wid) * 1024 + lane * 16, breg[u][j]);
+      vload(min(kt + S - 1, kt1 - 1), u);
+      __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0): stores done
+      barrier_no_fence();
+      mma_tile(as, bs, [](int) {});
+    };
+#pragma unroll
+    for (int st = 0; st < RS; ++st) vload(min(kt0 + st, kt1 - 1), st);
+    int kb = kt0;
+    for (; kb + RS <= kt1; kb += RS)
+      static_for<0, RS>([&](auto U) { vtile(kb + decltype(U)::value, U); });
+    static_for<0, RS - 1>([&](auto U) {
+      if (kb + decltype(U)::value < kt1) vtile(kb + decltype(U)::value, U);
+    });
   }
   __syncthreads();   // every wave is done with the pipeline's LDS
 
@@ -336,7 +405,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   // when the tile is larger than the pipeline's LDS; then every thread handles
   // runs of 8 (4 for the residual) consecutive outputs with 16-byte accesses.
   constexpr int LDW = BN + 8;
-  constexpr int SMEM = S * C::StageBytes;
+  constexpr int SMEM = kStages * C::StageBytes;
   constexpr int PR = (BM * LDW * 4 <= SMEM) ? BM : (BM / 2 * LDW * 4 <= SMEM) ? BM / 2 : (BM / 4 * LDW * 4 <= SMEM) ? BM / 4 : 32;
   static_assert(PR >= 32 && PR % 32 == 0 && BM % PR == 0 && PR * LDW * 4 <= SMEM, "epilogue pass");
   float* tile = (float*)smem;
@@ -358,7 +427,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 }
 
 // ------------------------------------------------------------------ dispatch
-template <typename T, int BM, int BN, int WM, int WN, int RB, int S>
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, bool VB = false>
 static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int split) {
   const int MT = (a.M + BM - 1) / BM, NT = a.Nv / BN;
   const int KI = a.K * (int)sizeof(T) / RB;
@@ -368,10 +437,10 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
   b.split_k = nsplit;
   const dim3 grid(MT * NT, 1, nsplit), block(64 * WM * WN);
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_QKV>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_SWIGLU>), grid, block, 0, s, b, MT, NT, kps); break;
-    case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_QKV, VB>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID, VB>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_SWIGLU, VB>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS, VB>), grid, block, 0, s, b, MT, NT, kps); break;
   }
   return hipGetLastError();
 }
@@ -379,38 +448,46 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
 // Tile shapes (4 or 8 waves; RB = k-tile row bytes; S = stages) and their
 // measured sustained rate per CU in multiply-adds per microsecond (bf16,
 // calibrated on the 4096 / 12288 projections at M = 64 .. 1024 on MI355X,
-// weights rotated over copies larger than the Infinity Cache).
-struct TileCfg { int BM, BN, RB, S; float rate; };
-constexpr int kNumCfgs = 9;
+// weights rotated over copies larger than the Infinity Cache); occ =
+// workgroups one CU holds at once, cap = chip-wide weight streaming rate.
+struct TileCfg { int BM, BN, RB, S; float rate; int occ; float cap; bool vb; };
+constexpr int kNumCfgs = 10;
+constexpr float kStreamCapBytesPerUs = 5.0e6f;  // weight streaming from HBM by direct-to-LDS loads
 static const TileCfg kCfgs[kNumCfgs] = {
-    {256, 256, 64, 4, 2.35e6f},   // 0: eight waves 2x4, wave tile 128x64
-    {256, 128, 128, 3, 2.17e6f},  // 1: eight waves 4x2, wave tile 64x64
-    {128, 256, 128, 3, 2.13e6f},  // 2: eight waves 2x4, wave tile 64x64
-    {128, 128, 128, 3, 1.55e6f},  // 3: four waves, wave tile 64x64
-    {128, 64, 128, 4, 1.25e6f},   // 4: four waves 4x1, wave tile 32x64
-    {256, 192, 64, 4, 1.90e6f},   // 5: four waves, wave tile 128x96 (256 tiles at M = 1024, N = 12288)
-    {128, 384, 64, 4, 1.87e6f},   // 6: four waves, wave tile 64x192
-    {64, 128, 128, 6, 1.06e6f},   // 7: four waves 1x4, wave tile 64x32: weight streaming at small M
-    {64, 64, 128, 8, 0.82e6f},    // 8: four waves 2x2, wave tile 32x32: weight streaming at small M
+    {256, 256, 64, 4, 2.35e6f, 1, kStreamCapBytesPerUs, false},   // 0: eight waves 2x4, wave tile 128x64
+    {256, 128, 128, 3, 2.17e6f, 1, kStreamCapBytesPerUs, false},  // 1: eight waves 4x2, wave tile 64x64
+    {128, 256, 128, 3, 2.13e6f, 1, kStreamCapBytesPerUs, false},  // 2: eight waves 2x4, wave tile 64x64
+    {128, 128, 128, 3, 1.55e6f, 1, kStreamCapBytesPerUs, false},  // 3: four waves, wave tile 64x64
+    {128, 64, 128, 4, 1.25e6f, 1, kStreamCapBytesPerUs, false},   // 4: four waves 4x1, wave tile 32x64
+    {256, 192, 64, 4, 1.90e6f, 1, kStreamCapBytesPerUs, false},   // 5: four waves, wave tile 128x96 (256 tiles at M = 1024, N = 12288)
+    {128, 384, 64, 4, 1.87e6f, 1, kStreamCapBytesPerUs, false},   // 6: four waves, wave tile 64x192
+    {64, 128, 128, 6, 1.06e6f, 1, kStreamCapBytesPerUs, false},   // 7: four waves 1x4, wave tile 64x32: weight streaming at small M
+    {64, 64, 128, 8, 0.82e6f, 1, kStreamCapBytesPerUs, false},    // 8: four waves 2x2, wave tile 32x32: weight streaming at small M
+    {64, 128, 128, 6, 1.06e6f, 2, 6.0e6f, true},                  // 9: as 7, through registers (VB), two per CU
 };
 constexpr int kCUs = 256;
-constexpr float kStreamCapBytesPerUs = 5.0e6f;  // weight streaming from HBM, whole chip
+constexpr float kCuBytesPerUs = 4.2e4f;        // what one CU pulls from HBM (latency bound)
 constexpr float kLoadLatencyUs = 1.0f;          // what a workgroup's S-1 tiles in flight amortise
 constexpr float kAtomicBytesPerUs = 1.5e6f;     // fp32 atomic adds of split-K partials
 constexpr float kLaunchUs = 2.0f;
 
-// Estimated time of a launch: compute over full waves of tiles, or streaming
-// the weights, whichever is longer.  A workgroup keeps (S-1) weight tiles
-// (BN x RB bytes each) in flight, so few workgroups stream slower than the chip
-// can; split-K adds its atomic traffic.
+// Estimated time of a launch: the compute of the most loaded CU, or streaming
+// the weights, whichever is longer.  The resident workgroups keep
+// (S-1) weight tiles (BN x RB bytes each) in flight, and each CU pulls at most
+// kCuBytesPerUs, so few workgroups stream slower than the chip can; split-K adds
+// its atomic traffic.
 static float est_us(const GemmArgs& a, int eb, int c, int split) {
   const TileCfg& g = kCfgs[c];
   const long MT = (a.M + g.BM - 1) / g.BM, NT = a.Nv / g.BN;
   const long blocks = MT * NT * split;
-  const long waves = (blocks + kCUs - 1) / kCUs;
-  const float comp = (float)waves * g.BM * g.BN * ((float)a.K / split) / g.rate;
-  float bw = (float)blocks * (g.S - 1) * g.BN * g.RB / kLoadLatencyUs;
-  if (bw > kStreamCapBytesPerUs) bw = kStreamCapBytesPerUs;
+  const long slots = (long)g.occ * kCUs;
+  const long per_cu = (blocks + kCUs - 1) / kCUs;   // tiles per CU (shared when occ > 1)
+  const float comp = (float)per_cu * g.BM * g.BN * ((float)a.K / split) / g.rate;
+  const long resident = blocks < slots ? blocks : slots;
+  const long cus = blocks < kCUs ? blocks : kCUs;
+  float bw = (float)resident * (g.S - 1) * g.BN * g.RB / kLoadLatencyUs;
+  if (bw > (float)cus * kCuBytesPerUs) bw = (float)cus * kCuBytesPerUs;
+  if (bw > g.cap) bw = g.cap;
   const float mem = (float)a.Nv * a.K * eb / bw;
   const float atom = split > 1 ? (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs : 0.f;
   return (comp > mem ? comp : mem) + atom + kLaunchUs;
@@ -422,9 +499,10 @@ static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& spli
   for (int c = 0; c < kNumCfgs; ++c) {
     const TileCfg& g = kCfgs[c];
     if (a.Nv % g.BN || (a.K * eb) % g.RB) continue;
+    if (g.vb && eb != 2) continue;   // the register path is calibrated for bf16 only
     const int KI = a.K * eb / g.RB;
     for (int sp = 1; sp <= 8; sp *= 2) {
-      if (sp > 1 && (epi != EPI_RESID || KI / sp < 8)) break;
+      if (sp > 1 && (epi != EPI_RESID || KI / sp < 8 || g.vb)) break;   // the register path streams whole K
       const float t = est_us(a, eb, c, sp);
       if (t < best) { best = t; cfg = c; split = sp; }
     }
@@ -453,11 +531,12 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
     case 6: return run_cfg<T, 128, 384, 2, 2, 64, 4>(epi, a, s, split);
     case 7: return run_cfg<T, 64, 128, 1, 4, 128, 6>(epi, a, s, split);
     case 8: return run_cfg<T, 64, 64, 2, 2, 128, 8>(epi, a, s, split);
+    case 9: return run_cfg<T, 64, 128, 1, 4, 128, 6, true>(epi, a, s, split);
   }
   return hipErrorInvalidValue;
 }
 
-void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split) {
+void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split, int* vb) {
   GemmArgs a{};
   a.M = M; a.K = K; a.Nv = Nv;
   int c, sp;
@@ -465,6 +544,7 @@ void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, i
   *bm = c >= 0 ? kCfgs[c].BM : 0;
   *bn = c >= 0 ? kCfgs[c].BN : 0;
   *split = c >= 0 ? sp : 0;
+  if (vb) *vb = c >= 0 && kCfgs[c].vb ? 1 : 0;
 }
 
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s) {

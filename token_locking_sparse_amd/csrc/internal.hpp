@@ -88,7 +88,8 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s);
 int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh);
-// Tile (rows, columns) and split-K the launcher picks for this shape.
-void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split);
+// Tile (rows, columns), split-K and load path (1: through registers) the launcher
+// picks for this shape; vb may be NULL.
+void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split, int* vb);
 
 }  // namespace sl

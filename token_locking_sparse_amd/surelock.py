@@ -88,7 +88,8 @@ def lib():
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
         "sl_gemm": (i, [i, i, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp, vp, i, i, vp]),
-        "sl_gemm_plan": (i, [i, i, i, i, i, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
+        "sl_gemm_plan": (i, [i, i, i, i, i, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
+                             C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -224,12 +225,14 @@ def sl_step(model: sl_model, state: sl_state, params: sl_step_params, ws, stream
 SL_EPI_QKV_ROPE, SL_EPI_RESIDUAL, SL_EPI_SWIGLU, SL_EPI_LOGITS = 0, 1, 2, 3
 
 
-def sl_gemm_plan(dtype, epilogue, M, K, n_out):
-    """(tile rows, tile columns, split-K) that sl_gemm launches for this shape."""
-    tm, tn, sk = C.c_int(0), C.c_int(0), C.c_int(0)
-    st = lib().sl_gemm_plan(dtype_code(dtype), int(epilogue), M, K, n_out, C.byref(tm), C.byref(tn), C.byref(sk))
+def sl_gemm_plan(dtype, epilogue, M, K, n_out, with_path=False):
+    """(tile rows, tile columns, split-K) that sl_gemm launches for this shape; with_path adds
+    1 when the tiles go through registers, 0 for direct global-to-LDS loads."""
+    tm, tn, sk, vb = C.c_int(0), C.c_int(0), C.c_int(0), C.c_int(0)
+    st = lib().sl_gemm_plan(dtype_code(dtype), int(epilogue), M, K, n_out, C.byref(tm), C.byref(tn), C.byref(sk),
+                            C.byref(vb))
     _check("sl_gemm_plan", st)
-    return tm.value, tn.value, sk.value
+    return (tm.value, tn.value, sk.value, vb.value) if with_path else (tm.value, tn.value, sk.value)
 
 
 def sl_gemm(epilogue, A, M, K, n_out, w0, w1=None, w2=None, out0=None, out1=None, out2=None, rope=None,
