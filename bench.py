@@ -9,6 +9,8 @@ One timed step = the hot path over one batch of synthetic input:
   * the KL-lock pass (N=4096, V=126464, 60 % already locked -> M=1639,
     eps=0.01, gate at the 0.5 quantile): vocabulary pass, gate, lock update,
     compaction.
+Also reported, outside `value`: the batched ragged step (8 x N=2048, one layer +
+LM head + KL-lock + compaction) and the 32-layer sampler loop.
 value = algorithmic TFLOP/s of the layer sweep (FLOPs of the four layer steps
 over their summed time).  Inputs are resident in HBM; weights rotate over 3
 copies and logits over 2 copies (each larger than the 256 MB Infinity Cache).
@@ -310,6 +312,120 @@ def e2e_loop(eps_list=(0.0, 0.01, 0.05), steps=128, N=512, n_prompt=128, unmask=
     return out
 
 
+def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
+    """The batched ragged workload: 8 sequences x N=2048, active fraction per sequence uniform on
+    [0.05, 0.8] (seeded), one LLaDA-8B-shaped layer + final norm + LM head (V=126464) + KL-lock
+    (eps 0.05, gate at each sequence's median u) + compaction, all in one sl_step at t = 1.  The
+    previous posterior is this step's own logits plus N(0, 0.05^2) drift, so the KL test passes
+    almost everywhere and the gate decides.  Also times, on the same active rows, the layer alone, the
+    LM head GEMM alone and the KL-lock pass alone.  Lock state is restored between timed steps
+    (outside the timed region)."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import token_locking_sparse_amd.surelock as S
+    import workloads as W
+
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    bf = torch.bfloat16
+    V = V_KL
+
+    def randn(shape, std):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+
+    Ms = W.ragged_ms(B, N, key=B * N)
+    acts = [W.choose_active(N, M, W.SEED_SETS, B * N * 64 + b) for b, M in enumerate(Ms)]
+    locked_np = np.concatenate([W.locked_from_active(N, a) for a in acts])
+    M_tot = int(sum(Ms))
+    shapes = {"wq": (D, D), "wk": (D, D), "wv": (D, D), "wo": (D, D), "wg": (F, D), "wu": (F, D), "wd": (D, F)}
+    layer = {k: randn(sh, 0.02) for k, sh in shapes.items()}
+    head = randn((V, D), 0.02)
+    common = dict(dtype=bf, n_layers=1, d=D, n_heads=H, head_dim=DH, ffn=F, vocab=V, rms_eps=1e-5, rope_theta=1e4,
+                  layers=[layer], rope_n=N)
+    model = sl.DeviceModel(lm_head=head, **common)
+    model_l = sl.DeviceModel(**common)
+    h_in = randn((B * N, D), 1.0)
+    kc = randn((1, B, N, H, DH), 1.0)
+    vc = randn((1, B, N, H, DH), 1.0)
+    locked0 = torch.from_numpy(locked_np).to(dev)
+    st = sl.DeviceState(model, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc,
+                        cand=torch.ones(B * N, dtype=torch.uint8, device=dev))
+    st_l = sl.DeviceState(model_l, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc)
+    assert st.M_tot == M_tot and st_l.M_tot == M_tot
+    ai0, ao0 = st.act_idx.clone(), st.act_off.clone()
+    # previous posterior: this step's logits (t = 0, no lock) plus drift, in buffer 0
+    st.step(0.0, do_lock=False)
+    for r0 in range(0, B * N, 1024):
+        blk = st.logits[0][r0:r0 + 1024]
+        blk.copy_((blk.float() + 0.05 * torch.randn(blk.shape, generator=g, device=dev)).to(bf))
+    st.t = 1
+    sst = st.struct()
+    sst.m_tot_host = None                     # no host copy of M: nothing to wait for inside the timing
+    p_full = S.sl_step_params(eps, gate, -1, 1, 0)
+    sst_l = st_l.struct()
+    p_layer = S.sl_step_params(0.0, -1.0, -1, 0, 0)
+    x = randn((M_tot, D), 1.0)
+    kl_o = {k: torch.empty(M_tot, device=dev) for k in ("kl", "u", "lse", "conf")}
+    kl_am = torch.empty(M_tot, dtype=torch.int32, device=dev)
+    kl_thr = torch.empty(B, device=dev)
+    kl_nai = torch.empty(B * N, dtype=torch.int32, device=dev)
+    kl_nao = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    kl_lk = locked0.clone()
+    kl_ws = torch.empty(sl.sl_kl_lock_workspace_size(B, N, M_tot, V), dtype=torch.uint8, device=dev)
+
+    def restore():
+        st.locked.copy_(locked0)
+        st.act_idx.copy_(ai0)
+        st.act_off.copy_(ao0)
+        kl_lk.copy_(locked0)
+
+    calls = {
+        "step": lambda: S.sl_step(model.s, sst, p_full, st.ws),
+        "layer": lambda: S.sl_step(model_l.s, sst_l, p_layer, st_l.ws),
+        "lm_head": lambda: sl.sl_gemm(sl.SL_EPI_LOGITS, x, M_tot, D, V, head, out0=st.logits[1], act_idx=ai0,
+                                      act_off=ao0, B=B, N=N),
+        "kl_lock": lambda: sl.sl_kl_lock(st.logits[1], st.logits[0], V, ai0, ao0, B, N, M_tot, None, eps, gate, -1,
+                                         True, kl_lk, kl_o["kl"], kl_o["u"], kl_o["lse"], kl_am, kl_o["conf"],
+                                         kl_thr, kl_nai, kl_nao, kl_ws),
+    }
+    ms = {}
+    for name, fn in calls.items():
+        es = []
+        for i in range(warmup + steps):
+            restore()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        ms[name] = float(np.mean([a.elapsed_time(b) for a, b in es[warmup:]]))
+    restore()
+    calls["step"]()
+    torch.cuda.synchronize()
+    M_after = int(st.act_off[B].item())
+    fl_layer = layer_flops(M_tot, N=N)
+    fl_head = 2.0 * M_tot * D * V
+    kb = kl_bytes(M_tot, N=B * N, V=V)
+    head_plan = sl.sl_gemm_plan(bf, sl.SL_EPI_LOGITS, M_tot, D, V)
+    out = {"B": B, "N": N, "M_b": Ms, "M_tot": M_tot, "M_after": M_after, "eps": eps, "gate": gate,
+           "ms_step": round(ms["step"], 4), "ms_layer": round(ms["layer"], 4), "ms_lm_head": round(ms["lm_head"], 4),
+           "ms_kl_lock": round(ms["kl_lock"], 4),
+           "step_tflops": round((fl_layer + fl_head) / (ms["step"] * 1e-3) / 1e12, 2),
+           "layer_tflops": round(fl_layer / (ms["layer"] * 1e-3) / 1e12, 2),
+           "lm_head": {"kernel": "gemm_kernel<bf16,%dx%d,split %d,EPI_LOGITS>" % head_plan, "bound": "mfma",
+                       "tflops": round(fl_head / (ms["lm_head"] * 1e-3) / 1e12, 2),
+                       "frac_mfma_peak": round(fl_head / (ms["lm_head"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+           "kl": {"bound": "hbm", "bytes": kb, "gbs": round(kb / (ms["kl_lock"] * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(kb / (ms["kl_lock"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    del st, st_l, model, model_l, layer, head, h_in, kc, vc, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def profile_kernels():
     """Launch only the two roofline kernels and a plain copy of known size, 3 times each
     (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; the copy calibrates the counters)."""
@@ -394,6 +510,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-e2e", action="store_true", help="skip the 32-layer sampler loop")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched ragged step")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the roofline kernels and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -429,6 +546,7 @@ def main():
         "kernels_ms_M1024": res["kernels_ms_M1024"],
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
+        "batched_step": None if args.no_batched else batched_step(),
         "e2e_loop": None if args.no_e2e else e2e_loop(),
         "cpu_baseline": None if args.no_cpu else cpu_part(args.cpu_seconds),
     }

@@ -371,3 +371,93 @@ def test_batched_ragged_step(dm, B, N, gate):
     ri, ro = O.active_set(g_locked, B, N)
     np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
     np.testing.assert_array_equal(st.act_idx[:st.M_tot].cpu().numpy(), ri)
+
+
+@pytest.mark.slow
+def test_batched_step_full_shape_with_head():
+    """The batched ragged workload at full size: 8 sequences x N=2048 (active fraction per sequence
+    uniform on [0.05, 0.8]), one LLaDA-8B-shaped layer, final norm, LM head over V=126464, KL-lock
+    (eps 0.05, gate at each sequence's median u) and compaction in one sl_step at t = 1.
+
+    Teacher-forced: the previous posterior is the oracle's own logits of this step plus N(0, 0.05^2)
+    drift, so every KL is near 0.00125 and the gate decides the locks.  Logits go through one layer of
+    bf16 intermediates, so they are held to the hidden-row bound (relative L2 1e-2, no element beyond
+    7 rms).  KL within 1e-3; u and lse within the bound their definitions give from the largest logit
+    error.  The gate, lock and compaction are checked exactly against the GPU's own statistics, and
+    against the oracle's decisions except where the gap between u and the gate threshold is inside
+    what the u error can move."""
+    sl = _sl()
+    dm = W.LLADA_LAYER
+    B, N, eps, gate = 8, 2048, 0.05, 0.5
+    Ms = W.ragged_ms(B, N, key=B * N)
+    say("batched full step with LM head", Ms)
+    case = W.layer_case(dm, N, Ms, key=B * N)
+    M = case.M_tot
+    Wnp = W.layer_weights(dm, 0)
+    head = W.lm_head_weights(dm)
+    locked = np.ones(B * N, np.uint8)
+    for b in range(B):
+        locked[b * N + case.act_idx[case.act_off[b]:case.act_off[b + 1]]] = 0
+    rows_seq = O.seq_of_rows(case.act_off)
+    glob = rows_seq * N + case.act_idx.astype(np.int64)
+    # oracle: hidden rows of the active set, final norm and LM head, then the posterior statistics
+    od = _odims(dm)
+    W64 = {k: O.widen(v, "bf16") for k, v in Wnp.items()}
+    ost = O.OracleState(B=B, N=N, t=0, locked=locked.copy(), kc=[O.widen(case.k_cache, "bf16")],
+                        vc=[O.widen(case.v_cache, "bf16")], h_in=O.widen(case.h_in, "bf16"))
+    h = O.step(O.OracleModel(od, 1, lambda l: W64), ost, 0.0, -1.0, do_lock=False).h
+    del W64, ost
+    z = O.rmsnorm(h, dm.rms_eps) @ O.widen(head, "bf16").T
+    prev_st = W.to_storage(z.astype(np.float32) + W.normal(W.rng(W.SEED_DRIFT, 4343), z.shape, 0.05), "bf16")
+    prev64 = O.widen(prev_st, "bf16")
+    ref = O.posterior_stats(z, prev64)
+    del prev64
+    lr = O.lock_update(locked, case.act_idx, case.act_off, B, N, ref.kl, ref.u, None, eps, gate, True)
+    say("oracle done: new locks %d" % int(lr.new_lock.sum()))
+    # GPU: the same step at t = 1 with that previous posterior in buffer 0
+    model = _dev_model(dm, [Wnp], None, head, rope_n=N)
+    H, Dh = dm.n_heads, dm.head_dim
+    st = sl.DeviceState(model, B, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, "bf16"),
+                        k_cache=dev(case.k_cache, "bf16").reshape(1, B, N, H, Dh),
+                        v_cache=dev(case.v_cache, "bf16").reshape(1, B, N, H, Dh),
+                        cand=torch.ones(B * N, dtype=torch.uint8, device="cuda"))
+    assert st.M_tot == M
+    gi = torch.from_numpy(glob).cuda()
+    st.logits[0].index_copy_(0, gi, dev(prev_st, "bf16"))
+    del prev_st
+    st.t = 1
+    st.step(eps, gate, -1, True, 0)
+    torch.cuda.synchronize()
+    cur = host64(st.logits[1].index_select(0, gi))
+    l2, rms, mx = check_hidden(cur, z, 1e-2, "logits")
+    say("logits: rel L2 %.3e rms %.3e max %.3e" % (l2, rms, mx))
+    dz = float(np.max(np.abs(cur - z)))
+    del cur, z
+    kl, u, lse = st.kl[:M].cpu().numpy(), st.u[:M].cpu().numpy(), st.lse[:M].cpu().numpy()
+    assert np.max(np.abs(kl - ref.kl)) <= KL_BAND
+    # lse moves by at most the largest logit error; u = 1 - exp(max z - lse) by at most twice that
+    assert np.max(np.abs(lse - ref.lse)) <= dz + 1e-4
+    du = float(np.max(np.abs(u - ref.u)))
+    assert du <= 2 * dz + 1e-5
+    # gate, lock and compaction, exactly, on the GPU's own statistics
+    thr = st.gate_thr.cpu().numpy()
+    g_locked = st.locked.cpu().numpy()
+    new = np.zeros(M, dtype=bool)
+    for b in range(B):
+        s_ = slice(case.act_off[b], case.act_off[b + 1])
+        kth = int(np.floor(np.float32(gate) * (Ms[b] - 1)))
+        assert thr[b] == np.sort(u[s_])[kth]
+        new[s_] = (kl[s_] <= np.float32(eps)) & (u[s_] <= thr[b])
+    want = locked.copy()
+    want[glob[new]] = 1
+    np.testing.assert_array_equal(g_locked, want)
+    ri, ro = O.active_set(g_locked, B, N)
+    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(st.act_idx[:int(ro[-1])].cpu().numpy(), ri)
+    # against the oracle's decisions: a row may differ only where |u - q| is within what the errors allow
+    band = 2 * du + np.abs(thr - lr.gate_thr)[rows_seq]
+    diff = np.flatnonzero(new != lr.new_lock)
+    near = np.abs(ref.u - lr.gate_thr[rows_seq]) <= band
+    say("lock decisions: gpu %d oracle %d differing %d (u error %.2e)" % (int(new.sum()), int(lr.new_lock.sum()),
+                                                                       len(diff), du))
+    assert np.all(near[diff])
