@@ -154,7 +154,10 @@ def lock_update(locked: np.ndarray, act_idx: np.ndarray, act_off: np.ndarray, B:
     active row).  Locks are never undone, so the active set only shrinks
     (zhaoyang97 notes, "永久锁定机制" and "关键发现").
     Readings: eps <= 0 disables locking; gate_m < 0 disables the gate;
-    without a previous posterior nothing locks.
+    without a previous posterior nothing locks.  The notes page's ablations
+    (zhaoyang97 notes, 消融实验) are settings of the same rule: KL only is
+    the gate off; confidence gate only is eps = +inf (the KL test always
+    passes) with the gate on.
     """
     locked = np.array(locked, dtype=np.uint8, copy=True)
     M = len(act_idx)
@@ -236,7 +239,7 @@ class OracleDims:
 
 
 def layer_forward(h: np.ndarray, pos: np.ndarray, W: dict, Kc: np.ndarray, Vc: np.ndarray,
-                  dm: OracleDims) -> np.ndarray:
+                  dm: OracleDims, attend_locked: bool = True) -> np.ndarray:
     """One transformer block for the active rows of one sequence; updates the cache in place.
 
     Active rows compute their Q projection and FFN; their fresh K/V are written
@@ -245,6 +248,9 @@ def layer_forward(h: np.ndarray, pos: np.ndarray, W: dict, Kc: np.ndarray, Vc: n
     lock action: K/V cached for every layer, Q projection and FFN skipped for
     locked rows).  Block: pre-RMSNorm, QKV + RoPE, attention, O projection +
     residual, pre-RMSNorm, SwiGLU FFN + residual.
+    attend_locked=False is the "no KV cache" ablation of the notes page
+    (zhaoyang97 notes, 消融实验): locked positions cannot be attended, so the
+    active rows attend over the active positions only (their fresh K/V).
     h: [M][d] float64; W: float64 [out][in] matrices; Kc, Vc: [N][H][Dh].
     """
     M = h.shape[0]
@@ -257,7 +263,11 @@ def layer_forward(h: np.ndarray, pos: np.ndarray, W: dict, Kc: np.ndarray, Vc: n
     k = rope(k, pos, dm.rope_theta)
     Kc[pos] = k
     Vc[pos] = v
-    o = attention(q, Kc, Vc, 1.0 / np.sqrt(Dh)).reshape(M, H * Dh)
+    if attend_locked:
+        o = attention(q, Kc, Vc, 1.0 / np.sqrt(Dh))
+    else:
+        o = attention(q, Kc[pos], Vc[pos], 1.0 / np.sqrt(Dh))
+    o = o.reshape(M, H * Dh)
     h = h + o @ W["wo"].T
     x2 = rmsnorm(h, dm.rms_eps)
     a = silu(x2 @ W["wg"].T) * (x2 @ W["wu"].T)
@@ -300,7 +310,8 @@ class StepOut:
 
 
 def step(model: OracleModel, st: OracleState, eps: float, gate_m: float,
-         do_lock: bool = True, mask_id: int = -1, prev_logits: np.ndarray | None = None) -> StepOut:
+         do_lock: bool = True, mask_id: int = -1, prev_logits: np.ndarray | None = None,
+         attend_locked: bool = True) -> StepOut:
     """One SureLock iteration on the oracle state (modified in place).
 
     1. gather A_t; 2. layer-0 input for the active rows (embedding of the
@@ -311,6 +322,7 @@ def step(model: OracleModel, st: OracleState, eps: float, gate_m: float,
     so a locked row keeps the posterior of its lock step (zhaoyang97 notes,
     "永久锁定机制": p_hat_t = p_{t*}); 9. next active set.
     prev_logits ([M_tot][V]) overrides st.post as the previous posterior.
+    attend_locked=False: the no-KV-cache ablation (see layer_forward).
     """
     dm = model.dims
     B, N = st.B, st.N
@@ -327,7 +339,7 @@ def step(model: OracleModel, st: OracleState, eps: float, gate_m: float,
         for b in range(B):
             sl = slice(act_off[b], act_off[b + 1])
             if act_off[b + 1] > act_off[b]:
-                h[sl] = layer_forward(h[sl], act_idx[sl], W, st.kc[l][b], st.vc[l][b], dm)
+                h[sl] = layer_forward(h[sl], act_idx[sl], W, st.kc[l][b], st.vc[l][b], dm, attend_locked)
     out = StepOut(act_idx, act_off, h, None, None, None)
     if model.lm_head is None:
         return out
@@ -392,7 +404,8 @@ class LoopRecord:
 
 
 def run_loop(model: OracleModel, tok0: np.ndarray, B: int, N: int, T: int, eps: float,
-             gate_m: float, unmask_k: int, on_step: Callable | None = None) -> list:
+             gate_m: float, unmask_k: int, on_step: Callable | None = None,
+             attend_locked: bool = True) -> list:
     """The MDLM sampler loop with SureLock: T steps of (SureLock step, unmask k).
 
     Candidates at step t are the positions already unmasked in the step's
@@ -409,7 +422,7 @@ def run_loop(model: OracleModel, tok0: np.ndarray, B: int, N: int, T: int, eps: 
     recs = []
     for t in range(T):
         st.t = t
-        out = step(model, st, eps, gate_m, True, mask_id)
+        out = step(model, st, eps, gate_m, True, mask_id, attend_locked=attend_locked)
         sampler_unmask(st.tok, st.cand, out.act_idx, out.act_off, N, out.stats.argmax,
                        out.stats.conf, mask_id, unmask_k)
         rec = LoopRecord(t, len(out.act_idx), int(out.lock.new_lock.sum()), out.act_idx, out.act_off,

@@ -30,11 +30,12 @@ def rope_complex(x: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tens
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def dense_block(h: torch.Tensor, W: dict, n_heads: int, eps: float, theta: float):
-    """h [N][d] -> (h_out [N][d], k [N][H][Dh], v [N][H][Dh])."""
+def dense_block(h: torch.Tensor, W: dict, n_heads: int, eps: float, theta: float, pos=None):
+    """h [N][d] -> (h_out [N][d], k [N][H][Dh], v [N][H][Dh]); pos = the rows' RoPE positions
+    (default 0 .. N-1)."""
     N, d = h.shape
     Dh = d // n_heads
-    pos = torch.arange(N)
+    pos = torch.arange(N) if pos is None else torch.as_tensor(np.asarray(pos, dtype=np.int64))
     x = F.rms_norm(h, (d,), eps=eps)
     q = (x @ _t(W["wq"]).T).view(N, n_heads, Dh)
     k = (x @ _t(W["wk"]).T).view(N, n_heads, Dh)

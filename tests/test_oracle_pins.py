@@ -270,6 +270,55 @@ def test_layer_equals_dense_block():
     pin_layer_dense()
 
 
+def pin_no_kv_cache_ablation():
+    """The no-KV-cache ablation (zhaoyang97 notes, 消融实验: locked positions cannot be attended)
+    equals a dense block over the active rows alone at their own positions, and never reads the
+    cache rows of locked positions (NaN there changes nothing)."""
+    dm, od, layers, _, _ = _tiny_model(n_layers=1)
+    N = 12
+    h = np.random.default_rng(9).normal(size=(N, od.d))
+    sub = np.array([1, 2, 6, 7, 10])
+    Kc = np.full((N, od.n_heads, od.head_dim), np.nan); Vc = Kc.copy()
+    out = O.layer_forward(h[sub], sub, layers[0], Kc, Vc, od, attend_locked=False)
+    ref, k, v = dense_block(torch.tensor(h[sub]), layers[0], od.n_heads, od.rms_eps, od.rope_theta, pos=sub)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(Kc[sub], k.numpy(), rtol=1e-11, atol=1e-11)
+    # with every position active the ablation is the ordinary layer
+    Kc2 = np.zeros((N, od.n_heads, od.head_dim)); Vc2 = np.zeros_like(Kc2)
+    Kc3, Vc3 = Kc2.copy(), Vc2.copy()
+    np.testing.assert_allclose(O.layer_forward(h, np.arange(N), layers[0], Kc2, Vc2, od, attend_locked=False),
+                               O.layer_forward(h, np.arange(N), layers[0], Kc3, Vc3, od), rtol=1e-13, atol=1e-13)
+
+
+def test_no_kv_cache_ablation():
+    pin_no_kv_cache_ablation()
+
+
+def test_gate_only_rule_is_eps_infinity():
+    """Confidence gate only (zhaoyang97 notes, 消融实验) as eps = +inf with the gate on: candidates
+    lock exactly when u <= q_m (brute force); KL only is the gate off."""
+    rng = np.random.default_rng(21)
+    B, N = 2, 40
+    locked = (rng.random(B * N) < 0.3).astype(np.uint8)
+    ai, ao = O.active_set(locked, B, N)
+    M = len(ai)
+    kl = rng.random(M) * 0.2
+    u = rng.random(M)
+    cand = (rng.random(B * N) < 0.7).astype(np.uint8)
+    lr = O.lock_update(locked, ai, ao, B, N, kl, u, cand, np.inf, 0.5, True)
+    for b in range(B):
+        rows = range(ao[b], ao[b + 1])
+        us = sorted(u[r] for r in rows)
+        q = us[int(np.floor(0.5 * (len(us) - 1)))]
+        for r in rows:
+            g = b * N + ai[r]
+            assert lr.new_lock[r] == bool(cand[g] and u[r] <= q)
+    # KL only: gate off, eps finite
+    lr2 = O.lock_update(locked, ai, ao, B, N, kl, u, cand, 0.1, -1.0, True)
+    glob = O.seq_of_rows(ao) * N + ai
+    np.testing.assert_array_equal(lr2.new_lock, (cand[glob] != 0) & (kl <= 0.1))
+
+
 def test_eps_zero_step_equals_dense_sampler():
     dm, od, layers, emb, head = _tiny_model()
     B, N, T = 2, 16, 4
@@ -380,3 +429,11 @@ def test_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "silu", lambda g: g / (1 + np.exp(g)))  # wrong sign in the sigmoid
     _expect_fail(pin_layer_dense)
     monkeypatch.setattr(O, "silu", good_silu)
+
+    good_layer = O.layer_forward
+
+    def layer_attends_everything(h, pos, W, Kc, Vc, dm, attend_locked=True):   # ablation flag ignored
+        return good_layer(h, pos, W, Kc, Vc, dm)
+    monkeypatch.setattr(O, "layer_forward", layer_attends_everything)
+    _expect_fail(pin_no_kv_cache_ablation)
+    monkeypatch.setattr(O, "layer_forward", good_layer)
