@@ -174,6 +174,22 @@ def gpu_part(args):
     ms_kl = float(np.mean([evk[i][0].elapsed_time(evk[i][1]) for i in range(args.warmup, n_it)]))
     M_after = int(kl_nao[1].item())
 
+    # ---------------- the no-KV-cache ablation on the same active sets: attention over the M
+    # active positions instead of all N (outside `value`)
+    p_abl = S.sl_step_params(0.0, -1.0, -1, 0, 0, 1)
+    ms_abl = {}
+    for M in MS:
+        st, sst = states[M]
+        es = []
+        for i in range(args.warmup + args.steps):
+            e0, e1 = ev(), ev()
+            e0.record()
+            S.sl_step(models[i % 3].s, sst, p_abl, st.ws)
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        ms_abl[M] = float(np.mean([a.elapsed_time(b) for a, b in es[args.warmup:]]))
+
     # ---------------- dominant kernel alone: the FFN gate/up GEMM + SwiGLU at M = 1024
     Mg = 1024
     xa = randn((Mg, D))
@@ -233,6 +249,7 @@ def gpu_part(args):
         "kl_lock": {"ms": round(ms_kl, 4), "gbs": round(kb / (ms_kl * 1e-3) / 1e9, 1), "bytes": kb, "M": M_kl,
                     "M_after": M_after, "frac_hbm_peak": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_ms_M1024": {k: round(v, 4) for k, v in br.items()},
+        "ablation_no_kv_cache_ms": {str(M): round(v, 4) for M, v in ms_abl.items()},
         "roofline": {"kernel": "gemm_kernel<bf16,%dx%d,split %d,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)" % gu_plan,
                      "bound": "mfma",
                      "achieved": round(fl_gu / (ms_gu * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -246,11 +263,18 @@ def gpu_part(args):
     return out
 
 
-def e2e_loop(eps_list=(0.0, 0.01, 0.05), steps=128, N=512, n_prompt=128, unmask=3):
+SURELOCK_RUNS = (("eps=0", 0.0, -1.0, False), ("eps=0.01", 0.01, -1.0, False), ("eps=0.05", 0.05, -1.0, False))
+# the notes page's ablations: confidence gate only (eps = +inf, gate at the median u), and
+# no KV cache (positions locked before a step are not attended)
+ABLATION_RUNS = (("gate_only m=0.5", math.inf, 0.5, False), ("no_kv_cache eps=0.05", 0.05, -1.0, True))
+
+
+def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1):
     """The whole sampler loop on a 32-layer LLaDA-8B-shaped model with random-init weights (d=4096,
-    32 heads x 128, SwiGLU 12288, vocab 126464, bf16), batch 1, N=512 = 128 seeded prompt ids + 384
-    [MASK]; 128 steps, 3 unmasks per step by confidence, gate off.  eps = 0 is the dense reference
-    (nothing locks).  Reports per-step time against the active count M_t."""
+    32 heads x 128, SwiGLU 12288, vocab 126464, bf16), B sequences of N=512 = 128 seeded prompt ids +
+    384 [MASK]; 128 steps, 3 unmasks per sequence per step by confidence.  Each run is (name, eps,
+    gate quantile or -1 for off, no-KV-cache ablation); eps = 0 is the dense reference (nothing
+    locks).  Reports per-step time against the active count M_t (summed over the batch)."""
     import numpy as np
     import torch
 
@@ -272,10 +296,10 @@ def e2e_loop(eps_list=(0.0, 0.01, 0.05), steps=128, N=512, n_prompt=128, unmask=
     head = randn((dm.vocab, D), 0.02)
     model = sl.DeviceModel(dtype=bf, n_layers=dm.n_layers, d=D, n_heads=H, head_dim=DH, ffn=F, vocab=dm.vocab,
                            rms_eps=1e-5, rope_theta=1e4, layers=layers, embed=embed, lm_head=head, rope_n=N)
-    tok0 = W.prompt_tokens(dm, 1, N, n_prompt).reshape(-1)
+    tok0 = W.prompt_tokens(dm, B, N, n_prompt).reshape(-1)
     out = {}
-    for eps in eps_list:
-        st = sl.DeviceState(model, 1, N, tok=torch.from_numpy(tok0.copy()).to(dev),
+    for name, eps, gate, no_kv in runs:
+        st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).to(dev),
                             cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).to(dev))
         Ms, ms = [], []
         torch.cuda.synchronize()
@@ -284,29 +308,33 @@ def e2e_loop(eps_list=(0.0, 0.01, 0.05), steps=128, N=512, n_prompt=128, unmask=
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             Ms.append(st.M_tot)
             e0.record()
-            st.step(eps, -1.0, dm.mask_id, True, unmask)
+            st.step(eps, gate, dm.mask_id, True, unmask, no_kv_cache=no_kv)
             e1.record()
             ms.append((e0, e1))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = [a.elapsed_time(b) for a, b in ms]
-        per_row = dm.n_layers * (8.0 * D * D + 6.0 * D * F + 4.0 * N * D) + 2.0 * D * dm.vocab
-        fl = per_row * sum(Ms)
+        # per row: the layers' projections and FFN, attention over N keys (over the M_t / B active
+        # positions of its sequence when locked positions are not attended), and the LM head
+        per_row = dm.n_layers * (8.0 * D * D + 6.0 * D * F) + 2.0 * D * dm.vocab
+        fl = sum(M_t * (per_row + dm.n_layers * 4.0 * (M_t / B if no_kv else N) * D) for M_t in Ms)
         by_M = {}
         for M_t, t_ms in zip(Ms, ms):
             by_M.setdefault(M_t, []).append(t_ms)
         curve = [[M_t, round(float(np.median(v)), 3)] for M_t, v in sorted(by_M.items(), reverse=True)]
         if len(curve) > 12:
             curve = [curve[i] for i in np.linspace(0, len(curve) - 1, 12).round().astype(int)]
-        out["eps=%g" % eps] = {"ms_total": round(wall * 1e3, 2), "ms_per_step_mean": round(wall * 1e3 / steps, 3),
-                               "tokens_per_s": round((N - n_prompt) / wall, 1),
+        out[name] = {"ms_total": round(wall * 1e3, 2), "ms_per_step_mean": round(wall * 1e3 / steps, 3),
+                               "tokens_per_s": round(B * (N - n_prompt) / wall, 1),
                                "tflops": round(fl / wall / 1e12, 2), "M_first": Ms[0], "M_last": st.M_tot,
-                               "rows_computed": int(sum(Ms)), "ms_vs_M": curve}
+                               "rows_computed": int(sum(Ms)), "flops": fl, "ms_vs_M": curve}
         del st
-    dense = out.get("eps=0", {}).get("rows_computed")
+    dense = out.get("eps=0")
     for k, v in out.items():
         if dense:
-            v["flops_frac_vs_dense"] = round(v["rows_computed"] / dense, 4)
+            v["rows_frac_vs_dense"] = round(v["rows_computed"] / dense["rows_computed"], 4)
+            v["flops_frac_vs_dense"] = round(v["flops"] / dense["flops"], 4)
+            v["time_frac_vs_dense"] = round(v["ms_total"] / dense["ms_total"], 4)
     del layers, embed, head, model
     torch.cuda.empty_cache()
     return out
@@ -544,10 +572,12 @@ def main():
         "per_M": res["per_M"],
         "kl_lock": res["kl_lock"],
         "kernels_ms_M1024": res["kernels_ms_M1024"],
+        "ablation_no_kv_cache_ms": res["ablation_no_kv_cache_ms"],
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
         "batched_step": None if args.no_batched else batched_step(),
-        "e2e_loop": None if args.no_e2e else e2e_loop(),
+        "e2e_loop": None if args.no_e2e else e2e_loop(runs=SURELOCK_RUNS + ABLATION_RUNS),
+        "e2e_loop_b8": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[0], SURELOCK_RUNS[2]), B=8),
         "cpu_baseline": None if args.no_cpu else cpu_part(args.cpu_seconds),
     }
     print(json.dumps(line), flush=True)

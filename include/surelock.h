@@ -103,19 +103,24 @@ sl_status sl_cache_scatter(int dtype, void* k_cache, void* v_cache, const void* 
  * (zhaoyang97 notes, 永久锁定机制; cost O(M N d), paperdance abstract).
  *   q        [M_tot][H][Dh] of `dtype`, RoPE already applied.
  *   k_cache, v_cache [B][N][H][Dh] of `dtype`.
+ *   key_excl [B*N] uint8 or NULL, 4-byte aligned: positions with a nonzero
+ *            flag are not attended (the "no KV cache" ablation of the notes
+ *            page, 消融实验: locked positions cannot be attended; pass the
+ *            lock mask).  Every query row must keep at least one key.
  *   out      [M_tot][H*Dh] of `dtype`.
  *   ws       workspace of at least sl_attn_workspace_size(...) bytes (any
  *            contents; used for split-KV partial results).
  * Limits: Dh in {32, 64, 128}; N % 64 == 0.
  */
 sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* act_off, int B, int N, int M_tot, int H, int Dh,
-                         float scale, void* out, void* ws, size_t ws_bytes, sl_stream stream);
+                         const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H,
+                         int Dh, float scale, void* out, void* ws, size_t ws_bytes, sl_stream stream);
 size_t sl_attn_workspace_size(int B, int N, int M_tot, int H, int Dh);
 
 /* Lock rule parameters (zhaoyang97 notes, 锁定判据 and 可选置信度门控). */
 typedef struct {
-  float eps;     /* lock when KL <= eps; eps <= 0 disables locking */
+  float eps;     /* lock when KL <= eps; eps <= 0 disables locking; eps = +inf drops the KL
+                    test (with the gate on: the notes page's confidence-gate-only ablation) */
   float gate_q;  /* quantile m in [0,1] of the gate u <= q_m(u); < 0 disables the gate */
   int mask_id;   /* [MASK] token id excluded from the argmax; -1 = none */
   int have_prev; /* 0 on the first step: no previous posterior, KL = +inf, nothing locks */
@@ -247,6 +252,9 @@ typedef struct {
   int mask_id;
   int do_lock;    /* 0: stop after the logits (no vocabulary pass, no lock) */
   int unmask_k;   /* > 0: sampler unmasks this many [MASK] positions per sequence */
+  int no_kv_cache; /* 0: SureLock (locked positions attended through their cached K/V);
+                      1: the notes page's "no KV cache" ablation (消融实验): positions
+                      locked before this step are not attended */
 } sl_step_params;
 
 /*

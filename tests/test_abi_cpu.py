@@ -46,9 +46,13 @@ def test_status_strings_and_host_checks():
                       None, None, None, None, None, None, None, 0, None)
     assert st == 1 and b"dtype" in L.sl_last_error()
     # unsupported head_dim
-    st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 64, 0, 1, 48,
-                          ctypes.c_float(1.0), None, ctypes.c_void_p(16), 1024, None)
+    st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, 1, 64, 0, 1,
+                          48, ctypes.c_float(1.0), None, ctypes.c_void_p(16), 1024, None)
     assert st == 2
+    # misaligned exclusion flags
+    st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(18),
+                          1, 64, 0, 1, 64, ctypes.c_float(1.0), None, ctypes.c_void_p(16), 1 << 20, None)
+    assert st == 1 and b"aligned" in L.sl_last_error()
 
 
 def test_workspace_sizes_are_monotone_in_rows():

@@ -154,6 +154,7 @@ KL_CASES = [
     (5000, 256, 1, 0.1, "f32", 0.05, 0.5, 255, True, None),           # tail in LDS, 4500 rows: select over LDS
     (10000, 256, 2, 0.7, "bf16", 0.05, 0.5, -1, True, 0.8),           # B*N above the tail's LDS copies
     (20000, 256, 1, 0.3, "bf16", 0.05, 0.5, -1, True, None),          # 14000 rows: tail reads global memory
+    (512, 4096, 2, 0.4, "bf16", math.inf, 0.5, -1, True, 0.8),        # eps = +inf: confidence gate only
 ]
 
 
@@ -377,6 +378,61 @@ def test_attention_parity(dtype, Dh, H, N, Ms):
     tol = 2e-2 if dtype == "bf16" else 2e-5
     for b in range(B):
         ref = O.attention(q64[off[b]:off[b + 1]], K64[b], V64[b], 1.0 / math.sqrt(Dh))
+        np.testing.assert_allclose(got[off[b]:off[b + 1]], ref, atol=tol, rtol=0)
+
+
+# The no-KV-cache ablation: every query attends over its sequence's active positions only
+# (the other positions' flags are set).  Key patterns: "random" = active set uniform;
+# "ends" = active positions in the first and last eighth (whole key tiles excluded in
+# between); "first" = active positions inside the first 64 keys (with a key split, every
+# other split sees no key at all).
+ATTN_EXCL_CASES = [
+    ("bf16", 128, 3, 1024, [5], "first"),
+    ("bf16", 128, 8, 512, [300, 1, 77], "random"),
+    ("bf16", 128, 32, 1024, [200, 180], "ends"),
+    ("bf16", 128, 16, 1024, [200], "ends"),
+    ("bf16", 128, 32, 1024, [1024], "random"),
+    ("bf16", 64, 2, 128, [1, 128, 70], "random"),
+    ("f32", 128, 2, 192, [150], "random"),
+    ("f32", 32, 4, 128, [3, 64], "first"),
+    ("f32", 64, 1, 512, [9, 120], "ends"),
+]
+
+
+def _active_keys(g, N, M, pattern):
+    if pattern == "random":
+        return np.sort(g.permutation(N)[:M]).astype(np.int32)
+    if pattern == "first":
+        return np.sort(g.permutation(64)[:M]).astype(np.int32)
+    pool = np.concatenate([np.arange(N // 8), np.arange(N - N // 8, N)])
+    return np.sort(g.permutation(pool)[:M]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype,Dh,H,N,Ms,pattern", ATTN_EXCL_CASES)
+def test_attention_excluded_keys_parity(dtype, Dh, H, N, Ms, pattern):
+    sl = _sl()
+    say("attn excl", dtype, Dh, H, N, Ms, pattern)
+    B = len(Ms)
+    g = W.rng(124, Dh, N, len(Ms))
+    acts = [_active_keys(g, N, M, pattern) for M in Ms]
+    off = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int32)
+    M_tot = int(off[-1])
+    excl = np.ones(B * N, np.uint8)
+    for b in range(B):
+        excl[b * N + acts[b]] = 0
+    q = W.to_storage(W.normal(g, (M_tot, H, Dh), 1.0), dtype)
+    Kc = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+    Vc = W.to_storage(W.normal(g, (B, N, H, Dh), 1.0), dtype)
+    out = torch.empty(M_tot, H * Dh, dtype=tdtype(dtype), device="cuda")
+    ws = torch.empty(max(1, sl.sl_attn_workspace_size(B, N, M_tot, H, Dh)), dtype=torch.uint8, device="cuda")
+    sl.sl_attn_active(dev(q, dtype), dev(Kc, dtype), dev(Vc, dtype), torch.from_numpy(off).cuda(), B, N, M_tot,
+                      H, Dh, 1.0 / math.sqrt(Dh), out, ws, key_excl=torch.from_numpy(excl).cuda())
+    got = host64(out).reshape(M_tot, H, Dh)
+    assert np.isfinite(got).all()
+    q64, K64, V64 = O.widen(q, dtype), O.widen(Kc, dtype), O.widen(Vc, dtype)
+    tol = 2e-2 if dtype == "bf16" else 2e-5
+    for b in range(B):
+        ref = O.attention(q64[off[b]:off[b + 1]], K64[b][acts[b]], V64[b][acts[b]], 1.0 / math.sqrt(Dh))
         np.testing.assert_allclose(got[off[b]:off[b + 1]], ref, atol=tol, rtol=0)
 
 

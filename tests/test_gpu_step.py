@@ -45,7 +45,7 @@ def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
 
 
 # ------------------------------------------------------------------ one layer, hidden rows in
-def _layer_case_run(dm, N, Ms, key, tol):
+def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False):
     sl = _sl()
     case = W.layer_case(dm, N, Ms, key=key)
     B, M = case.B, case.M_tot
@@ -61,7 +61,7 @@ def _layer_case_run(dm, N, Ms, key, tol):
                         k_cache=kc, v_cache=vc, with_h_out=True)
     assert st.M_tot == M
     np.testing.assert_array_equal(st.act_idx[:M].cpu().numpy(), case.act_idx)
-    st.step(eps=0.0, do_lock=False)
+    st.step(eps=0.0, do_lock=False, no_kv_cache=no_kv_cache)
     torch.cuda.synchronize()
     got_h = st.h_out[:M].cpu().numpy().astype(np.float64)
     # oracle
@@ -72,7 +72,7 @@ def _layer_case_run(dm, N, Ms, key, tol):
     V64 = O.widen(case.v_cache, dm.dtype)
     ostate = O.OracleState(B=B, N=N, t=0, locked=locked, kc=[K64], vc=[V64], h_in=h_in)
     om = O.OracleModel(od, 1, lambda l: W64)
-    out = O.step(om, ostate, 0.0, -1.0, do_lock=False)
+    out = O.step(om, ostate, 0.0, -1.0, do_lock=False, attend_locked=not no_kv_cache)
     if dm.dtype == "bf16":
         l2, rms, mx = check_hidden(got_h, out.h, tol[0], "hidden rows")
         say("hidden rows: rel L2 %.3e rms %.3e max %.3e" % (l2, rms, mx))
@@ -116,6 +116,18 @@ def test_layer_step_full_llada_shape(M):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("dm,N,Ms", [
+    (SMALL_BF16, 256, [100]), (SMALL_BF16, 128, [128, 3, 77]), (SMALL_F32, 64, [20, 64]),
+    (W.Dims(n_layers=1, d=512, n_heads=8, head_dim=64, ffn=1024, vocab=1024, dtype="bf16"), 320, [300, 17]),
+    (W.LLADA_LAYER, 1024, [256]),
+])
+def test_layer_step_no_kv_cache_ablation(dm, N, Ms):
+    """The no-KV-cache ablation (positions locked before the step are not attended) against the
+    oracle's step with attend_locked=False."""
+    say("layer step no kv cache", dm.d, dm.dtype, N, Ms)
+    _layer_case_run(dm, N, Ms, key=N + sum(Ms) + 1, tol=TOL[dm.dtype], no_kv_cache=True)
+
+
 def test_layer_step_batched_full_shape():
     """The LLaDA-8B-shaped layer on 8 sequences x N=2048 with ragged active sets (fraction per
     sequence uniform on [0.05, 0.8]): attention within each sequence only."""
@@ -240,12 +252,19 @@ def _step_compare(st, ost_before, out, dm, B, N, eps, gate_q, tol_logit):
     return len(diff)
 
 
-def test_tiny_loop_teacher_forced():
+# lock rules: SureLock (KL test, gate off); the notes page's ablations (消融实验): confidence gate
+# only (eps = +inf, gate at the median) and no KV cache (locked positions not attended)
+LOOP_RULES = {"surelock": (0.05, -1.0, False), "gate_only": (math.inf, 0.5, False), "no_kv_cache": (0.05, -1.0, True)}
+
+
+@pytest.mark.parametrize("rule", list(LOOP_RULES))
+def test_tiny_loop_teacher_forced(rule):
     """2-layer fp32 model, d=128, 4x32 heads, FFN 384, V=512, N=64 (16 prompt + 48 masked),
-    16 steps, 3 unmasks per step, eps=0.05, gate off."""
+    16 steps, 3 unmasks per step; eps=0.05 with the gate off, or one of the ablations."""
     sl = _sl()
     dm = W.TINY
-    B, N, T, eps = 1, 64, 16, 0.05
+    B, N, T = 1, 64, 16
+    eps, gate, no_kv = LOOP_RULES[rule]
     layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
     model = _dev_model(dm, layers, emb, head, rope_n=N)
     st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
@@ -262,14 +281,14 @@ def test_tiny_loop_teacher_forced():
         post_before = None if ost.post is None else ost.post.copy()
         M_before = st.M_tot
         ost.t = t
-        out = O.step(om, ost, eps, -1.0, True, dm.mask_id)
+        out = O.step(om, ost, eps, gate, True, dm.mask_id, attend_locked=not no_kv)
         tok_o = ost.tok.copy()
         O.sampler_unmask(ost.tok, ost.cand, out.act_idx, out.act_off, N, out.stats.argmax, out.stats.conf,
                          dm.mask_id, 3)
-        p = sl.surelock.sl_step_params(eps, -1.0, dm.mask_id, 1, 3)
+        p = sl.surelock.sl_step_params(eps, gate, dm.mask_id, 1, 3, int(no_kv))
         sl.sl_step(model.s, st.struct(), p, st.ws)
         torch.cuda.synchronize()
-        total_mismatch += _step_compare(st, None, out, dm, B, N, eps, -1.0, 1e-4)
+        total_mismatch += _step_compare(st, None, out, dm, B, N, eps, gate, 1e-4)
         # sampler: same positions unmasked to the same tokens (teacher-forced, fp32)
         np.testing.assert_array_equal(st.tok.cpu().numpy(), ost.tok)
         Ms.append(M_before)

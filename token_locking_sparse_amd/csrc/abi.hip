@@ -142,8 +142,8 @@ size_t sl_attn_workspace_size(int B, int N, int M_tot, int H, int Dh) {
 }
 
 sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* act_off, int B, int N, int M_tot, int H, int Dh, float scale,
-                         void* out, void* ws, size_t ws_bytes, sl_stream stream) {
+                         const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H,
+                         int Dh, float scale, void* out, void* ws, size_t ws_bytes, sl_stream stream) {
   g_err[0] = 0;
   sl_status st = check_dtype(dtype);
   if (st != SL_OK) return st;
@@ -153,9 +153,10 @@ sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const vo
   SL_REQUIRE(M_tot == 0 || (q && out), SL_ERR_INVALID, "NULL q / out");
   SL_REQUIRE(Dh == 32 || Dh == 64 || Dh == 128, SL_ERR_UNSUPPORTED, "head_dim %d not in {32, 64, 128}", Dh);
   SL_REQUIRE(N % 64 == 0, SL_ERR_UNSUPPORTED, "N %% 64 != 0 (N = %d)", N);
+  SL_REQUIRE((uintptr_t)key_excl % 4 == 0, SL_ERR_INVALID, "key_excl not 4-byte aligned");
   SL_REQUIRE(ws_bytes >= sl::attn_ws_bytes(B, N, M_tot, H, Dh) && ws, SL_ERR_INVALID,
              "workspace too small (%zu < %zu)", ws_bytes, sl::attn_ws_bytes(B, N, M_tot, H, Dh));
-  SL_TRY(sl::launch_attn(dtype, q, k_cache, v_cache, act_off, B, N, M_tot, H, Dh, scale, out, ws,
+  SL_TRY(sl::launch_attn(dtype, q, k_cache, v_cache, act_off, key_excl, B, N, M_tot, H, Dh, scale, out, ws,
                          (hipStream_t)stream),
          "sl_attn_active launch");
   return SL_OK;
@@ -308,6 +309,8 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
   void* attn_ws = w + L.attn;
   const size_t cache_layer = (size_t)B * N * d * eb;
   const float scale = 1.f / sqrtf((float)Dh);
+  // no-KV-cache ablation: the positions locked before this step are not attended
+  const uint8_t* key_excl = p->no_kv_cache ? st->locked : nullptr;
 
   if (M > 0) {
     SL_TRY(sl::launch_gather_norm(dt, st->h_in, m->embed, st->tok, st->act_idx, st->act_off, B, N, M, d,
@@ -324,7 +327,8 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       g.A = x; g.K = d; g.Nv = 3 * d; g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
       g.out0 = q; g.out1 = kc; g.out2 = vc; g.rope = m->rope;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_QKV, g, s), "qkv gemm");
-      SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, B, N, M, H, Dh, scale, o, attn_ws, s), "attention");
+      SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, key_excl, B, N, M, H, Dh, scale, o, attn_ws, s),
+             "attention");
       // O projection + residual
       g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s), "o gemm");

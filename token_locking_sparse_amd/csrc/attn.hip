@@ -65,10 +65,26 @@ __device__ __forceinline__ int find_tile(const int32_t* act_off, int B, int slot
   return -1;
 }
 
-template <typename T, int Dh>
+// Key exclusion (the no-KV-cache ablation: positions that may not be attended).
+// Score register v of a lane holds key 8 (v / 4) + 4 hl + v % 4 of its 32-key
+// subtile, so the lane needs four 4-byte words of the flags: word g covers keys
+// 8 g + 4 hl .. + 3.  Excluded keys get a score of -inf.
+__device__ __forceinline__ uint32_t excl_word(const uint8_t* excl_row, int key0, int sub, int g, int hl) {
+  return *(const uint32_t*)(excl_row + key0 + 32 * sub + 8 * g + 4 * hl);
+}
+__device__ __forceinline__ void mask_scores(f32x16& s, const uint32_t* w) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if ((w[g] >> (8 * r)) & 0xffu) s[4 * g + r] = -INFINITY;
+}
+
+template <typename T, int Dh, bool EXCL>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-            const int32_t* __restrict__ act_off, int B, int N, int H, float scale_log2,
+            const int32_t* __restrict__ act_off, const uint8_t* __restrict__ key_excl, int B, int N, int H,
+            float scale_log2,
             int nsplit, int tiles_per_split, T* __restrict__ out, float* __restrict__ part_o,
             float* __restrict__ part_ml, int M_tot) {
   using C = AttnCfg<T, Dh>;
@@ -112,11 +128,19 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
   const char* kbase = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
   const char* vbase = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
   const size_t krow_stride = (size_t)HD * sizeof(T);
+  const uint8_t* excl_row = EXCL ? key_excl + (size_t)b * N : nullptr;
 
   u32x4 kreg[C::KLoads];
   u32x4 vreg[C::VLoads][2];
+  uint32_t mw[2][4];   // exclusion words of the tile being loaded, per 32-key subtile
   auto gload = [&](int tile) {
     const int key0 = tile * kBKV;
+    if constexpr (EXCL) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mw[sub][g] = excl_word(excl_row, key0, sub, g, hl);
+    }
 #pragma unroll
     for (int i = 0; i < C::KLoads; ++i) {
       const int id = tid + i * kAttnThreads;
@@ -187,6 +211,13 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
   __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
     const int stage = (t - t_begin) & 1;
+    uint32_t mcur[2][4];
+    if constexpr (EXCL) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mcur[sub][g] = mw[sub][g];
+    }
     if (t + 1 < t_end) gload(t + 1);
     if (wave_live) {
       const char* ks = smem + stage * C::Stage;
@@ -202,6 +233,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
           const u32x4 a = *(const u32x4*)(ks + kr * (Dh * (int)sizeof(T)) + swz<Dh * (int)sizeof(T)>(kr, 2 * kk + hl) * 16);
           Mfma<T>::run(s[sub], a, qf[kk]);
         }
+        if constexpr (EXCL) mask_scores(s[sub], mcur[sub]);
       }
       // online softmax in log2 units; lane pair (l, l^32) shares a query row
       float mx = -INFINITY;
@@ -213,12 +245,14 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f;
       m_run = m_new;
+      // every key so far excluded: the scores are all -inf and P is 0
+      const float m_ref = m_new > -INFINITY ? m_new : 0.f;
       float ls = 0.f;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[sub][v], scale_log2, -m_new));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[sub][v], scale_log2, -m_ref));
           s[sub][v] = pv;
           ls += pv;
         }
@@ -364,10 +398,11 @@ __device__ __forceinline__ uint2 lds_tr16(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int QW, int G, int BKV>
+template <int QW, int G, int BKV, bool EXCL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-               const int32_t* __restrict__ act_off, int B, int N, int H, float scale_log2, int nsplit,
+               const int32_t* __restrict__ act_off, const uint8_t* __restrict__ key_excl, int B, int N, int H,
+               float scale_log2, int nsplit,
                int tiles_per_split, bf16* __restrict__ out, float* __restrict__ part_o,
                float* __restrict__ part_ml, int M_tot) {
   using C = TrCfg<QW, G, BKV>;
@@ -418,7 +453,16 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     voff[j] = (uint32_t)(r * krow) + vswz(r, pos) * 16;
   }
   auto stage_base = [&](int stage) { return smem + (stage * G + grp) * C::kStage; };
+  constexpr int NS = BKV / 32;   // 32-key subtiles of a tile
+  const uint8_t* excl_row = EXCL ? key_excl + (size_t)b * N : nullptr;
+  uint32_t mw[NS][4];            // exclusion words of the tile issued last, per subtile
   auto issue = [&](int tile, int stage) {
+    if constexpr (EXCL) {
+#pragma unroll
+      for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mw[sub][g] = excl_word(excl_row, tile * BKV, sub, g, hl);
+    }
     char* ks = stage_base(stage);
     char* vs = ks + C::kTile;
     const size_t t0 = (size_t)tile * BKV * krow;
@@ -452,11 +496,17 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                  // everyone's landed; the other stage is free again
     asm volatile("" ::: "memory");
+    uint32_t mcur[NS][4];
+    if constexpr (EXCL) {
+#pragma unroll
+      for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mcur[sub][g] = mw[sub][g];
+    }
     if (it + 1 < n_it && own_tile(it + 1) < t_end) issue(own_tile(it + 1), stage ^ 1);
     if (!wave_live || own_tile(it) >= t_end) continue;
     const char* ks = stage_base(stage);
     const char* vs = ks + C::kTile;
-    constexpr int NS = BKV / 32;   // 32-key subtiles
     f32x16 sc[NS];
 #pragma unroll
     for (int sub = 0; sub < NS; ++sub) {
@@ -468,6 +518,7 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
         const u32x4 a = *(const u32x4*)(ks + kr * kTrRB + swz<kTrRB>(kr, 2 * kk + hl) * 16);
         Mfma<bf16>::run(sc[sub], a, qf[kk]);
       }
+      if constexpr (EXCL) mask_scores(sc[sub], mcur[sub]);
     }
     // Online softmax with a lazily moved reference: the row's reference m_run
     // only moves when the tile max exceeds it by more than kLazy (log2 units),
@@ -489,12 +540,14 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
         for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
     }
     m_run = m_new;
+    // every key so far excluded: the scores are all -inf and P is 0
+    const float m_ref = m_new > -INFINITY ? m_new : 0.f;
     float ls = 0.f;
 #pragma unroll
     for (int sub = 0; sub < NS; ++sub)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[sub][v], scale_log2, -m_new));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[sub][v], scale_log2, -m_ref));
         sc[sub][v] = pv;
         ls += pv;
       }
@@ -688,10 +741,10 @@ size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh) {
   return (size_t)nsplit * M_tot * H * (Dh + 2) * 4 + 256;
 }
 
-template <typename T, int Dh>
+template <typename T, int Dh, bool EXCL>
 static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, const int32_t* act_off,
-                                int B, int N, int M_tot, int H, float scale, void* out, void* ws,
-                                hipStream_t s) {
+                                const uint8_t* key_excl, int B, int N, int M_tot, int H, float scale, void* out,
+                                void* ws, hipStream_t s) {
   const bool tr = sizeof(T) == 2 && Dh == kTrDh;
   const AttnPlan p = attn_plan(B, N, M_tot, H, tr);
   const int nsplit = p.nsplit, tps = p.tps;
@@ -700,14 +753,16 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
   const float sl2 = scale * kLog2e;
   const dim3 grid(p.slots * H * nsplit);
   if (tr && p.shape == 0)
-    hipLaunchKernelGGL((attn_tr_kernel<4, 2, 64>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
-                       (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml, M_tot);
+    hipLaunchKernelGGL((attn_tr_kernel<4, 2, 64, EXCL>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
+                       (const bf16*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml,
+                       M_tot);
   else if (tr)
-    hipLaunchKernelGGL((attn_tr_kernel<2, 4, 32>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
-                       (const bf16*)vc, act_off, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml, M_tot);
+    hipLaunchKernelGGL((attn_tr_kernel<2, 4, 32, EXCL>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
+                       (const bf16*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml,
+                       M_tot);
   else
-    hipLaunchKernelGGL((attn_kernel<T, Dh>), grid, dim3(kAttnThreads), 0, s, (const T*)q, (const T*)kc,
-                       (const T*)vc, act_off, B, N, H, sl2, nsplit, tps, (T*)out, part_o, part_ml, M_tot);
+    hipLaunchKernelGGL((attn_kernel<T, Dh, EXCL>), grid, dim3(kAttnThreads), 0, s, (const T*)q, (const T*)kc,
+                       (const T*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (T*)out, part_o, part_ml, M_tot);
   if (nsplit > 1) {
     const int waves = M_tot * H;
     hipLaunchKernelGGL((attn_combine_kernel<T, Dh>), dim3((waves + 3) / 4), dim3(256), 0, s, part_o,
@@ -716,18 +771,26 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
   return hipGetLastError();
 }
 
+template <typename T, int Dh>
+static hipError_t attn_launch_excl(const void* q, const void* kc, const void* vc, const int32_t* act_off,
+                                   const uint8_t* key_excl, int B, int N, int M_tot, int H, float scale, void* out,
+                                   void* ws, hipStream_t s) {
+  return key_excl ? attn_launch_t<T, Dh, true>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s)
+                  : attn_launch_t<T, Dh, false>(q, kc, vc, act_off, nullptr, B, N, M_tot, H, scale, out, ws, s);
+}
+
 hipError_t launch_attn(int dtype, const void* q, const void* kc, const void* vc,
-                       const int32_t* act_off, int B, int N, int M_tot, int H, int Dh, float scale,
-                       void* out, void* ws, hipStream_t s) {
+                       const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H, int Dh,
+                       float scale, void* out, void* ws, hipStream_t s) {
   if (M_tot <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (Dh == 128) return attn_launch_t<bf16, 128>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 64) return attn_launch_t<bf16, 64>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 32) return attn_launch_t<bf16, 32>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 128) return attn_launch_excl<bf16, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 64) return attn_launch_excl<bf16, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 32) return attn_launch_excl<bf16, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
   } else {
-    if (Dh == 128) return attn_launch_t<float, 128>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 64) return attn_launch_t<float, 64>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 32) return attn_launch_t<float, 32>(q, kc, vc, act_off, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 128) return attn_launch_excl<float, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 64) return attn_launch_excl<float, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 32) return attn_launch_excl<float, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
   }
   return hipErrorInvalidValue;
 }

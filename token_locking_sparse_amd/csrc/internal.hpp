@@ -52,9 +52,10 @@ hipError_t launch_cache_scatter(int dtype, void* kc, void* vc, const void* kn, c
                                 int M_tot, int row_elems, hipStream_t s);
 
 size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh);
+// key_excl: [B*N] flags or NULL; nonzero = that position is not attended.
 hipError_t launch_attn(int dtype, const void* q, const void* kc, const void* vc,
-                       const int32_t* act_off, int B, int N, int M_tot, int H, int Dh, float scale,
-                       void* out, void* ws, hipStream_t s);
+                       const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H, int Dh,
+                       float scale, void* out, void* ws, hipStream_t s);
 
 hipError_t launch_rope_table(int n_pos, int Dh, float theta, float* table, hipStream_t s);
 

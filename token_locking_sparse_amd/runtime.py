@@ -95,9 +95,11 @@ class DeviceState:
         return st
 
     def step(self, eps: float, gate_q: float = -1.0, mask_id: int = -1, do_lock: bool = True,
-             unmask_k: int = 0, stream=None) -> int:
-        """One SureLock iteration; returns the new active count."""
-        p = S.sl_step_params(float(eps), float(gate_q), int(mask_id), int(bool(do_lock)), int(unmask_k))
+             unmask_k: int = 0, stream=None, no_kv_cache: bool = False) -> int:
+        """One SureLock iteration; returns the new active count.  no_kv_cache: the ablation in
+        which positions locked before the step are not attended."""
+        p = S.sl_step_params(float(eps), float(gate_q), int(mask_id), int(bool(do_lock)), int(unmask_k),
+                             int(bool(no_kv_cache)))
         st = self.struct()
         S.sl_step(self.model.s, st, p, self.ws, stream)
         if do_lock and self.model.lm_head is not None:

@@ -54,7 +54,7 @@ class sl_state(C.Structure):
 
 class sl_step_params(C.Structure):
     _fields_ = [("eps", C.c_float), ("gate_q", C.c_float), ("mask_id", C.c_int), ("do_lock", C.c_int),
-                ("unmask_k", C.c_int)]
+                ("unmask_k", C.c_int), ("no_kv_cache", C.c_int)]
 
 
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
@@ -79,7 +79,7 @@ def lib():
         "sl_version": (C.c_char_p, []),
         "sl_compact": (i, [vp, i, i, vp, vp, vp, vp]),
         "sl_cache_scatter": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]),
-        "sl_attn_active": (i, [i, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]),
+        "sl_attn_active": (i, [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]),
         "sl_attn_workspace_size": (sz, [i, i, i, i, i]),
         "sl_kl_lock": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
                            vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -172,11 +172,13 @@ def sl_attn_workspace_size(B, N, M_tot, H, Dh) -> int:
     return int(lib().sl_attn_workspace_size(B, N, M_tot, H, Dh))
 
 
-def sl_attn_active(q, k_cache, v_cache, act_off, B, N, M_tot, H, Dh, scale, out, ws, stream=None):
+def sl_attn_active(q, k_cache, v_cache, act_off, B, N, M_tot, H, Dh, scale, out, ws, stream=None, key_excl=None):
+    """key_excl: optional [B*N] uint8 device tensor; nonzero positions are not attended."""
     dt = dtype_code(k_cache.dtype)
     st = lib().sl_attn_active(dt, _ptr(q, "q", k_cache.dtype, optional=M_tot == 0),
                               _ptr(k_cache, "k_cache", k_cache.dtype), _ptr(v_cache, "v_cache", k_cache.dtype),
-                              _ptr(act_off, "act_off", torch.int32), B, N, M_tot, H, Dh, float(scale),
+                              _ptr(act_off, "act_off", torch.int32),
+                              _ptr(key_excl, "key_excl", torch.uint8, optional=True), B, N, M_tot, H, Dh, float(scale),
                               _ptr(out, "out", k_cache.dtype, optional=M_tot == 0), _ptr(ws, "ws"),
                               ws.numel() * ws.element_size(), _stream(stream))
     _check("sl_attn_active", st)
