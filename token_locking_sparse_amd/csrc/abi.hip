@@ -57,6 +57,27 @@ struct StepLayout {
   }
 };
 
+// Bytes of split-K partial sums the O and down projections need at M rows (their output
+// width is d); 0 when neither splits or the row is too wide for the fused reduce.
+size_t resid_part_bytes(const sl_model* m, int M) {
+  if (M <= 0 || m->d > sl::kResidMaxD || m->d % 4) return 0;
+  const int so = sl::gemm_split(m->dtype, sl::EPI_RESID, M, m->d, m->d);
+  const int sd = sl::gemm_split(m->dtype, sl::EPI_RESID, M, m->ffn, m->d);
+  const int sp = so > sd ? so : sd;
+  return sp > 1 ? align256((size_t)sp * M * m->d * 4) : 0;
+}
+
+// The most partial-sum space any step with at most M_tot rows needs (the split the
+// launcher picks is not monotone in M).
+size_t resid_part_bytes_upto(const sl_model* m, int M_tot) {
+  size_t best = 0;
+  for (int M = 1; M <= M_tot; ++M) {
+    const size_t b = resid_part_bytes(m, M);
+    if (b > best) best = b;
+  }
+  return best;
+}
+
 sl_status check_dtype(int dtype) {
   SL_REQUIRE(dtype == SL_BF16 || dtype == SL_F32, SL_ERR_INVALID, "dtype %d is neither SL_BF16 nor SL_F32", dtype);
   return SL_OK;
@@ -263,7 +284,7 @@ sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* ti
 
 size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot) {
   if (!model) return 0;
-  return StepLayout(model, B, N, M_tot).total;
+  return StepLayout(model, B, N, M_tot).total + resid_part_bytes_upto(model, M_tot);
 }
 
 sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void* ws, size_t ws_bytes,
@@ -296,6 +317,10 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
   }
   const StepLayout L(m, B, N, M);
   SL_REQUIRE(ws && ws_bytes >= L.total, SL_ERR_INVALID, "workspace too small (%zu < %zu)", ws_bytes, L.total);
+  // split-K partial sums of the residual projections go after the fixed regions when they fit
+  // (a workspace of sl_step_workspace_size bytes always has room); otherwise fp32 atomics
+  const size_t part_need = resid_part_bytes(m, M);
+  float* part = (part_need > 0 && ws_bytes - L.total >= part_need) ? (float*)((char*)ws + L.total) : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   const int dt = m->dtype, eb = elem_bytes(dt);
@@ -329,17 +354,21 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       SL_TRY(sl::launch_gemm(dt, sl::EPI_QKV, g, s), "qkv gemm");
       SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, key_excl, B, N, M, H, Dh, scale, o, attn_ws, s),
              "attention");
-      // O projection + residual
-      g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32;
-      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s), "o gemm");
-      SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
-      // SwiGLU FFN + residual
-      g.A = x; g.K = d; g.Nv = 2 * F; g.w0 = W.wg; g.w1 = W.wu; g.out0 = act;
+      // O projection + residual, then the pre-FFN RMSNorm (fused with the partial sums' reduce
+      // when the projection is split over K)
+      int ns = 1;
+      g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32; g.part = part;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "o gemm");
+      if (part && ns > 1) SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, x, s), "residual + norm");
+      else SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+      // SwiGLU FFN + residual, then the next block's RMSNorm (none after the last layer without a head)
+      g.A = x; g.K = d; g.Nv = 2 * F; g.w0 = W.wg; g.w1 = W.wu; g.out0 = act; g.part = nullptr;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_SWIGLU, g, s), "gate/up gemm");
-      g.A = act; g.K = F; g.Nv = d; g.w0 = W.wd; g.w1 = nullptr; g.out0 = h32;
-      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s), "down gemm");
-      if (head || l + 1 < m->n_layers)
-        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+      g.A = act; g.K = F; g.Nv = d; g.w0 = W.wd; g.w1 = nullptr; g.out0 = h32; g.part = part;
+      SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "down gemm");
+      void* xn = (head || l + 1 < m->n_layers) ? x : nullptr;
+      if (part && ns > 1) SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, xn, s), "residual + norm");
+      else if (xn) SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, xn, s), "norm");
     }
     if (head) {
       sl::GemmArgs g{};

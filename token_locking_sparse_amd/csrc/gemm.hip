@@ -124,7 +124,16 @@ template <typename T, int EPI, int BN, int TN, int LDW, int PR, int NT>
 __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int mrow0, int n0) {
   const int tid = threadIdx.x;
   if (EPI == EPI_RESID) {
-    if (a.split_k > 1) {
+    if (a.split_k > 1 && a.part) {
+      // this split's partial sums, plane blockIdx.z, with 16-byte stores
+      constexpr int CPR = BN / 4;
+      float* plane = a.part + (size_t)blockIdx.z * a.M * a.Nv;
+      for (int id = tid; id < PR * CPR; id += NT) {
+        const int r = id / CPR, c = (id % CPR) * 4;
+        const int m = mrow0 + r;
+        if (m < a.M) *(f32x4*)(plane + (size_t)m * a.Nv + n0 + c) = *(const f32x4*)(tile + r * LDW + c);
+      }
+    } else if (a.split_k > 1) {
       // fp32 atomics, consecutive lanes on consecutive floats of a row
       for (int id = tid; id < PR * BN; id += NT) {
         const int r = id / BN, c = id % BN;
@@ -427,12 +436,18 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 }
 
 // ------------------------------------------------------------------ dispatch
+// K splits actually launched for a requested split: every split takes the same number of k-tiles.
+static int splits_launched(int KI, int split) {
+  const int kps = (KI + split - 1) / split;
+  return (KI + kps - 1) / kps;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, bool VB = false>
 static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int split) {
   const int MT = (a.M + BM - 1) / BM, NT = a.Nv / BN;
   const int KI = a.K * (int)sizeof(T) / RB;
   const int kps = (KI + split - 1) / split;
-  const int nsplit = (KI + kps - 1) / kps;
+  const int nsplit = splits_launched(KI, split);
   GemmArgs b = a;
   b.split_k = nsplit;
   const dim3 grid(MT * NT, 1, nsplit), block(64 * WM * WN);
@@ -518,9 +533,10 @@ int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh) {
 }
 
 template <typename T>
-static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit) {
   int c, split;
   pick_cfg(a, epi, (int)sizeof(T), c, split);
+  if (nsplit) *nsplit = c >= 0 ? splits_launched(a.K * (int)sizeof(T) / kCfgs[c].RB, split) : 1;
   switch (c) {
     case 0: return run_cfg<T, 256, 256, 2, 4, 64, 4>(epi, a, s, split);
     case 1: return run_cfg<T, 256, 128, 4, 2, 128, 3>(epi, a, s, split);
@@ -547,9 +563,19 @@ void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, i
   if (vb) *vb = c >= 0 && kCfgs[c].vb ? 1 : 0;
 }
 
-hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s) {
+int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv) {
+  GemmArgs a{};
+  a.M = M; a.K = K; a.Nv = Nv;
+  const int eb = dtype == 0 ? 2 : 4;
+  int c, sp;
+  pick_cfg(a, epi, eb, c, sp);
+  return c >= 0 ? splits_launched(K * eb / kCfgs[c].RB, sp) : 1;
+}
+
+hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit) {
+  if (nsplit) *nsplit = 1;
   if (a.M <= 0) return hipSuccess;
-  return dtype == 0 ? launch_t<bf16>(epi, a, s) : launch_t<float>(epi, a, s);
+  return dtype == 0 ? launch_t<bf16>(epi, a, s, nsplit) : launch_t<float>(epi, a, s, nsplit);
 }
 
 }  // namespace sl

@@ -63,6 +63,11 @@ hipError_t launch_rope_table(int n_pos, int Dh, float theta, float* table, hipSt
 hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, const int32_t* tok,
                               const int32_t* act_idx, const int32_t* act_off, int B, int N,
                               int M_tot, int d, float eps, float* h32, void* x, hipStream_t s);
+// Split-K residual: h32 += the nsplit partial planes of part, then x = RMSNorm(h32) in the
+// storage type (x NULL: no norm).  d % 4 == 0, d <= kResidMaxD, 2 <= nsplit <= 8.
+constexpr int kResidMaxD = 4096;
+hipError_t launch_resid_norm(int dtype, const float* part, int nsplit, float* h32, int M_tot, int d, float eps,
+                             void* x, hipStream_t s);
 hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x,
                        hipStream_t s);
 
@@ -85,9 +90,14 @@ struct GemmArgs {
   const int32_t* act_idx;
   const int32_t* act_off;
   int B, N;
-  int split_k;         // RESID only (atomic accumulation)
+  int split_k;         // RESID only: K splits (set by the launcher)
+  float* part;         // RESID split over K: [splits][M][Nv] fp32 partial sums written with plain stores
+                       // (added into out0 by launch_resid_norm), or NULL: fp32 atomics into out0
 };
-hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s);
+// nsplit (may be NULL) receives the number of K splits launched.
+hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit = nullptr);
+// Number of K splits launch_gemm runs for this shape (1 = none).
+int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv);
 int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh);
 // Tile (rows, columns), split-K and load path (1: through registers) the launcher
 // picks for this shape; vb may be NULL.

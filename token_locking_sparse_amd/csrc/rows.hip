@@ -129,6 +129,88 @@ hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, co
   return hipGetLastError();
 }
 
+// Residual update of a projection split over K, fused with the next RMSNorm:
+// h[m] += sum of the S partial planes, then x[m] = h[m] / sqrt(mean(h[m]^2) + eps)
+// in the GEMM operand type (skipped when x is NULL).  One workgroup per row;
+// each thread takes four 16-byte chunks of the row (d <= 4096), and every load
+// of its chunks (the residual and all S partials) is issued before any is used.
+// Chunks past the row end re-read the last chunk (in bounds) and are not stored.
+constexpr int kResidThreads = 256, kResidCPT = kResidMaxD / 4 / kResidThreads;
+
+template <typename T, int S>
+__global__ void __launch_bounds__(kResidThreads)
+resid_norm_kernel(const float* __restrict__ part, float* __restrict__ h32, int M_tot, int d, float eps,
+                  T* __restrict__ x) {
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int nc = d / 4;
+  float* hrow = h32 + (size_t)m * d;
+  f32x4 acc[kResidCPT], pv[S][kResidCPT];
+#pragma unroll
+  for (int k = 0; k < kResidCPT; ++k) {
+    const int c = min(tid + kResidThreads * k, nc - 1);
+    acc[k] = *(const f32x4*)(hrow + 4 * c);
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) pv[sp][k] = *(const f32x4*)(part + ((size_t)sp * M_tot + m) * d + 4 * c);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kResidCPT; ++k) {
+    const int c = tid + kResidThreads * k;
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) acc[k] += pv[sp][k];
+    if (c < nc) {
+      *(f32x4*)(hrow + 4 * c) = acc[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(acc[k][j], acc[k][j], ss);
+    }
+  }
+  if (!x) return;   // uniform: a kernel argument
+  __shared__ float red[kResidThreads / kWave];
+  ss = wave_sum(ss);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kResidThreads / kWave; ++w) tot += red[w];
+  const float r = 1.f / sqrtf(tot / (float)d + eps);
+  T* xrow = x + (size_t)m * d;
+#pragma unroll
+  for (int k = 0; k < kResidCPT; ++k) {
+    const int c = tid + kResidThreads * k;
+    if (c < nc) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = acc[k][j] * r;
+      store_x(xrow + 4 * c, y, 4);
+    }
+  }
+}
+
+template <typename T>
+static hipError_t resid_norm_t(const float* part, int nsplit, float* h32, int M_tot, int d, float eps, T* x,
+                               hipStream_t s) {
+  const dim3 grid(M_tot), block(kResidThreads);
+  switch (nsplit) {
+    case 2: hipLaunchKernelGGL((resid_norm_kernel<T, 2>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 3: hipLaunchKernelGGL((resid_norm_kernel<T, 3>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 4: hipLaunchKernelGGL((resid_norm_kernel<T, 4>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 5: hipLaunchKernelGGL((resid_norm_kernel<T, 5>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 6: hipLaunchKernelGGL((resid_norm_kernel<T, 6>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 7: hipLaunchKernelGGL((resid_norm_kernel<T, 7>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 8: hipLaunchKernelGGL((resid_norm_kernel<T, 8>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(int dtype, const float* part, int nsplit, float* h32, int M_tot, int d, float eps,
+                             void* x, hipStream_t s) {
+  if (M_tot <= 0) return hipSuccess;
+  if (d % 4 || d > kResidMaxD || d < 4) return hipErrorInvalidValue;
+  return dtype == 0 ? resid_norm_t<bf16>(part, nsplit, h32, M_tot, d, eps, (bf16*)x, s)
+                    : resid_norm_t<float>(part, nsplit, h32, M_tot, d, eps, (float*)x, s);
+}
+
 hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x, hipStream_t s) {
   if (M_tot <= 0) return hipSuccess;
   const dim3 grid((M_tot + 3) / 4), block(256);
