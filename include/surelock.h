@@ -261,7 +261,8 @@ typedef struct {
  * sl_step — one whole SureLock iteration:
  *   gather the active rows (embedding of tok, or h_in rows) -> for every layer:
  *   RMSNorm, fused QKV projection + RoPE with the K/V rows scattered into the
- *   layer cache, active-query attention over all N cached rows, O projection
+ *   layer cache, active-query attention over all N cached rows (over the active
+ *   rows only with no_kv_cache), O projection
  *   + residual, RMSNorm, SwiGLU FFN + residual -> final RMSNorm, LM head
  *   writing logits rows b*N+pos of logits[t%2] -> sl_kl_lock against
  *   logits[(t+1)%2] -> optional sampler (the unmask_k most confident [MASK]
@@ -271,14 +272,21 @@ typedef struct {
  * (zhaoyang97 notes, 永久锁定机制: posterior frozen, K/V cached; gist.science/it
  * §2: block input frozen, K/V cached for every layer).  A_t within A_{t-1}
  * guarantees logits[(t+1)%2] holds p_{t-1} for every active row.
- *   ws: at least sl_step_workspace_size(...) bytes (any contents).  A workspace
- *       sized for the first step's M_tot serves every later step (M only shrinks).
+ *   ws: sl_step_workspace_size(...) bytes (any contents).  A workspace sized for
+ *       the first step's M_tot serves every later step (M only shrinks).  Less is
+ *       accepted down to the fixed buffers of the step; the O and down projections
+ *       then accumulate their split-K partial sums with fp32 atomics instead of the
+ *       partial-sum planes (same results up to the order of the additions); below
+ *       that the call fails with SL_ERR_INVALID.
  * Limits: d % 128 == 0, ffn % 64 == 0, vocab % 128 == 0, head_dim in {32, 64, 128},
  * n_heads*head_dim == d, N % 64 == 0, rope_n >= N.
  */
 sl_status sl_step(const sl_model* model, sl_state* state, const sl_step_params* params,
                   void* ws, size_t ws_bytes, sl_stream stream);
 size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot);
+/* The smallest workspace sl_step accepts for a step with M_tot active rows: the
+ * fixed buffers only (split-K residual projections then use fp32 atomics). */
+size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot);
 
 #ifdef __cplusplus
 }

@@ -56,7 +56,17 @@ def test_status_strings_and_host_checks():
 
 
 def test_workspace_sizes_are_monotone_in_rows():
+    import ctypes
+
     import token_locking_sparse_amd.surelock as S
+    # step workspace: the minimum (fixed buffers) never exceeds the recommended size, which grows with M
+    arr = (S.sl_layer_weights * 1)()
+    m = S.sl_model(0, 1, 4096, 32, 128, 12288, 126464, 1e-5, ctypes.cast(arr, ctypes.POINTER(S.sl_layer_weights)),
+                   None, None, None, 1024)
+    sizes = [(S.sl_step_workspace_min(m, 1, 1024, M), S.sl_step_workspace_size(m, 1, 1024, M)) for M in (1, 64, 256, 1024)]
+    assert all(0 < lo <= hi for lo, hi in sizes)
+    assert all(a[1] <= b[1] for a, b in zip(sizes, sizes[1:]))
+    assert sizes[2][1] > sizes[2][0]   # M = 256 splits the residual projections: partial planes reserved
     a = S.sl_kl_lock_workspace_size(1, 4096, 100, 126464)
     b = S.sl_kl_lock_workspace_size(1, 4096, 1639, 126464)
     assert b >= a > 0

@@ -45,7 +45,7 @@ def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
 
 
 # ------------------------------------------------------------------ one layer, hidden rows in
-def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False):
+def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False):
     sl = _sl()
     case = W.layer_case(dm, N, Ms, key=key)
     B, M = case.B, case.M_tot
@@ -58,7 +58,7 @@ def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False):
     vc = dev(case.v_cache, dm.dtype).reshape(1, B, N, dm.n_heads, dm.head_dim)
     kc0, vc0 = kc.clone(), vc.clone()
     st = sl.DeviceState(model, B, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, dm.dtype),
-                        k_cache=kc, v_cache=vc, with_h_out=True)
+                        k_cache=kc, v_cache=vc, with_h_out=True, minimal_workspace=minimal_ws)
     assert st.M_tot == M
     np.testing.assert_array_equal(st.act_idx[:M].cpu().numpy(), case.act_idx)
     st.step(eps=0.0, do_lock=False, no_kv_cache=no_kv_cache)
@@ -126,6 +126,14 @@ def test_layer_step_no_kv_cache_ablation(dm, N, Ms):
     oracle's step with attend_locked=False."""
     say("layer step no kv cache", dm.d, dm.dtype, N, Ms)
     _layer_case_run(dm, N, Ms, key=N + sum(Ms) + 1, tol=TOL[dm.dtype], no_kv_cache=True)
+
+
+@pytest.mark.parametrize("M", [512, 64])
+def test_layer_step_minimal_workspace(M):
+    """The smallest workspace sl_step accepts: the split-K residual projections (O and down at these
+    M) accumulate with fp32 atomics instead of partial-sum planes; same bar against the oracle."""
+    say("layer step minimal workspace", M)
+    _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M + 3, tol=TOL["bf16"], minimal_ws=True)
 
 
 def test_layer_step_batched_full_shape():

@@ -6,5 +6,5 @@ ABI of include/surelock.h); this package only loads it and marshals arguments.
 from .surelock import (SL_BF16, SL_F32, SureLockError, PinnedInt, lib, sl_attn_active,  # noqa: F401
                        sl_attn_workspace_size, sl_cache_scatter, sl_compact, sl_kl_lock,
                        sl_kl_lock_workspace_size, sl_rope_table, sl_step, sl_step_workspace_size,
-                       sl_gemm, sl_gemm_plan, SL_EPI_QKV_ROPE, SL_EPI_RESIDUAL, SL_EPI_SWIGLU, SL_EPI_LOGITS)
+                       sl_step_workspace_min, sl_gemm, sl_gemm_plan, SL_EPI_QKV_ROPE, SL_EPI_RESIDUAL, SL_EPI_SWIGLU, SL_EPI_LOGITS)
 from .runtime import DeviceModel, DeviceState  # noqa: F401

@@ -287,6 +287,11 @@ size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot) {
   return StepLayout(model, B, N, M_tot).total + resid_part_bytes_upto(model, M_tot);
 }
 
+size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot) {
+  if (!model) return 0;
+  return StepLayout(model, B, N, M_tot).total;
+}
+
 sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void* ws, size_t ws_bytes,
                   sl_stream stream) {
   g_err[0] = 0;

@@ -41,7 +41,11 @@ class DeviceModel:
                             C.cast(self._arr, C.POINTER(S.sl_layer_weights)), _dptr(embed), _dptr(lm_head),
                             self.rope.data_ptr(), rope_n)
 
-    def workspace_size(self, B: int, N: int, M_tot: int) -> int:
+    def workspace_size(self, B: int, N: int, M_tot: int, minimal: bool = False) -> int:
+        """Workspace bytes for a step of at most M_tot rows; minimal: the fixed buffers only
+        (split-K residual projections then accumulate with atomics)."""
+        if minimal:
+            return S.sl_step_workspace_min(self.s, B, N, M_tot)
         return S.sl_step_workspace_size(self.s, B, N, M_tot)
 
 
@@ -49,7 +53,7 @@ class DeviceState:
     """Sampler state for B sequences of N positions on the GPU."""
 
     def __init__(self, model: DeviceModel, B: int, N: int, *, tok=None, cand=None, locked=None, h_in=None,
-                 k_cache=None, v_cache=None, with_h_out=False, device="cuda"):
+                 k_cache=None, v_cache=None, with_h_out=False, minimal_workspace=False, device="cuda"):
         dm = model.dims
         L, d, H, Dh, V = dm["n_layers"], dm["d"], dm["n_heads"], dm["head_dim"], dm["vocab"]
         dt = model.dtype
@@ -78,7 +82,8 @@ class DeviceState:
         self.M_tot = S.sl_compact(self.locked, B, N, self.act_idx, self.act_off, self.m_host)
         self.t = 0
         # sized for M_tot = B*N, so it serves every later step (M only shrinks)
-        self.ws = torch.empty(model.workspace_size(B, N, B * N), dtype=torch.uint8, device=device)
+        self.ws = torch.empty(model.workspace_size(B, N, B * N, minimal_workspace), dtype=torch.uint8,
+                              device=device)
 
     def struct(self) -> S.sl_state:
         st = S.sl_state()

@@ -59,7 +59,8 @@ class sl_step_params(C.Structure):
 
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
-           "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_gemm", "sl_gemm_plan")
+           "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_step_workspace_min", "sl_gemm",
+           "sl_gemm_plan")
 
 _lib = None
 
@@ -87,6 +88,7 @@ def lib():
         "sl_rope_table": (i, [i, i, f, vp, vp]),
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
+        "sl_step_workspace_min": (sz, [C.POINTER(sl_model), i, i, i]),
         "sl_gemm": (i, [i, i, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp, vp, i, i, vp]),
         "sl_gemm_plan": (i, [i, i, i, i, i, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
                              C.POINTER(C.c_int)]),
@@ -216,6 +218,10 @@ def sl_rope_table(n_pos, head_dim, theta, table, stream=None):
 
 def sl_step_workspace_size(model: sl_model, B, N, M_tot) -> int:
     return int(lib().sl_step_workspace_size(C.byref(model), B, N, M_tot))
+
+
+def sl_step_workspace_min(model: sl_model, B, N, M_tot) -> int:
+    return int(lib().sl_step_workspace_min(C.byref(model), B, N, M_tot))
 
 
 def sl_step(model: sl_model, state: sl_state, params: sl_step_params, ws, stream=None):
