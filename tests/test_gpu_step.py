@@ -336,16 +336,40 @@ def test_tiny_loop_free_running_invariants():
     assert len(frozen) > 0
 
 
-# ------------------------------------------------------------------ batched ragged step with LM head and lock
-@pytest.mark.parametrize("dm,B,N,gate", [
-    (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=2048, dtype="bf16"), 3, 128, 0.5),
-    (W.Dims(n_layers=2, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16"), 2, 192, -1.0),
-])
-def test_batched_ragged_step(dm, B, N, gate):
+def test_step_with_every_position_locked_is_a_no_op():
+    """M_tot = 0 (every position locked): the step launches nothing and changes nothing."""
     sl = _sl()
-    say("batched step", B, N, gate)
+    dm = W.TINY
+    B, N = 2, 64
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                        cand=torch.ones(B * N, dtype=torch.uint8, device="cuda"),
+                        locked=torch.ones(B * N, dtype=torch.uint8, device="cuda"))
+    assert st.M_tot == 0
+    for t in range(2):
+        st.logits[t].fill_(3.0)
+    before = [x.clone() for x in (st.tok, st.locked, st.k_cache, st.v_cache, st.logits[0], st.logits[1])]
+    for t in range(2):
+        assert st.step(0.05, 0.5, dm.mask_id, True, 3) == 0
+    torch.cuda.synchronize()
+    after = (st.tok, st.locked, st.k_cache, st.v_cache, st.logits[0], st.logits[1])
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+    np.testing.assert_array_equal(st.act_off.cpu().numpy(), np.zeros(B + 1, np.int32))
+
+
+# ------------------------------------------------------------------ batched ragged step with LM head and lock
+@pytest.mark.parametrize("dm,B,N,gate,ms", [
+    (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=2048, dtype="bf16"), 3, 128, 0.5, None),
+    (W.Dims(n_layers=2, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16"), 2, 192, -1.0, None),
+    # one sequence fully locked (no active row) between two active ones
+    (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16"), 3, 128, 0.5, [40, 0, 100]),
+])
+def test_batched_ragged_step(dm, B, N, gate, ms):
+    sl = _sl()
+    say("batched step", B, N, gate, ms)
     eps = 0.05
-    Ms = W.ragged_ms(B, N, key=B * N)
+    Ms = W.ragged_ms(B, N, key=B * N) if ms is None else ms
     case = W.layer_case(dm, N, Ms, key=B + N)
     layers = [W.layer_weights(dm, l) for l in range(dm.n_layers)]
     head = W.lm_head_weights(dm)
