@@ -364,16 +364,20 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       int ns = 1;
       g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32; g.part = part;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "o gemm");
-      if (part && ns > 1) SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, x, s), "residual + norm");
-      else SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+      if (part && ns > 1)
+        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, x, s), "residual + norm");
+      else
+        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
       // SwiGLU FFN + residual, then the next block's RMSNorm (none after the last layer without a head)
       g.A = x; g.K = d; g.Nv = 2 * F; g.w0 = W.wg; g.w1 = W.wu; g.out0 = act; g.part = nullptr;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_SWIGLU, g, s), "gate/up gemm");
       g.A = act; g.K = F; g.Nv = d; g.w0 = W.wd; g.w1 = nullptr; g.out0 = h32; g.part = part;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "down gemm");
       void* xn = (head || l + 1 < m->n_layers) ? x : nullptr;
-      if (part && ns > 1) SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, xn, s), "residual + norm");
-      else if (xn) SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, xn, s), "norm");
+      if (part && ns > 1)
+        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, xn, s), "residual + norm");
+      else if (xn)
+        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, xn, s), "norm");
     }
     if (head) {
       sl::GemmArgs g{};
