@@ -136,6 +136,29 @@ def test_layer_step_minimal_workspace(M):
     _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M + 3, tol=TOL["bf16"], minimal_ws=True)
 
 
+@pytest.mark.parametrize("M", [256, 64])
+def test_layer_step_is_deterministic(M):
+    """Two runs of the same step give bit-identical hidden rows and caches: split-K partial sums are
+    added in a fixed order (no atomics) and every other reduction has a fixed shape."""
+    sl = _sl()
+    say("layer step determinism", M)
+    dm, N = W.LLADA_LAYER, 1024
+    case = W.layer_case(dm, N, [M], key=M + 5)
+    model = _dev_model(dm, [W.layer_weights(dm, 0)], rope_n=N)
+    locked = np.ones(N, np.uint8)
+    locked[case.act_idx] = 0
+    outs = []
+    for _ in range(2):
+        kc = dev(case.k_cache, "bf16").reshape(1, 1, N, dm.n_heads, dm.head_dim)
+        vc = dev(case.v_cache, "bf16").reshape(1, 1, N, dm.n_heads, dm.head_dim)
+        st = sl.DeviceState(model, 1, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, "bf16"),
+                            k_cache=kc, v_cache=vc, with_h_out=True)
+        st.step(eps=0.0, do_lock=False)
+        torch.cuda.synchronize()
+        outs.append((st.h_out[:M].clone(), kc.clone(), vc.clone()))
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
+
+
 def test_layer_step_batched_full_shape():
     """The LLaDA-8B-shaped layer on 8 sequences x N=2048 with ragged active sets (fraction per
     sequence uniform on [0.05, 0.8]): attention within each sequence only."""
