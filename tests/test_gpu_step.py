@@ -381,6 +381,27 @@ def test_step_with_every_position_locked_is_a_no_op():
     np.testing.assert_array_equal(st.act_off.cpu().numpy(), np.zeros(B + 1, np.int32))
 
 
+def test_tiny_loop_is_deterministic():
+    """Two free-running loops from the same start take the same lock decisions and produce the same
+    tokens, masks and posteriors, bit for bit."""
+    sl = _sl()
+    dm = W.TINY
+    B, N, T = 2, 64, 12
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    runs = []
+    for r in range(2):
+        say("deterministic loop run", r)
+        st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                            cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+        Ms = [st.step(0.05, 0.5, dm.mask_id, True, 3) for _ in range(T)]
+        torch.cuda.synchronize()
+        runs.append((Ms, st.tok.clone(), st.locked.clone(), st.lock_step.clone(), st.logits[0].clone(),
+                     st.logits[1].clone()))
+    assert runs[0][0] == runs[1][0]
+    assert all(torch.equal(a, b) for a, b in zip(runs[0][1:], runs[1][1:]))
+
+
 # ------------------------------------------------------------------ batched ragged step with LM head and lock
 @pytest.mark.parametrize("dm,B,N,gate,ms", [
     (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=2048, dtype="bf16"), 3, 128, 0.5, None),
