@@ -167,6 +167,22 @@ def test_layer_step_batched_full_shape():
     _layer_case_run(W.LLADA_LAYER, 2048, Ms, key=8 * 2048, tol=TOL["bf16"])
 
 
+_LLADA8B = {}
+
+
+def _llada8b_weights():
+    """Storage weights of the 32-layer LLaDA-8B-shaped model (generated once per test session)."""
+    if not _LLADA8B:
+        from concurrent.futures import ThreadPoolExecutor
+        dm = W.LLADA_8B
+        say("32-layer model: generating weights")
+        with ThreadPoolExecutor(16) as ex:
+            layers = list(ex.map(lambda l: W.layer_weights(dm, l), range(dm.n_layers)))
+            emb_f, head_f = ex.submit(W.embed_weights, dm), ex.submit(W.lm_head_weights, dm)
+            _LLADA8B["w"] = (layers, emb_f.result(), head_f.result())
+    return _LLADA8B["w"]
+
+
 @pytest.mark.slow
 def test_full_model_step_32_layers():
     """One step (t = 0, all 512 positions active) of the 32-layer LLaDA-8B-shaped model: embedding of
@@ -177,15 +193,10 @@ def test_full_model_step_32_layers():
     bf16 gives those figures against the float64 oracle.  The test holds the GPU to relative L2
     <= 1.5e-2 with no element beyond 7 rms; argmax and sampler choices may differ only at near-ties
     within that error."""
-    from concurrent.futures import ThreadPoolExecutor
     sl = _sl()
     dm = W.LLADA_8B
     B, N, n_prompt, k_unmask = 1, 512, 128, 3
-    say("32-layer step: generating weights")
-    with ThreadPoolExecutor(16) as ex:
-        layers = list(ex.map(lambda l: W.layer_weights(dm, l), range(dm.n_layers)))
-        emb_f, head_f = ex.submit(W.embed_weights, dm), ex.submit(W.lm_head_weights, dm)
-        emb, head = emb_f.result(), head_f.result()
+    layers, emb, head = _llada8b_weights()
     tok0 = W.prompt_tokens(dm, B, N, n_prompt)
     cand0 = (tok0 != dm.mask_id).astype(np.uint8)
     model = _dev_model(dm, layers, emb, head, rope_n=N)
@@ -232,6 +243,122 @@ def test_full_model_step_32_layers():
     for gp in set(picked) & set(gpu_picked.tolist()):
         i = int(gp)
         assert gtok[gp] == ost.tok[gp] or top2[i, 1] - top2[i, 0] <= 2 * 7 * rms
+
+
+@pytest.mark.slow
+def test_full_model_late_step_32_layers():
+    """A late step of the 32-layer LLaDA-8B-shaped model, teacher-forced from a seeded mid-loop state:
+    N = 512 with 128 prompt ids and 200 positions already unmasked to random ids; 260 of those 328
+    positions locked (their cached K/V in every layer random N(0,1)), 252 active; t = 40 with the
+    previous posterior equal to the oracle's logits of this step plus N(0, 0.05^2) drift; eps = 0.05,
+    gate at the median, 3 unmasks.
+
+    Attending to random unit-variance caches grows the residual stream faster than at t = 0 (hidden
+    rms 13.4 after layer 31 against the oracle), and the bf16 roundings compound with it: a CPU
+    emulation that rounds to bf16 exactly where the kernels store bf16 gives logits relative L2
+    2.23e-2, rms 0.0286, max 0.181 (6.3 rms) on this state.  The test holds the GPU to relative L2
+    <= 2.8e-2 (the t = 0 test's 1.25x margin over its emulation) with no element beyond 7 rms; an
+    argmax may differ only at a top-two margin within 2 * 7 rms.  KL within 1e-3; gate, lock,
+    compaction and sampler exact against the GPU's own statistics, and against the oracle except where
+    the measured u error or a confidence near-tie can move a decision."""
+    sl = _sl()
+    dm = W.LLADA_8B
+    B, N, t, eps, gate, k_unmask = 1, 512, 40, 0.05, 0.5, 3
+    layers, emb, head = _llada8b_weights()
+    g = W.rng(W.SEED_SETS, 7777)
+    tok0 = W.prompt_tokens(dm, B, N, 128)
+    done = 128 + g.permutation(N - 128)[:200]
+    tok0[done] = g.integers(0, dm.vocab - 1, size=200)
+    unmasked = np.flatnonzero(tok0 != dm.mask_id)
+    locked = np.zeros(N, np.uint8)
+    locked[g.permutation(unmasked)[:260]] = 1
+    cand0 = (tok0 != dm.mask_id).astype(np.uint8)
+    act = np.flatnonzero(locked == 0).astype(np.int32)
+    M = len(act)
+    kc_st = [W.to_storage(W.normal(W.rng(W.SEED_CACHE, 7777, l, 0), (B, N, dm.n_heads, dm.head_dim), 1.0), "bf16")
+             for l in range(dm.n_layers)]
+    vc_st = [W.to_storage(W.normal(W.rng(W.SEED_CACHE, 7777, l, 1), (B, N, dm.n_heads, dm.head_dim), 1.0), "bf16")
+             for l in range(dm.n_layers)]
+    # oracle: this step's logits (the layers and LM head over the active rows), then the statistics
+    say("32-layer late step: oracle, M = %d" % M)
+    od = _odims(dm)
+    om = O.OracleModel(od, dm.n_layers, lambda l: {k: O.widen(v, dm.dtype) for k, v in layers[l].items()},
+                       O.widen(emb, dm.dtype), O.widen(head, dm.dtype))
+    ost = O.OracleState(B=B, N=N, t=0, locked=locked.copy(), kc=[O.widen(k, "bf16") for k in kc_st],
+                        vc=[O.widen(v, "bf16") for v in vc_st], tok=tok0.copy(), cand=cand0.copy())
+    z = O.step(om, ost, 0.0, -1.0, do_lock=False, mask_id=dm.mask_id).logits
+    prev_st = W.to_storage(z.astype(np.float32) + W.normal(W.rng(W.SEED_DRIFT, 7777), z.shape, 0.05), "bf16")
+    ref = O.posterior_stats(z, O.widen(prev_st, "bf16"), dm.mask_id)
+    off = np.array([0, M], np.int32)
+    lr = O.lock_update(locked, act, off, B, N, ref.kl, ref.u, cand0, eps, gate, True)
+    # GPU: the same state at step t
+    say("32-layer late step: GPU")
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    kc = torch.stack([dev(k, "bf16") for k in kc_st])
+    vc = torch.stack([dev(v, "bf16") for v in vc_st])
+    lk = torch.from_numpy(np.flatnonzero(locked)).cuda()
+    kc_lock0, vc_lock0 = kc[:, 0, lk].clone(), vc[:, 0, lk].clone()
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(), cand=torch.from_numpy(cand0.copy()).cuda(),
+                        locked=torch.from_numpy(locked.copy()).cuda(), k_cache=kc, v_cache=vc)
+    assert st.M_tot == M
+    gi = torch.from_numpy(act.astype(np.int64)).cuda()
+    st.logits[(t + 1) & 1].index_copy_(0, gi, dev(prev_st, "bf16"))
+    st.t = t
+    st.step(eps, gate, dm.mask_id, True, k_unmask)
+    torch.cuda.synchronize()
+    gz = host64(st.logits[t & 1].index_select(0, gi))
+    d = gz - z
+    rms = float(np.sqrt(np.mean(d * d)))
+    rel = float(np.linalg.norm(d) / np.linalg.norm(z))
+    say("32-layer late-step logits: rel L2 %.3e rms %.3e max %.3e" % (rel, rms, np.abs(d).max()))
+    assert rel <= 2.8e-2
+    assert np.abs(d).max() <= max(7 * rms, 2e-2)
+    keep = np.ones(dm.vocab, bool)
+    keep[dm.mask_id] = False
+    zk, gk = z[:, keep], gz[:, keep]
+    ia, ga = np.argmax(zk, 1), np.argmax(gk, 1)
+    top2 = np.sort(zk, 1)[:, -2:]
+    say("late-step argmax agreement %.4f" % float(np.mean(ia == ga)))
+    for i in np.flatnonzero(ia != ga):
+        assert top2[i, 1] - top2[i, 0] <= 2 * 7 * rms, "argmax mismatch at %d with margin %.3g" % (i, top2[i, 1] - top2[i, 0])
+    del zk, gk
+    # locked rows' caches untouched in every layer
+    assert torch.equal(kc[:, 0, lk], kc_lock0) and torch.equal(vc[:, 0, lk], vc_lock0)
+    kl, u = st.kl[:M].cpu().numpy(), st.u[:M].cpu().numpy()
+    assert np.max(np.abs(kl - ref.kl)) <= KL_BAND
+    du = float(np.max(np.abs(u - ref.u)))
+    # exact against the GPU's own statistics: gate threshold, lock update, compaction
+    thr = float(st.gate_thr[0].item())
+    assert thr == np.sort(u)[int(np.floor(np.float32(gate) * (M - 1)))]
+    new = (cand0[act] != 0) & (kl <= np.float32(eps)) & (u <= thr)
+    want = locked.copy()
+    want[act[new]] = 1
+    g_locked = st.locked.cpu().numpy()
+    np.testing.assert_array_equal(g_locked, want)
+    ri, ro = O.active_set(g_locked, B, N)
+    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(st.act_idx[:int(ro[-1])].cpu().numpy(), ri)
+    # against the oracle: differing decisions only inside the band the u error allows
+    band = 2 * du + abs(thr - lr.gate_thr[0])
+    diff = np.flatnonzero(new != lr.new_lock)
+    say("late-step locks: gpu %d oracle %d differing %d (u error %.2e)" % (int(new.sum()), int(lr.new_lock.sum()),
+                                                                        len(diff), du))
+    assert np.all(np.abs(ref.u[diff] - lr.gate_thr[0]) <= band)
+    # sampler: the GPU's picks follow its own confidences; against the oracle only near-ties differ
+    gtok = st.tok.cpu().numpy()
+    gpu_picked = np.flatnonzero(gtok != tok0)
+    assert len(gpu_picked) == k_unmask and np.all(tok0[gpu_picked] == dm.mask_id)
+    conf_g = st.conf[:M].cpu().numpy()
+    masked_rows = np.flatnonzero(tok0[act] == dm.mask_id)
+    order = masked_rows[np.lexsort((act[masked_rows], -conf_g[masked_rows]))][:k_unmask]
+    np.testing.assert_array_equal(np.sort(act[order]), np.sort(gpu_picked))
+    g_am = st.argmax[:M].cpu().numpy()
+    np.testing.assert_array_equal(gtok[act[order]], g_am[order])
+    picked = O.sampler_unmask(tok0.copy(), cand0.copy(), act, off, N, ref.argmax, ref.conf, dm.mask_id, k_unmask)
+    kth = np.sort(ref.conf[masked_rows])[-k_unmask]
+    rowof = {int(p): i for i, p in enumerate(act)}
+    for gp in set(picked) ^ set(gpu_picked.tolist()):
+        assert abs(ref.conf[rowof[gp]] - kth) <= 0.1 * kth, "sampler pick %d not a near-tie" % gp
 
 
 # ------------------------------------------------------------------ tiny fp32 sampler loop (teacher-forced)
