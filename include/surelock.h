@@ -182,7 +182,9 @@ typedef enum {
  *            RESIDUAL and LOGITS take w0 only (n = n_out).
  *   rope     [>=N][head_dim/2][2] from sl_rope_table (QKV_ROPE only).
  *   act_idx/act_off/B/N map compact rows to positions (QKV_ROPE, LOGITS).
- * Limits: K*elem_size % 128 == 0; n_out % 64 == 0; QKV_ROPE needs d % 128 == 0.
+ * Limits: K*elem_size % 128 == 0; n_out % 64 == 0; QKV_ROPE needs d % 128 == 0;
+ * M*K*elem_size <= 4 GiB (A rows are addressed with 32-bit offsets).  Beyond
+ * them the call returns SL_ERR_UNSUPPORTED and launches nothing.
  */
 sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
                   const void* w1, const void* w2, void* out0, void* out1, void* out2,
@@ -279,7 +281,8 @@ typedef struct {
  *       partial-sum planes (same results up to the order of the additions); below
  *       that the call fails with SL_ERR_INVALID.
  * Limits: d % 128 == 0, ffn % 64 == 0, vocab % 128 == 0, head_dim in {32, 64, 128},
- * n_heads*head_dim == d, N % 64 == 0, rope_n >= N.
+ * n_heads*head_dim == d, N % 64 == 0, N <= 65536, rope_n >= N, and
+ * M_tot*max(d, ffn)*elem_size <= 4 GiB (the GEMMs' A operands).
  */
 sl_status sl_step(const sl_model* model, sl_state* state, const sl_step_params* params,
                   void* ws, size_t ws_bytes, sl_stream stream);

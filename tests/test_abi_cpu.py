@@ -53,6 +53,11 @@ def test_status_strings_and_host_checks():
     st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(18),
                           1, 64, 0, 1, 64, ctypes.c_float(1.0), None, ctypes.c_void_p(16), 1 << 20, None)
     assert st == 1 and b"aligned" in L.sl_last_error()
+    # a GEMM A operand beyond the 32-bit row offsets (300000 x 8192 bf16 = 4.9 GB) is refused, not launched
+    dummy = ctypes.c_void_p(256)
+    st = L.sl_gemm(0, 1, dummy, 300000, 8192, 4096, dummy, None, None, dummy, None, None, None, 0, 0, None, None,
+                   1, 1, None)
+    assert st == 2 and b"4 GiB" in L.sl_last_error()
 
 
 def test_workspace_sizes_are_monotone_in_rows():

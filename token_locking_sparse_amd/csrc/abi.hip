@@ -253,6 +253,7 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
   const sl::EpiKind epi = (sl::EpiKind)epilogue;
   SL_REQUIRE(sl::gemm_supported(dtype, epi, n_out, K, d, head_dim), SL_ERR_UNSUPPORTED,
              "unsupported GEMM shape (K=%d, n_out=%d)", K, n_out);
+  SL_REQUIRE(sl::gemm_a_fits(M, K, elem_bytes(dtype)), SL_ERR_UNSUPPORTED, "A operand of %d x %d exceeds 4 GiB", M, K);
   if (epi == sl::EPI_QKV) {
     SL_REQUIRE(w1 && w2 && out1 && out2 && rope && act_idx && act_off, SL_ERR_INVALID, "QKV needs wk, wv, caches, rope, act lists");
     SL_REQUIRE(n_out == 3 * d && d % 128 == 0 && head_dim > 0 && d % head_dim == 0 && head_dim % 2 == 0,
@@ -308,6 +309,8 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
              "NULL state buffer");
   SL_REQUIRE(st->h_in || (m->embed && st->tok), SL_ERR_INVALID, "need h_in, or embed and tok");
   SL_REQUIRE(st->t >= 0, SL_ERR_INVALID, "t < 0");
+  SL_REQUIRE(sl::gemm_a_fits(M, m->d > m->ffn ? m->d : m->ffn, elem_bytes(m->dtype)), SL_ERR_UNSUPPORTED,
+             "M_tot = %d active rows exceed the GEMMs' 4 GiB A operand", M);
   const bool head = m->lm_head != nullptr;
   const bool lock = head && p->do_lock;
   if (head) SL_REQUIRE(st->logits[0] && st->logits[1], SL_ERR_INVALID, "logits buffers missing");

@@ -99,6 +99,8 @@ hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s,
 // Number of K splits launch_gemm runs for this shape (1 = none).
 int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv);
 int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh);
+// The GEMM addresses its A rows with 32-bit byte offsets: M * K * element bytes must stay within 4 GiB.
+inline bool gemm_a_fits(long long M, long long K, int elem_bytes) { return M * K * elem_bytes <= (1LL << 32); }
 // Tile (rows, columns), split-K and load path (1: through registers) the launcher
 // picks for this shape; vb may be NULL.
 void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, int* split, int* vb);
