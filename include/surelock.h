@@ -197,7 +197,10 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
  * the load path (*through_registers = 1: both operands' tiles go through vector
  * registers into LDS, used when few rows stream a wide weight matrix; 0: direct
  * global-to-LDS loads), chosen by the library's cost model.  through_registers
- * may be NULL.  Writes nothing on error.  No device work.
+ * may be NULL.  Writes nothing on error.  No device work.  sl_step's residual
+ * projections may split K differently: there the split-K partial sums go to
+ * workspace planes that the fused residual reduce + RMSNorm adds up, which the
+ * cost model prices below sl_gemm's fp32 atomics.
  */
 sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* tile_m, int* tile_n,
                        int* split_k, int* through_registers);

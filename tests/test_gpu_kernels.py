@@ -248,10 +248,13 @@ GEMM_CASES = [
     ("qkv", 700, 1024, 3072), ("logits", 130, 512, 6144), ("logits", 600, 1024, 12288),
     ("swiglu", 16, 512, 24576), ("swiglu", 16, 512, 768), ("resid", 1, 2048, 6144),
     ("logits", 5, 1024, 24576), ("qkv", 16, 8192, 24576),
+    ("qkv", 250, 512, 12288), ("swiglu", 450, 512, 6144), ("resid", 200, 512, 12288), ("logits", 770, 512, 3072),
+    ("qkv", 390, 512, 12288), ("swiglu", 200, 512, 18432), ("resid", 700, 512, 6144), ("logits", 450, 512, 12288),
+    ("qkv", 520, 512, 6144), ("resid", 900, 512, 8192),
 ]
 # (tile rows, tile columns, weights through registers instead of direct-to-LDS loads)
 ALL_TILES = {(256, 256, 0), (256, 128, 0), (128, 256, 0), (128, 128, 0), (128, 64, 0), (256, 192, 0), (128, 384, 0),
-             (64, 128, 0), (64, 64, 0), (64, 128, 1)}
+             (64, 128, 0), (64, 64, 0), (64, 128, 1), (128, 96, 0), (128, 192, 0)}
 
 
 def bf16_out_err(got, ref):

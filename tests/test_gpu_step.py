@@ -130,8 +130,9 @@ def test_layer_step_no_kv_cache_ablation(dm, N, Ms):
 
 @pytest.mark.parametrize("M", [512, 64])
 def test_layer_step_minimal_workspace(M):
-    """The smallest workspace sl_step accepts: the split-K residual projections (O and down at these
-    M) accumulate with fp32 atomics instead of partial-sum planes; same bar against the oracle."""
+    """The smallest workspace sl_step accepts: the split-K residual projections (down at M = 512, O and
+    down at M = 64) accumulate with fp32 atomics instead of partial-sum planes; same bar against the
+    oracle."""
     say("layer step minimal workspace", M)
     _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M + 3, tol=TOL["bf16"], minimal_ws=True)
 

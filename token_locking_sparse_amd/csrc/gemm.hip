@@ -466,7 +466,7 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
 // weights rotated over copies larger than the Infinity Cache); occ =
 // workgroups one CU holds at once, cap = chip-wide weight streaming rate.
 struct TileCfg { int BM, BN, RB, S; float rate; int occ; float cap; bool vb; };
-constexpr int kNumCfgs = 10;
+constexpr int kNumCfgs = 12;
 constexpr float kStreamCapBytesPerUs = 5.0e6f;  // weight streaming from HBM by direct-to-LDS loads
 static const TileCfg kCfgs[kNumCfgs] = {
     {256, 256, 64, 4, 2.35e6f, 1, kStreamCapBytesPerUs, false},   // 0: eight waves 2x4, wave tile 128x64
@@ -479,19 +479,25 @@ static const TileCfg kCfgs[kNumCfgs] = {
     {64, 128, 128, 6, 1.06e6f, 1, kStreamCapBytesPerUs, false},   // 7: four waves 1x4, wave tile 64x32: weight streaming at small M
     {64, 64, 128, 8, 0.82e6f, 1, kStreamCapBytesPerUs, false},    // 8: four waves 2x2, wave tile 32x32: weight streaming at small M
     {64, 128, 128, 6, 1.06e6f, 2, 6.0e6f, true},                  // 9: as 7, through registers (VB), two per CU
+    // 96-wide wave tiles: 12288 columns make 128 column tiles of 96 (256 tiles at 256 rows) and 64 of
+    // 192 (256 tiles at 512 rows), where 128-wide tiles leave a quarter of the CUs idle
+    {128, 96, 128, 4, 1.30e6f, 1, kStreamCapBytesPerUs, false},   // 10: four waves 4x1, wave tile 32x96
+    {128, 192, 128, 3, 1.80e6f, 1, kStreamCapBytesPerUs, false},  // 11: four waves 2x2, wave tile 64x96
 };
 constexpr int kCUs = 256;
 constexpr float kCuBytesPerUs = 4.2e4f;        // what one CU pulls from HBM (latency bound)
 constexpr float kLoadLatencyUs = 1.0f;          // what a workgroup's S-1 tiles in flight amortise
 constexpr float kAtomicBytesPerUs = 1.5e6f;     // fp32 atomic adds of split-K partials
+constexpr float kPartBytesPerUs = 3.0e6f;       // partial-sum planes beyond the first (store, then read back)
 constexpr float kLaunchUs = 2.0f;
 
 // Estimated time of a launch: the compute of the most loaded CU, or streaming
 // the weights, whichever is longer.  The resident workgroups keep
 // (S-1) weight tiles (BN x RB bytes each) in flight, and each CU pulls at most
-// kCuBytesPerUs, so few workgroups stream slower than the chip can; split-K adds
-// its atomic traffic.
-static float est_us(const GemmArgs& a, int eb, int c, int split) {
+// kCuBytesPerUs, so few workgroups stream slower than the chip can.  Split-K adds
+// its atomic traffic, or, when the caller provides partial-sum planes that the
+// residual reduce + RMSNorm sums (part), the extra planes it stores and reads back.
+static float est_us(const GemmArgs& a, int eb, int c, int split, bool part) {
   const TileCfg& g = kCfgs[c];
   const long MT = (a.M + g.BM - 1) / g.BM, NT = a.Nv / g.BN;
   const long blocks = MT * NT * split;
@@ -504,11 +510,13 @@ static float est_us(const GemmArgs& a, int eb, int c, int split) {
   if (bw > (float)cus * kCuBytesPerUs) bw = (float)cus * kCuBytesPerUs;
   if (bw > g.cap) bw = g.cap;
   const float mem = (float)a.Nv * a.K * eb / bw;
-  const float atom = split > 1 ? (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs : 0.f;
+  const float atom = split <= 1 ? 0.f
+                     : part ? (float)a.M * a.Nv * 4.f * (split - 1) / kPartBytesPerUs
+                            : (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs;
   return (comp > mem ? comp : mem) + atom + kLaunchUs;
 }
 
-static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& split) {
+static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, bool part, int& cfg, int& split) {
   float best = 3.4e38f;
   cfg = -1; split = 1;
   for (int c = 0; c < kNumCfgs; ++c) {
@@ -518,7 +526,7 @@ static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, int& cfg, int& spli
     const int KI = a.K * eb / g.RB;
     for (int sp = 1; sp <= 8; sp *= 2) {
       if (sp > 1 && (epi != EPI_RESID || KI / sp < 8 || g.vb)) break;   // the register path streams whole K
-      const float t = est_us(a, eb, c, sp);
+      const float t = est_us(a, eb, c, sp, part && epi == EPI_RESID);
       if (t < best) { best = t; cfg = c; split = sp; }
     }
   }
@@ -535,7 +543,7 @@ int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh) {
 template <typename T>
 static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit) {
   int c, split;
-  pick_cfg(a, epi, (int)sizeof(T), c, split);
+  pick_cfg(a, epi, (int)sizeof(T), a.part != nullptr, c, split);
   if (nsplit) *nsplit = c >= 0 ? splits_launched(a.K * (int)sizeof(T) / kCfgs[c].RB, split) : 1;
   switch (c) {
     case 0: return run_cfg<T, 256, 256, 2, 4, 64, 4>(epi, a, s, split);
@@ -548,6 +556,8 @@ static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s, int* n
     case 7: return run_cfg<T, 64, 128, 1, 4, 128, 6>(epi, a, s, split);
     case 8: return run_cfg<T, 64, 64, 2, 2, 128, 8>(epi, a, s, split);
     case 9: return run_cfg<T, 64, 128, 1, 4, 128, 6, true>(epi, a, s, split);
+    case 10: return run_cfg<T, 128, 96, 4, 1, 128, 4>(epi, a, s, split);
+    case 11: return run_cfg<T, 128, 192, 2, 2, 128, 3>(epi, a, s, split);
   }
   return hipErrorInvalidValue;
 }
@@ -556,7 +566,7 @@ void gemm_plan(int dtype, EpiKind epi, int M, int K, int Nv, int* bm, int* bn, i
   GemmArgs a{};
   a.M = M; a.K = K; a.Nv = Nv;
   int c, sp;
-  pick_cfg(a, epi, dtype == 0 ? 2 : 4, c, sp);
+  pick_cfg(a, epi, dtype == 0 ? 2 : 4, false, c, sp);
   *bm = c >= 0 ? kCfgs[c].BM : 0;
   *bn = c >= 0 ? kCfgs[c].BN : 0;
   *split = c >= 0 ? sp : 0;
@@ -568,7 +578,7 @@ int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv) {
   a.M = M; a.K = K; a.Nv = Nv;
   const int eb = dtype == 0 ? 2 : 4;
   int c, sp;
-  pick_cfg(a, epi, eb, c, sp);
+  pick_cfg(a, epi, eb, true, c, sp);
   return c >= 0 ? splits_launched(K * eb / kCfgs[c].RB, sp) : 1;
 }
 

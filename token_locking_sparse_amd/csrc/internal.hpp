@@ -96,7 +96,8 @@ struct GemmArgs {
 };
 // nsplit (may be NULL) receives the number of K splits launched.
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit = nullptr);
-// Number of K splits launch_gemm runs for this shape (1 = none).
+// Number of K splits launch_gemm runs for this shape when partial-sum planes are
+// provided (GemmArgs::part set; 1 = none): the planes' workspace is sized from it.
 int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv);
 int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh);
 // The GEMM addresses its A rows with 32-bit byte offsets: M * K * element bytes must stay within 4 GiB.
