@@ -278,7 +278,8 @@ typedef struct {
  * §2: block input frozen, K/V cached for every layer).  A_t within A_{t-1}
  * guarantees logits[(t+1)%2] holds p_{t-1} for every active row.
  *   ws: sl_step_workspace_size(...) bytes (any contents).  A workspace sized for
- *       the first step's M_tot serves every later step (M only shrinks).  Less is
+ *       the first step's M_tot serves every later step (M only shrinks): the size is
+ *       the largest any step with at most M_tot rows needs.  Less is
  *       accepted down to the fixed buffers of the step; the O and down projections
  *       then accumulate their split-K partial sums with fp32 atomics instead of the
  *       partial-sum planes (same results up to the order of the additions); below
@@ -289,9 +290,12 @@ typedef struct {
  */
 sl_status sl_step(const sl_model* model, sl_state* state, const sl_step_params* params,
                   void* ws, size_t ws_bytes, sl_stream stream);
+/* The largest workspace any step with at most M_tot active rows needs.  Not
+ * a per-row product: fewer rows can need more (the attention splits its keys,
+ * and stores per-split partials, only when few query tiles would idle the chip). */
 size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot);
-/* The smallest workspace sl_step accepts for a step with M_tot active rows: the
- * fixed buffers only (split-K residual projections then use fp32 atomics). */
+/* The smallest workspace sl_step accepts for every step with at most M_tot active
+ * rows: the fixed buffers only (split-K residual projections then use fp32 atomics). */
 size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot);
 
 #ifdef __cplusplus

@@ -72,6 +72,10 @@ def test_workspace_sizes_are_monotone_in_rows():
     assert all(0 < lo <= hi for lo, hi in sizes)
     assert all(a[1] <= b[1] for a, b in zip(sizes, sizes[1:]))
     assert sizes[2][1] > sizes[2][0]   # M = 256 splits the residual projections: partial planes reserved
+    # a workspace sized for M rows serves every later step with fewer rows, also where the attention's
+    # key-split partials make a smaller step need more (M = 128 splits its keys, M = 129 does not)
+    dense = [(S.sl_step_workspace_min(m, 1, 1024, M), S.sl_step_workspace_size(m, 1, 1024, M)) for M in range(100, 160)]
+    assert all(a[0] <= b[0] and a[1] <= b[1] for a, b in zip(dense, dense[1:]))
     a = S.sl_kl_lock_workspace_size(1, 4096, 100, 126464)
     b = S.sl_kl_lock_workspace_size(1, 4096, 1639, 126464)
     assert b >= a > 0

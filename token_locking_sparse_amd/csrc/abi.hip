@@ -67,12 +67,14 @@ size_t resid_part_bytes(const sl_model* m, int M) {
   return sp > 1 ? align256((size_t)sp * M * m->d * 4) : 0;
 }
 
-// The most partial-sum space any step with at most M_tot rows needs (the split the
-// launcher picks is not monotone in M).
-size_t resid_part_bytes_upto(const sl_model* m, int M_tot) {
+// The largest workspace any step with at most M_tot rows needs: the fixed regions, plus the
+// split-K partial planes when with_part.  Neither is monotone in M: the attention splits its keys
+// (and stores per-split partials) only when few query tiles leave the chip idle, and the
+// launcher's split of the residual projections changes with M.
+size_t step_ws_upto(const sl_model* m, int B, int N, int M_tot, bool with_part) {
   size_t best = 0;
-  for (int M = 1; M <= M_tot; ++M) {
-    const size_t b = resid_part_bytes(m, M);
+  for (int M = 1; M <= (M_tot > 1 ? M_tot : 1); ++M) {
+    const size_t b = StepLayout(m, B, N, M).total + (with_part ? resid_part_bytes(m, M) : 0);
     if (b > best) best = b;
   }
   return best;
@@ -285,12 +287,12 @@ sl_status sl_gemm_plan(int dtype, int epilogue, int M, int K, int n_out, int* ti
 
 size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot) {
   if (!model) return 0;
-  return StepLayout(model, B, N, M_tot).total + resid_part_bytes_upto(model, M_tot);
+  return step_ws_upto(model, B, N, M_tot, true);
 }
 
 size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot) {
   if (!model) return 0;
-  return StepLayout(model, B, N, M_tot).total;
+  return step_ws_upto(model, B, N, M_tot, false);
 }
 
 sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void* ws, size_t ws_bytes,
