@@ -348,6 +348,10 @@ ATTN_CASES = [
     # dtype, Dh, H, N, Ms
     ("bf16", 128, 2, 256, [256, 37]),
     ("bf16", 128, 3, 1024, [5]),          # few query tiles: split over keys + merge
+    ("bf16", 128, 32, 1024, [40]),        # split four ways (128 keys per key group)
+    ("bf16", 128, 32, 512, [9]),          # short sequence, few queries: four key groups, no split
+    ("bf16", 128, 4, 256, [3, 60]),       # the same with two sequences
+    ("bf16", 128, 2, 64, [7]),            # four key groups over two 32-key tiles: two groups idle
     ("bf16", 128, 8, 512, [300, 1, 77]),  # heads a multiple of 8 (XCD placement), ragged
     ("bf16", 128, 16, 1024, [640]),       # several query tiles per head, no split
     ("bf16", 128, 32, 1024, [1024]),      # 128-query workgroups (two key groups)
@@ -391,6 +395,7 @@ def test_attention_parity(dtype, Dh, H, N, Ms):
 # other split sees no key at all).
 ATTN_EXCL_CASES = [
     ("bf16", 128, 3, 1024, [5], "first"),
+    ("bf16", 128, 32, 512, [9], "random"),
     ("bf16", 128, 8, 512, [300, 1, 77], "random"),
     ("bf16", 128, 32, 1024, [200, 180], "ends"),
     ("bf16", 128, 16, 1024, [200], "ends"),

@@ -716,7 +716,12 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
 // = 64-query workgroups with four key groups, for when 128-query workgroups
 // would leave the chip half idle and 64-query ones need no key split.  Splitting the keys over workgroups costs a
 // second pass over fp32 partials (several us), so it is used only when the
-// query tiles alone leave most of the chip idle.
+// query tiles alone leave most of the chip idle.  Then each key group's run of
+// keys is the latency chain: the transposed-score kernels split only down to
+// 128 keys per key group, and for N <= 512 take shape 1 (four key groups of at
+// most 128 keys) with no split and no merge pass.  Measured at 32 heads and
+// M <= 64: N = 512, 13.4-14.3 us against 16.6-17.9 us split four ways;
+// N = 1024, 15.2-17.1 us split four ways against 16.2-18.6 us split eight ways.
 struct AttnPlan { int bq, shape, slots, nsplit, tps; };
 
 static AttnPlan attn_plan(int B, int N, int M_tot, int H, bool tr) {
@@ -727,8 +732,16 @@ static AttnPlan attn_plan(int B, int N, int M_tot, int H, bool tr) {
   if (tr && ((M_tot + kBQ - 1) / kBQ) * H < 256 && ((M_tot + 63) / 64) * H >= 64) { p.bq = 64; p.shape = 1; }
   const int blocks = ((M_tot + p.bq - 1) / p.bq) * H;   // useful workgroups without a split
   p.nsplit = 1;
-  if (blocks < 64)
-    while (blocks * p.nsplit < 256 && p.nsplit * 2 <= tiles / 2) p.nsplit *= 2;
+  if (blocks < 64) {
+    if (tr && N <= 4 * 128) {
+      p.bq = 64;
+      p.shape = 1;
+    } else {
+      const int G = tr ? 2 : 1;   // key groups of shape 0
+      while (blocks * p.nsplit < 256 && p.nsplit * 2 <= tiles / 2 && (!tr || N / (2 * p.nsplit * G) >= 128))
+        p.nsplit *= 2;
+    }
+  }
   p.tps = (tiles + p.nsplit - 1) / p.nsplit;
   p.slots = (M_tot + p.bq - 1) / p.bq + B;
   return p;
