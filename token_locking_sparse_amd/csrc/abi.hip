@@ -207,7 +207,7 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
   SL_REQUIRE(B >= 1 && N >= 1 && V > 0 && M_tot >= 0, SL_ERR_INVALID, "bad size");
   SL_REQUIRE((long long)M_tot <= (long long)B * N, SL_ERR_INVALID, "M_tot > B*N");
   SL_REQUIRE(N <= 65536, SL_ERR_UNSUPPORTED, "N > 65536");
-  SL_REQUIRE((V * elem_bytes(dtype)) % 16 == 0, SL_ERR_UNSUPPORTED, "V*elem_size %% 16 != 0 (V = %d)", V);
+  SL_REQUIRE(((long long)V * elem_bytes(dtype)) % 16 == 0, SL_ERR_UNSUPPORTED, "V*elem_size %% 16 != 0 (V = %d)", V);
   SL_REQUIRE(M_tot == 0 || (logits_cur && kl && u && lse), SL_ERR_INVALID, "NULL logits / kl / u / lse");
   SL_REQUIRE(M_tot == 0 || !params->have_prev || logits_prev, SL_ERR_INVALID, "NULL logits_prev");
   SL_REQUIRE(params->gate_q <= 1.f, SL_ERR_INVALID, "gate_q > 1");
