@@ -486,6 +486,7 @@ static const TileCfg kCfgs[kNumCfgs] = {
 };
 constexpr int kCUs = 256;
 constexpr float kCuBytesPerUs = 4.2e4f;        // what one CU pulls from HBM (latency bound)
+constexpr float kCuLoadBytesPerUs = 5.5e4f;    // what one CU loads of both operands, L2 hits included
 constexpr float kLoadLatencyUs = 1.0f;          // what a workgroup's S-1 tiles in flight amortise
 constexpr float kAtomicBytesPerUs = 1.5e6f;     // fp32 atomic adds of split-K partials
 constexpr float kPartBytesPerUs = 3.0e6f;       // partial-sum planes beyond the first (store, then read back)
@@ -509,7 +510,11 @@ static float est_us(const GemmArgs& a, int eb, int c, int split, bool part) {
   float bw = (float)resident * (g.S - 1) * g.BN * g.RB / kLoadLatencyUs;
   if (bw > (float)cus * kCuBytesPerUs) bw = (float)cus * kCuBytesPerUs;
   if (bw > g.cap) bw = g.cap;
-  const float mem = (float)a.Nv * a.K * eb / bw;
+  float mem = (float)a.Nv * a.K * eb / bw;
+  // each tile also loads its BM activation rows (rows past M repeat the last one), and one
+  // CU loads both operands at a bounded rate: at few rows, 128-row tiles load twice the bytes
+  const float cu_load = (float)per_cu * (g.BM + g.BN) * ((float)a.K * eb / split) / kCuLoadBytesPerUs;
+  if (cu_load > mem) mem = cu_load;
   const float atom = split <= 1 ? 0.f
                      : part ? (float)a.M * a.Nv * 4.f * (split - 1) / kPartBytesPerUs
                             : (float)a.M * a.Nv * 4.f * split / kAtomicBytesPerUs;
