@@ -45,7 +45,7 @@ def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
 
 
 # ------------------------------------------------------------------ one layer, hidden rows in
-def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False):
+def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False, ws_rows=None):
     sl = _sl()
     case = W.layer_case(dm, N, Ms, key=key)
     B, M = case.B, case.M_tot
@@ -61,6 +61,8 @@ def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False):
                         k_cache=kc, v_cache=vc, with_h_out=True, minimal_workspace=minimal_ws)
     assert st.M_tot == M
     np.testing.assert_array_equal(st.act_idx[:M].cpu().numpy(), case.act_idx)
+    if ws_rows is not None:   # the workspace a first step with ws_rows active rows would have been given
+        st.ws = torch.empty(model.workspace_size(B, N, ws_rows, minimal_ws), dtype=torch.uint8, device="cuda")
     st.step(eps=0.0, do_lock=False, no_kv_cache=no_kv_cache)
     torch.cuda.synchronize()
     got_h = st.h_out[:M].cpu().numpy().astype(np.float64)
@@ -135,6 +137,14 @@ def test_layer_step_minimal_workspace(M):
     oracle."""
     say("layer step minimal workspace", M)
     _layer_case_run(W.LLADA_LAYER, 1024, [M], key=M + 3, tol=TOL["bf16"], minimal_ws=True)
+
+
+def test_layer_step_in_workspace_sized_for_more_rows():
+    """A step at M = 128 in exactly the workspace sized for 129 rows (a later, smaller step of the same
+    loop).  At 128 rows the attention splits its keys and stores per-split partials, so the step needs
+    more than 129 rows' own layout; the size covers every M up to the one it is asked for."""
+    say("layer step M=128 in the workspace for 129 rows")
+    _layer_case_run(W.LLADA_LAYER, 1024, [128], key=128 + 5, tol=TOL["bf16"], ws_rows=129)
 
 
 @pytest.mark.parametrize("M", [256, 64])
