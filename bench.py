@@ -548,7 +548,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the SureLock path here is built and measured on a single MI355X "
-              "(sequences are independent, so data parallelism needs no collective; see DESIGN.md). "
+              "(sequences are independent, so data parallelism needs no collective). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     res = gpu_part(args)

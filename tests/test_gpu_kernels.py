@@ -3,8 +3,8 @@
 sl_compact and the lock/compaction decisions of sl_kl_lock are integer work:
 bit-exact, except (for sl_kl_lock) positions whose oracle KL lies within 1e-3
 of eps (the tolerance band the lock rule allows) or whose oracle u lies within
-GATE_BAND of the oracle gate threshold (fp32 vs fp64 ordering of u values;
-derivation in DESIGN.md).  Floating-point outputs: KL within 1e-3 absolute;
+GATE_BAND of the oracle gate threshold (an fp32 u and the fp64 u can order
+near-equal values differently).  Floating-point outputs: KL within 1e-3 absolute;
 LSE, u, conf within the fp32 accumulation error of a V-term sum; attention
 outputs within bf16 / fp32 rounding.
 """

@@ -3,7 +3,7 @@
 Hidden rows and K/V (bf16 storage): relative L2 <= 1e-2 and no element beyond
 max(7 rms(d), 2e-2 max(1,|ref|)) -- the bf16 rounding of intermediates gives a
 near-Gaussian error whose maximum over millions of elements exceeds a fixed
-2e-2 at full width (see DESIGN.md); fp32 storage is held to 1e-4.  Logits: max-abs 2e-2.  KL: 1e-3
+2e-2 at full width; fp32 storage is held to 1e-4.  Logits: max-abs 2e-2.  KL: 1e-3
 absolute.  Lock masks and active lists: bit-exact except near-threshold
 positions (|KL-eps| <= 1e-3, or |u - q| <= 1e-5 when the gate is on).
 Locked positions' cache rows and posterior rows: bitwise unchanged.

@@ -372,7 +372,7 @@ def test_loop_invariants_with_locking():
 
 def test_layer_flops_model():
     od = O.OracleDims(4096, 32, 128, 12288, 126464, 1e-5, 1e4)
-    # SURVEY/BASELINE figure: M * 453.0 MFLOP per row at N = 1024
+    # 8 d^2 + 6 d F + 4 N d = 453.0 MFLOP per row at d = 4096, F = 12288, N = 1024
     assert abs(O.layer_flops(od, 1, 1024) / 1e6 - 453.0) < 0.1
 
 
