@@ -349,6 +349,7 @@ ATTN_CASES = [
     ("bf16", 128, 2, 256, [256, 37]),
     ("bf16", 128, 3, 1024, [5]),          # few query tiles: split over keys + merge
     ("bf16", 128, 32, 1024, [40]),        # split four ways (128 keys per key group)
+    ("bf16", 128, 32, 1024, [768]),       # 128-query workgroups: 64-query ones would not fit one wave
     ("bf16", 128, 32, 512, [9]),          # short sequence, few queries: four key groups, no split
     ("bf16", 128, 4, 256, [3, 60]),       # the same with two sequences
     ("bf16", 128, 2, 64, [7]),            # four key groups over two 32-key tiles: two groups idle

@@ -722,6 +722,8 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
 // most 128 keys) with no split and no merge pass.  Measured at 32 heads and
 // M <= 64: N = 512, 13.4-14.3 us against 16.6-17.9 us split four ways;
 // N = 1024, 15.2-17.1 us split four ways against 16.2-18.6 us split eight ways.
+// Shape 1 only when its workgroups fit in one wave of the chip: at 32 heads and
+// M = 768 its 384 workgroups take 37-39 us against 25-26 us for shape 0's 192.
 struct AttnPlan { int bq, shape, slots, nsplit, tps; };
 
 static AttnPlan attn_plan(int B, int N, int M_tot, int H, bool tr) {
@@ -729,7 +731,8 @@ static AttnPlan attn_plan(int B, int N, int M_tot, int H, bool tr) {
   const int tiles = N / kBKV;
   p.bq = kBQ;
   p.shape = 0;
-  if (tr && ((M_tot + kBQ - 1) / kBQ) * H < 256 && ((M_tot + 63) / 64) * H >= 64) { p.bq = 64; p.shape = 1; }
+  const int b64 = ((M_tot + 63) / 64) * H;   // 64-query workgroups
+  if (tr && ((M_tot + kBQ - 1) / kBQ) * H < 256 && b64 >= 64 && b64 <= 256) { p.bq = 64; p.shape = 1; }
   const int blocks = ((M_tot + p.bq - 1) / p.bq) * H;   // useful workgroups without a split
   p.nsplit = 1;
   if (blocks < 64) {
