@@ -3,10 +3,12 @@
 sl_compact and the lock/compaction decisions of sl_kl_lock are integer work:
 bit-exact, except (for sl_kl_lock) positions whose oracle KL lies within 1e-3
 of eps (the tolerance band the lock rule allows) or whose oracle u lies within
-GATE_BAND of the oracle gate threshold (an fp32 u and the fp64 u can order
-near-equal values differently).  Floating-point outputs: KL within 1e-3 absolute;
-LSE, u, conf within the fp32 accumulation error of a V-term sum; attention
-outputs within bf16 / fp32 rounding.
+GATE_BAND = 4e-6 of the oracle gate threshold (twice the asserted 2e-6 bound on
+the fp32 u: an fp32 u and the fp64 u can order values that close differently).
+Floating-point outputs: KL within 2e-5 (the benchmark spec's band is 1e-3); LSE, u,
+conf within the fp32 accumulation error of a V-term sum; bf16 GEMM outputs within
+half a bf16 ulp plus fp32 accumulation; bf16 attention outputs within the margin
+over the bf16-storage emulation (tests/bf16_emulation.py) of the same inputs.
 """
 import math
 
@@ -16,12 +18,10 @@ import torch
 
 import oracle.surelock_oracle as O
 import workloads as W
-from tests.gpu_util import dev, host64, say, tdtype
+from tests import bf16_emulation as E
+from tests.gpu_util import bf16_out_err, compare_lock, dev, host64, say, tdtype
 
 pytestmark = pytest.mark.gpu
-
-GATE_BAND = 1e-5
-KL_BAND = 1e-3
 
 
 def _sl():
@@ -104,41 +104,8 @@ def _oracle_kl(case, eps, gate_q, mask_id, have_prev):
 
 
 def _compare_kl(case, g, st, lr, eps, gate_q, have_prev):
-    M = case.M_tot
-    if M:
-        if have_prev:
-            assert np.max(np.abs(g["kl"][:M] - st.kl)) <= KL_BAND
-            assert np.max(np.abs(g["kl"][:M] - st.kl)) <= 2e-5   # what fp32 actually achieves here
-        else:
-            assert np.all(np.isinf(g["kl"][:M]))
-        np.testing.assert_allclose(g["lse"][:M], st.lse, rtol=2e-6, atol=2e-5)
-        np.testing.assert_allclose(g["u"][:M], st.u, rtol=0, atol=2e-6)
-        np.testing.assert_allclose(g["conf"][:M], st.conf, rtol=1e-5, atol=1e-7)
-        np.testing.assert_array_equal(g["argmax"][:M], st.argmax)   # exact: comparisons of exact inputs
-    if gate_q >= 0:
-        np.testing.assert_allclose(g["gate_thr"], lr.gate_thr, rtol=0, atol=2e-6)
-    # lock mask: exact except near-threshold positions
-    diff = np.flatnonzero(g["locked"] != lr.locked)
-    if len(diff):
-        rows_seq = O.seq_of_rows(case.act_off)
-        glob = rows_seq * case.N + case.act_idx.astype(np.int64)
-        row_of = {int(gp): i for i, gp in enumerate(glob)}
-        for gp in diff:
-            i = row_of.get(int(gp))
-            assert i is not None, "a position outside A_t changed its lock state"
-            near_kl = abs(st.kl[i] - eps) <= KL_BAND
-            near_gate = gate_q >= 0 and abs(st.u[i] - lr.gate_thr[rows_seq[i]]) <= GATE_BAND
-            assert near_kl or near_gate, "lock mismatch at %d (kl %.6g u %.9g thr %.9g)" % (
-                gp, st.kl[i], st.u[i], lr.gate_thr[rows_seq[i]])
-    assert np.all(g["locked"] >= case.locked)                          # monotone
-    # compaction of the GPU's own mask (property), and equality with the oracle when masks agree
-    ri, ro = O.active_set(g["locked"], case.B, case.N)
-    assert g["M"] == int(ro[-1])
-    np.testing.assert_array_equal(g["act_off"], ro)
-    np.testing.assert_array_equal(g["act_idx"][:g["M"]], ri)
-    if len(diff) == 0:
-        np.testing.assert_array_equal(g["act_idx"][:g["M"]], lr.act_idx)
-    return len(diff)
+    return compare_lock(g, st, lr, case.locked, case.act_idx, case.act_off, case.B, case.N, eps, gate_q,
+                        have_prev)
 
 
 KL_CASES = [
@@ -190,6 +157,7 @@ def test_kl_lock_full_size():
     nd = _compare_kl(case, g, st, lr, 0.01, 0.5, True)
     say("full-size KL-lock: new locks gpu %d oracle %d, exempt mismatches %d" % (
         int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
+    assert nd == 0
 
 
 @pytest.mark.slow
@@ -205,6 +173,7 @@ def test_kl_lock_batched_full_size():
     nd = _compare_kl(case, g, st, lr, 0.05, 0.5, True)
     say("batched KL-lock: M=%d, new locks gpu %d oracle %d, exempt mismatches %d" % (
         case.M_tot, int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
+    assert nd == 0
 
 
 # ------------------------------------------------------------------ LM head at full vocabulary
@@ -257,12 +226,6 @@ ALL_TILES = {(256, 256, 0), (256, 128, 0), (128, 256, 0), (128, 128, 0), (128, 6
              (64, 128, 0), (64, 64, 0), (64, 128, 1), (128, 96, 0), (128, 192, 0)}
 
 
-def bf16_out_err(got, ref):
-    """Largest excess of |got - ref| over the bound for a bf16-stored product: 2e-2 absolute, or,
-    where larger, half a bf16 ulp (2^-8 relative) plus 2e-3 of float32 accumulation over K."""
-    return float(np.max(np.abs(got - ref) - np.maximum(2e-2, 2.0 ** -8 * np.abs(ref) + 2e-3)))
-
-
 def tile_of(sl, epi, M, K, n):
     bm, bn, _, vb = sl.sl_gemm_plan(torch.bfloat16, epi, M, K, n, with_path=True)
     return bm, bn, vb
@@ -293,8 +256,19 @@ def test_gemm_parity(kind, M, K, n_out):
         sl.sl_gemm(sl.SL_EPI_SWIGLU, dev(A, "bf16"), M, K, n_out, dev(w0, "bf16"), dev(w1, "bf16"), out0=out)
         ref = O.silu(A64 @ O.widen(w0, "bf16").T) * (A64 @ O.widen(w1, "bf16").T)
         got = host64(out)
-        assert np.max(np.abs(got - ref) / (1e-2 + np.abs(ref))) <= 1.0, "swiglu mismatch"
-        assert np.max(np.abs(got - ref)) <= 2e-2
+        # half a bf16 ulp of the stored product, plus the fp32 accumulation of g = a.w_g and u = a.w_u
+        # over K (|dg| <= K 2^-24 sum_k |a_k w_k|, likewise du) carried through SiLU(g) u:
+        # |d(SiLU(g) u)| <= max|SiLU'| |u| |dg| + |SiLU(g)| |du|, with max|SiLU'| < 1.1; 2e-6 relative
+        # covers the fp32 evaluation of SiLU (exp and reciprocal) and of the product
+        wg64, wu64 = O.widen(w0, "bf16"), O.widen(w1, "bf16")
+        gg, uu = A64 @ wg64.T, A64 @ wu64.T
+        dg = K * 2.0 ** -24 * (np.abs(A64) @ np.abs(wg64).T)
+        du = K * 2.0 ** -24 * (np.abs(A64) @ np.abs(wu64).T)
+        acc = 1.1 * np.abs(uu) * dg + np.abs(O.silu(gg)) * du
+        bound = (2.0 ** -8 + 2e-6) * np.abs(ref) + (1 + 2.0 ** -8) * acc
+        excess = np.abs(got - ref) - bound
+        say("swiglu max |d| %.3e, max excess over the bound %.3e" % (np.abs(got - ref).max(), excess.max()))
+        assert excess.max() <= 0, "swiglu mismatch"
         return
     if kind == "resid":
         w0 = W.to_storage(W.normal(g, (n_out, K), 0.02), "bf16")
@@ -365,6 +339,23 @@ ATTN_CASES = [
 ]
 
 
+def _check_attention(got, q64, K64, V64, off, keys, Dh, dtype):
+    """Per sequence against the float64 oracle over the attended keys (all N, or `keys`).  fp32:
+    2e-5 absolute.  bf16: relative L2 and max |d| within the margin over the bf16-storage emulation
+    (P rounded before P.V, output rounded) of the same inputs."""
+    for b in range(len(off) - 1):
+        s_ = slice(off[b], off[b + 1])
+        Kb, Vb = (K64[b], V64[b]) if keys[b] is None else (K64[b][keys[b]], V64[b][keys[b]])
+        ref = O.attention(q64[s_], Kb, Vb, 1.0 / math.sqrt(Dh))
+        if dtype == "f32":
+            np.testing.assert_allclose(got[s_], ref, atol=2e-5, rtol=0)
+            continue
+        emu = E.err_stats(E.attention(q64[s_], Kb, Vb, 1.0 / math.sqrt(Dh)), ref)
+        g = E.check(got[s_], ref, emu, "attention, sequence %d" % b)
+        say("attention seq %d: rel L2 %.3e (emulated %.3e), max %.3e (emulated %.3e)" % (
+            b, g.rel_l2, emu.rel_l2, g.max, emu.max))
+
+
 @pytest.mark.parametrize("dtype,Dh,H,N,Ms", ATTN_CASES)
 def test_attention_parity(dtype, Dh, H, N, Ms):
     sl = _sl()
@@ -383,10 +374,7 @@ def test_attention_parity(dtype, Dh, H, N, Ms):
                       H, Dh, 1.0 / math.sqrt(Dh), out, ws)
     got = host64(out).reshape(M_tot, H, Dh)
     q64, K64, V64 = O.widen(q, dtype), O.widen(Kc, dtype), O.widen(Vc, dtype)
-    tol = 2e-2 if dtype == "bf16" else 2e-5
-    for b in range(B):
-        ref = O.attention(q64[off[b]:off[b + 1]], K64[b], V64[b], 1.0 / math.sqrt(Dh))
-        np.testing.assert_allclose(got[off[b]:off[b + 1]], ref, atol=tol, rtol=0)
+    _check_attention(got, q64, K64, V64, off, [None] * B, Dh, dtype)
 
 
 # The no-KV-cache ablation: every query attends over its sequence's active positions only
@@ -439,10 +427,7 @@ def test_attention_excluded_keys_parity(dtype, Dh, H, N, Ms, pattern):
     got = host64(out).reshape(M_tot, H, Dh)
     assert np.isfinite(got).all()
     q64, K64, V64 = O.widen(q, dtype), O.widen(Kc, dtype), O.widen(Vc, dtype)
-    tol = 2e-2 if dtype == "bf16" else 2e-5
-    for b in range(B):
-        ref = O.attention(q64[off[b]:off[b + 1]], K64[b][acts[b]], V64[b][acts[b]], 1.0 / math.sqrt(Dh))
-        np.testing.assert_allclose(got[off[b]:off[b + 1]], ref, atol=tol, rtol=0)
+    _check_attention(got, q64, K64, V64, off, acts, Dh, dtype)
 
 
 # ------------------------------------------------------------------ cache scatter

@@ -1,14 +1,23 @@
 """GPU parity of sl_step (whole SureLock iterations) against the CPU oracle.
 
-Hidden rows and K/V (bf16 storage): relative L2 <= 1e-2 and no element beyond
-max(7 rms(d), 2e-2 max(1,|ref|)) -- the bf16 rounding of intermediates gives a
-near-Gaussian error whose maximum over millions of elements exceeds a fixed
-2e-2 at full width; fp32 storage is held to 1e-4.  Logits: max-abs 2e-2.  KL: 1e-3
-absolute.  Lock masks and active lists: bit-exact except near-threshold
-positions (|KL-eps| <= 1e-3, or |u - q| <= 1e-5 when the gate is on).
-Locked positions' cache rows and posterior rows: bitwise unchanged.
-Multi-step loops are checked teacher-forced: every GPU step starts from the
-oracle's state (rounded to the storage type).
+Floating point, bf16 storage: hidden rows, fresh K/V and the logits of deep
+models deviate from the float64 oracle by the rounding of the intermediates the
+kernels store in bf16.  tests/bf16_emulation.py computes that deviation for the
+same inputs on the CPU; the GPU's relative L2 and max |d| must stay within a
+1.25 margin of it.  Logits that come straight from the LM head (a small model's,
+or the product of the GPU's own final hidden rows) are held to max-abs 2e-2, or
+half a bf16 ulp where that is larger.  fp32 storage: 1e-4.  KL: 1e-3 absolute
+against the oracle's logits, and 2e-5 against the oracle's statistics of the
+GPU's own logits.
+
+Integer work: the lock mask, the next active list and the sampler's picks are
+compared with the oracle's gate / lock / compaction / sampler run on identical
+inputs (the GPU's own stored logits and the same previous posterior), bit-exact
+except positions whose oracle KL lies within 1e-3 of eps, or whose u lies within
+4e-6 of the gate threshold (twice the asserted fp32 error of u).  Locked
+positions' cache rows and posterior rows: bitwise unchanged.  Multi-step loops
+are checked teacher-forced (every GPU step starts from the oracle's state,
+rounded to the storage type) and free-running (first divergence reported).
 """
 import math
 
@@ -18,11 +27,11 @@ import torch
 
 import oracle.surelock_oracle as O
 import workloads as W
-from tests.gpu_util import check_hidden, check_rel, dev, host64, round_storage, say, tdtype
+from tests import bf16_emulation as E
+from tests.gpu_util import (GATE_BAND, KL_BAND, bf16_out_err, check_rel, compare_lock, dev, host64, round_storage,
+                            say, tdtype)
 
 pytestmark = pytest.mark.gpu
-
-KL_BAND, GATE_BAND = 1e-3, 1e-5
 
 
 def _sl():
@@ -32,6 +41,10 @@ def _sl():
 
 def _odims(dm):
     return O.OracleDims(dm.d, dm.n_heads, dm.head_dim, dm.ffn, dm.vocab, dm.rms_eps, dm.rope_theta)
+
+
+def _edims(dm):
+    return E.Dims(dm.d, dm.n_heads, dm.head_dim, dm.ffn, dm.rms_eps, dm.rope_theta)
 
 
 def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
@@ -45,6 +58,11 @@ def _dev_model(dm, layers_np, embed=None, head=None, rope_n=None):
 
 
 # ------------------------------------------------------------------ one layer, hidden rows in
+def ostate_glob(case, N):
+    """Rows b*N + pos of the active positions of a layer case, in compact order."""
+    return O.seq_of_rows(case.act_off) * N + case.act_idx.astype(np.int64)
+
+
 def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False, ws_rows=None):
     sl = _sl()
     case = W.layer_case(dm, N, Ms, key=key)
@@ -72,22 +90,30 @@ def _layer_case_run(dm, N, Ms, key, tol, no_kv_cache=False, minimal_ws=False, ws
     h_in = O.widen(case.h_in, dm.dtype)
     K64 = O.widen(case.k_cache, dm.dtype)
     V64 = O.widen(case.v_cache, dm.dtype)
+    ek, ev = [K64.copy()], [V64.copy()]      # the emulation's caches (the oracle updates K64, V64)
     ostate = O.OracleState(B=B, N=N, t=0, locked=locked, kc=[K64], vc=[V64], h_in=h_in)
     om = O.OracleModel(od, 1, lambda l: W64)
     out = O.step(om, ostate, 0.0, -1.0, do_lock=False, attend_locked=not no_kv_cache)
-    if dm.dtype == "bf16":
-        l2, rms, mx = check_hidden(got_h, out.h, tol[0], "hidden rows")
-        say("hidden rows: rel L2 %.3e rms %.3e max %.3e" % (l2, rms, mx))
-    else:
-        check_rel(got_h, out.h, tol[0], tol[1], "hidden rows")
     gk = host64(kc).reshape(B * N, -1)
     gv = host64(vc).reshape(B * N, -1)
     rk = ostate.kc[0].reshape(B * N, -1)
     rv = ostate.vc[0].reshape(B * N, -1)
     act_g = np.flatnonzero(locked == 0)
-    chk = (lambda a, b, w: check_hidden(a, b, tol[0], w)) if dm.dtype == "bf16" else (lambda a, b, w: check_rel(a, b, tol[0], tol[1], w))
-    chk(gk[act_g], rk[act_g], "fresh K rows")
-    chk(gv[act_g], rv[act_g], "fresh V rows")
+    if dm.dtype == "bf16":
+        # the same step with bf16 rounding where the kernels store bf16
+        eh = E.step_rows(h_in[ostate_glob(case, N)], case.act_idx, case.act_off, lambda l: W64, 1, ek, ev,
+                         _edims(dm), attend_locked=not no_kv_cache)
+        for what, got, ref, emu in (("hidden rows", got_h, out.h, eh),
+                                    ("fresh K rows", gk[act_g], rk[act_g], ek[0].reshape(B * N, -1)[act_g]),
+                                    ("fresh V rows", gv[act_g], rv[act_g], ev[0].reshape(B * N, -1)[act_g])):
+            es = E.err_stats(emu, ref)
+            g = E.check(got, ref, es, what)
+            say("%s: rel L2 %.3e (emulated %.3e) rms %.3e max %.3e (emulated %.3e)" % (
+                what, g.rel_l2, es.rel_l2, g.rms, g.max, es.max))
+    else:
+        check_rel(got_h, out.h, tol[0], tol[1], "hidden rows")
+        check_rel(gk[act_g], rk[act_g], tol[0], tol[1], "fresh K rows")
+        check_rel(gv[act_g], rv[act_g], tol[0], tol[1], "fresh V rows")
     lk = np.flatnonzero(locked != 0)
     assert torch.equal(kc.reshape(B * N, -1)[torch.from_numpy(lk).cuda()], kc0.reshape(B * N, -1)[torch.from_numpy(lk).cuda()])
     assert torch.equal(vc.reshape(B * N, -1)[torch.from_numpy(lk).cuda()], vc0.reshape(B * N, -1)[torch.from_numpy(lk).cuda()])
@@ -194,66 +220,161 @@ def _llada8b_weights():
     return _LLADA8B["w"]
 
 
-@pytest.mark.slow
-def test_full_model_step_32_layers():
-    """One step (t = 0, all 512 positions active) of the 32-layer LLaDA-8B-shaped model: embedding of
-    128 prompt ids + 384 [MASK], 32 layers, LM head over V = 126464, sampler unmasking 3 positions.
+def _deep_logits_check(gz, z, ez, what):
+    """GPU logits after many bf16 layers against the oracle's, within the margin over the emulated
+    error of the same step.  Returns the max-abs bound."""
+    es = E.err_stats(ez, z)
+    g = E.check(gz, z, es, what)
+    say("%s: rel L2 %.3e (emulated %.3e) rms %.3e (emulated %.3e) max %.3e (emulated %.3e)" % (
+        what, g.rel_l2, es.rel_l2, g.rms, es.rms, g.max, es.max))
+    return E.bounds(es)[1]
 
-    After 32 layers the bf16 storage of the intermediates leaves a logits error of relative L2
-    1.20e-2 (rms 0.0154, max 0.095): a CPU emulation that rounds exactly where the kernels store
-    bf16 gives those figures against the float64 oracle.  The test holds the GPU to relative L2
-    <= 1.5e-2 with no element beyond 7 rms; argmax and sampler choices may differ only at near-ties
-    within that error."""
+
+def _argmax_check(gz, z, mask_id, zbound, what):
+    """argmax over ids other than [MASK]: a mismatch only where the oracle's top two are within
+    twice the logits bound (each of the two may move by that much)."""
+    keep = np.ones(z.shape[1], bool)
+    keep[mask_id] = False
+    zk, gk = z[:, keep], gz[:, keep]
+    ia, ga = np.argmax(zk, 1), np.argmax(gk, 1)
+    top2 = np.sort(zk, 1)[:, -2:]
+    say("%s argmax agreement %.4f" % (what, float(np.mean(ia == ga))))
+    for i in np.flatnonzero(ia != ga):
+        assert top2[i, 1] - top2[i, 0] <= 2 * zbound, "argmax mismatch at %d with margin %.3g" % (
+            i, top2[i, 1] - top2[i, 0])
+
+
+def _head_from_own_hidden_check(gz, h_gpu, head64, eps, what):
+    """The LM head alone: the GPU's logits against the float64 product of the GPU's own final hidden
+    rows (normalised and rounded to bf16 as the kernels store them), max-abs 2e-2 or half a bf16 ulp
+    where that is larger."""
+    zr = E.round_bf16(O.rmsnorm(h_gpu, eps)) @ head64.T
+    err = bf16_out_err(gz, zr)
+    say("%s: LM head from the GPU's own hidden rows, max |d| %.3e" % (what, float(np.abs(gz - zr).max())))
+    assert err <= 0
+
+
+def _sampler_check(gtok, tok0, cand0, act, off, N, stg, mask_id, k):
+    """The GPU's picks equal the oracle sampler's on identical statistics (the oracle's statistics of
+    the GPU's own logits), except where a confidence ties the k-th largest within fp32 error."""
+    picked = O.sampler_unmask(tok0.copy(), cand0.copy(), act, off, N, stg.argmax, stg.conf, mask_id, k)
+    gpu_picked = np.flatnonzero(gtok != tok0)
+    assert len(gpu_picked) == len(picked) and np.all(tok0[gpu_picked] == mask_id)
+    rowof = {int(p) + 0: i for i, p in enumerate(O.seq_of_rows(off) * N + act.astype(np.int64))}
+    masked = [rowof[int(p)] for p in np.flatnonzero(tok0 == mask_id) if int(p) in rowof]
+    kth = np.sort(stg.conf[masked])[-k]
+    for gp in set(picked) ^ set(gpu_picked.tolist()):
+        assert abs(stg.conf[rowof[gp]] - kth) <= 1e-5 * kth, "sampler pick %d is not a near-tie" % gp
+    for gp in gpu_picked:
+        assert gtok[gp] == stg.argmax[rowof[int(gp)]]
+
+
+def _oracle_llada(layers, emb, head):
+    dm = W.LLADA_8B
+    return O.OracleModel(_odims(dm), dm.n_layers, lambda l: {k: O.widen(v, dm.dtype) for k, v in layers[l].items()},
+                         O.widen(emb, dm.dtype), O.widen(head, dm.dtype))
+
+
+def _emulated_logits(layers, h_rows, act, off, kc, vc, head64):
+    dm = W.LLADA_8B
+    hh = E.step_rows(h_rows, act, off, lambda l: {k: O.widen(v, dm.dtype) for k, v in layers[l].items()},
+                     dm.n_layers, kc, vc, _edims(dm))
+    return E.logits(hh, head64, dm.rms_eps, f32=True)
+
+
+@pytest.mark.slow
+def test_full_model_steps_t0_t1_32_layers():
+    """Steps t = 0 and t = 1 of the 32-layer LLaDA-8B-shaped model: embedding of 128 prompt ids +
+    384 [MASK], 32 layers, LM head over V = 126464, eps = 0.05 with the gate off, sampler unmasking 3
+    positions.  t = 1 is the first step at which a position can lock; it is teacher-forced from the
+    oracle's state after t = 0 (tokens, candidates and the posterior rounded to bf16).
+
+    Logits: within 1.25x the error of the bf16-storage emulation of the t = 0 step (after 32 layers
+    the roundings compound to a relative L2 near 1.2e-2; the t = 1 step differs from it in three
+    tokens only); the LM head alone within max-abs 2e-2 of the product of the GPU's own final hidden
+    rows.  KL within 1e-3 of the oracle's.  Gate, lock, compaction and sampler against the oracle's
+    rules on the GPU's own logits."""
     sl = _sl()
     dm = W.LLADA_8B
-    B, N, n_prompt, k_unmask = 1, 512, 128, 3
+    B, N, n_prompt, k_unmask, eps = 1, 512, 128, 3, 0.05
     layers, emb, head = _llada8b_weights()
+    head64 = O.widen(head, dm.dtype)
     tok0 = W.prompt_tokens(dm, B, N, n_prompt)
     cand0 = (tok0 != dm.mask_id).astype(np.uint8)
     model = _dev_model(dm, layers, emb, head, rope_n=N)
     st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
-                        cand=torch.from_numpy(cand0.copy()).cuda())
-    st.step(0.05, -1.0, dm.mask_id, True, k_unmask)
+                        cand=torch.from_numpy(cand0.copy()).cuda(), with_h_out=True)
+    st.step(eps, -1.0, dm.mask_id, True, k_unmask)
     torch.cuda.synchronize()
     gz = host64(st.logits[0])[:N]
+    gh = st.h_out[:N].cpu().numpy().astype(np.float64)
     gtok = st.tok.cpu().numpy()
     assert st.M_tot == N and int(st.locked.sum()) == 0            # t = 0: no previous posterior, no lock
-    say("32-layer step: oracle")
-    od = _odims(dm)
-    om = O.OracleModel(od, dm.n_layers, lambda l: {k: O.widen(v, dm.dtype) for k, v in layers[l].items()},
-                       O.widen(emb, dm.dtype), O.widen(head, dm.dtype))
+    act, off = np.arange(N, dtype=np.int32), np.array([0, N], np.int32)
+    say("32-layer step t=0: oracle")
+    om = _oracle_llada(layers, emb, head)
     ost = O.OracleState(B=B, N=N, t=0, locked=np.zeros(B * N, np.uint8),
                         kc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
                         vc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
                         tok=tok0.copy(), cand=cand0.copy())
-    out = O.step(om, ost, 0.05, -1.0, True, dm.mask_id)
-    z = out.logits
-    d = gz - z
-    rms = float(np.sqrt(np.mean(d * d)))
-    rel = float(np.linalg.norm(d) / np.linalg.norm(z))
-    say("32-layer logits: rel L2 %.3e rms %.3e max %.3e" % (rel, rms, np.abs(d).max()))
-    assert rel <= 1.5e-2
-    assert np.abs(d).max() <= max(7 * rms, 2e-2)
-    # argmax over ids other than [MASK]: a mismatch only where the oracle's top two are within the error
-    keep = np.ones(dm.vocab, bool)
-    keep[dm.mask_id] = False
-    zk, gk = z[:, keep], gz[:, keep]
-    ia, ga = np.argmax(zk, 1), np.argmax(gk, 1)
-    top2 = np.sort(zk, 1)[:, -2:]
-    for i in np.flatnonzero(ia != ga):
-        assert top2[i, 1] - top2[i, 0] <= 2 * 7 * rms, "argmax mismatch at %d with margin %.3g" % (i, top2[i, 1] - top2[i, 0])
-    # sampler: the k most confident [MASK] positions; differing picks only at near-ties of confidence
-    picked = O.sampler_unmask(ost.tok, ost.cand, out.act_idx, out.act_off, N, out.stats.argmax, out.stats.conf,
-                              dm.mask_id, k_unmask)
-    gpu_picked = np.flatnonzero(gtok != tok0)
-    assert len(gpu_picked) == k_unmask
-    conf = out.stats.conf
-    kth = np.sort(conf[tok0 == dm.mask_id])[-k_unmask]
-    for gp in set(picked) ^ set(gpu_picked.tolist()):
-        assert abs(conf[gp] - kth) <= 0.1 * kth, "sampler pick %d not a near-tie" % gp
-    for gp in set(picked) & set(gpu_picked.tolist()):
-        i = int(gp)
-        assert gtok[gp] == ost.tok[gp] or top2[i, 1] - top2[i, 0] <= 2 * 7 * rms
+    out0 = O.step(om, ost, eps, -1.0, True, dm.mask_id)
+    z0 = out0.logits
+    say("32-layer step t=0: bf16-storage emulation")
+    ez = _emulated_logits(layers, om.embed[tok0], act, off,
+                          [np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
+                          [np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)], head64)
+    zb = _deep_logits_check(gz, z0, ez, "t=0 logits")
+    es0 = E.err_stats(ez, z0)
+    del ez
+    _argmax_check(gz, z0, dm.mask_id, zb, "t=0")
+    _head_from_own_hidden_check(gz, gh, head64, dm.rms_eps, "t=0")
+    stg0 = O.posterior_stats(gz, None, dm.mask_id)
+    compare_lock(dict(kl=st.kl.cpu().numpy(), u=st.u.cpu().numpy(), lse=st.lse.cpu().numpy(),
+                      conf=st.conf.cpu().numpy(), argmax=st.argmax.cpu().numpy(), locked=st.locked.cpu().numpy(),
+                      act_idx=st.act_idx.cpu().numpy(), act_off=st.act_off.cpu().numpy(), M=st.M_tot),
+                 stg0, O.lock_update(np.zeros(N, np.uint8), act, off, B, N, stg0.kl, stg0.u, cand0, eps, -1.0, False),
+                 np.zeros(N, np.uint8), act, off, B, N, eps, -1.0, False)
+    _sampler_check(gtok, tok0, cand0, act, off, N, stg0, dm.mask_id, k_unmask)
+    # oracle sampler after t = 0 -> the teacher-forced state of t = 1
+    O.sampler_unmask(ost.tok, ost.cand, out0.act_idx, out0.act_off, N, out0.stats.argmax, out0.stats.conf,
+                     dm.mask_id, k_unmask)
+    tok1, cand1 = ost.tok.copy(), ost.cand.copy()
+    prev_st = W.to_storage(z0.astype(np.float32), "bf16")
+    prev64 = O.widen(prev_st, "bf16")
+    say("32-layer step t=1: oracle")
+    ost.t = 1
+    out1 = O.step(om, ost, eps, -1.0, True, dm.mask_id, prev_logits=prev64)
+    z1 = out1.logits
+    say("32-layer step t=1: GPU, teacher-forced; oracle locks %d" % int(out1.lock.new_lock.sum()))
+    st.tok.copy_(torch.from_numpy(tok1).cuda())
+    st.cand.copy_(torch.from_numpy(cand1).cuda())
+    st.locked.zero_()
+    st.M_tot = sl.sl_compact(st.locked, B, N, st.act_idx, st.act_off, st.m_host)
+    st.logits[0].copy_(dev(prev_st, "bf16"))
+    st.t = 1
+    st.step(eps, -1.0, dm.mask_id, True, k_unmask)
+    torch.cuda.synchronize()
+    gz1 = host64(st.logits[1])[:N]
+    gh1 = st.h_out[:N].cpu().numpy().astype(np.float64)
+    g1 = E.check(gz1, z1, es0, "t=1 logits")
+    say("t=1 logits: rel L2 %.3e rms %.3e max %.3e (bound from the t=0 emulation)" % (g1.rel_l2, g1.rms, g1.max))
+    _argmax_check(gz1, z1, dm.mask_id, zb, "t=1")
+    _head_from_own_hidden_check(gz1, gh1, head64, dm.rms_eps, "t=1")
+    kl1 = st.kl[:N].cpu().numpy()
+    assert np.max(np.abs(kl1 - out1.stats.kl)) <= KL_BAND
+    say("t=1 KL: max |d| against the oracle %.3e" % float(np.max(np.abs(kl1 - out1.stats.kl))))
+    # gate (off), lock and compaction on identical inputs: the GPU's logits, the same previous posterior
+    stg1 = O.posterior_stats(gz1, prev64, dm.mask_id)
+    lr1 = O.lock_update(np.zeros(N, np.uint8), act, off, B, N, stg1.kl, stg1.u, cand1, eps, -1.0, True)
+    g_locked = st.locked.cpu().numpy()
+    nd = compare_lock(dict(kl=kl1, u=st.u[:N].cpu().numpy(), lse=st.lse[:N].cpu().numpy(),
+                           conf=st.conf[:N].cpu().numpy(), argmax=st.argmax[:N].cpu().numpy(), locked=g_locked,
+                           act_idx=st.act_idx.cpu().numpy(), act_off=st.act_off.cpu().numpy(), M=st.M_tot),
+                      stg1, lr1, np.zeros(N, np.uint8), act, off, B, N, eps, -1.0, True)
+    say("t=1 locks: gpu %d, oracle on the GPU's logits %d, oracle on its own logits %d; exempt differences %d" % (
+        int(g_locked.sum()), int(lr1.new_lock.sum()), int(out1.lock.new_lock.sum()), nd))
+    assert int(g_locked.sum()) > 0                 # the first step that can lock does lock
+    _sampler_check(st.tok.cpu().numpy(), tok1, cand1, act, off, N, stg1, dm.mask_id, k_unmask)
 
 
 @pytest.mark.slow
@@ -264,18 +385,16 @@ def test_full_model_late_step_32_layers():
     previous posterior equal to the oracle's logits of this step plus N(0, 0.05^2) drift; eps = 0.05,
     gate at the median, 3 unmasks.
 
-    Attending to random unit-variance caches grows the residual stream faster than at t = 0 (hidden
-    rms 13.4 after layer 31 against the oracle), and the bf16 roundings compound with it: a CPU
-    emulation that rounds to bf16 exactly where the kernels store bf16 gives logits relative L2
-    2.23e-2, rms 0.0286, max 0.181 (6.3 rms) on this state.  The test holds the GPU to relative L2
-    <= 2.8e-2 (the t = 0 test's 1.25x margin over its emulation) with no element beyond 7 rms; an
-    argmax may differ only at a top-two margin within 2 * 7 rms.  KL within 1e-3; gate, lock,
-    compaction and sampler exact against the GPU's own statistics, and against the oracle except where
-    the measured u error or a confidence near-tie can move a decision."""
+    Attending to random unit-variance caches grows the residual stream faster than at t = 0, and the
+    bf16 roundings compound with it: the logits are held to 1.25x the bf16-storage emulation of this
+    very step (relative L2 near 2.2e-2); the LM head alone to max-abs 2e-2 against the product of the
+    GPU's own final hidden rows.  KL within 1e-3 of the oracle's.  Gate, lock, compaction and sampler
+    against the oracle's rules on the GPU's own logits and the same previous posterior."""
     sl = _sl()
     dm = W.LLADA_8B
     B, N, t, eps, gate, k_unmask = 1, 512, 40, 0.05, 0.5, 3
     layers, emb, head = _llada8b_weights()
+    head64 = O.widen(head, dm.dtype)
     g = W.rng(W.SEED_SETS, 7777)
     tok0 = W.prompt_tokens(dm, B, N, 128)
     done = 128 + g.permutation(N - 128)[:200]
@@ -286,22 +405,26 @@ def test_full_model_late_step_32_layers():
     cand0 = (tok0 != dm.mask_id).astype(np.uint8)
     act = np.flatnonzero(locked == 0).astype(np.int32)
     M = len(act)
+    off = np.array([0, M], np.int32)
     kc_st = [W.to_storage(W.normal(W.rng(W.SEED_CACHE, 7777, l, 0), (B, N, dm.n_heads, dm.head_dim), 1.0), "bf16")
              for l in range(dm.n_layers)]
     vc_st = [W.to_storage(W.normal(W.rng(W.SEED_CACHE, 7777, l, 1), (B, N, dm.n_heads, dm.head_dim), 1.0), "bf16")
              for l in range(dm.n_layers)]
-    # oracle: this step's logits (the layers and LM head over the active rows), then the statistics
+    # oracle: this step's logits (the layers and LM head over the active rows)
     say("32-layer late step: oracle, M = %d" % M)
-    od = _odims(dm)
-    om = O.OracleModel(od, dm.n_layers, lambda l: {k: O.widen(v, dm.dtype) for k, v in layers[l].items()},
-                       O.widen(emb, dm.dtype), O.widen(head, dm.dtype))
+    om = _oracle_llada(layers, emb, head)
     ost = O.OracleState(B=B, N=N, t=0, locked=locked.copy(), kc=[O.widen(k, "bf16") for k in kc_st],
                         vc=[O.widen(v, "bf16") for v in vc_st], tok=tok0.copy(), cand=cand0.copy())
     z = O.step(om, ost, 0.0, -1.0, do_lock=False, mask_id=dm.mask_id).logits
+    del ost
     prev_st = W.to_storage(z.astype(np.float32) + W.normal(W.rng(W.SEED_DRIFT, 7777), z.shape, 0.05), "bf16")
-    ref = O.posterior_stats(z, O.widen(prev_st, "bf16"), dm.mask_id)
-    off = np.array([0, M], np.int32)
-    lr = O.lock_update(locked, act, off, B, N, ref.kl, ref.u, cand0, eps, gate, True)
+    prev64 = O.widen(prev_st, "bf16")
+    ref = O.posterior_stats(z, prev64, dm.mask_id)
+    say("32-layer late step: bf16-storage emulation")
+    ez = _emulated_logits(layers, om.embed[tok0[act]], act, off, [O.widen(k, "bf16") for k in kc_st],
+                          [O.widen(v, "bf16") for v in vc_st], head64)
+    es = E.err_stats(ez, z)
+    del ez
     # GPU: the same state at step t
     say("32-layer late step: GPU")
     model = _dev_model(dm, layers, emb, head, rope_n=N)
@@ -310,7 +433,7 @@ def test_full_model_late_step_32_layers():
     lk = torch.from_numpy(np.flatnonzero(locked)).cuda()
     kc_lock0, vc_lock0 = kc[:, 0, lk].clone(), vc[:, 0, lk].clone()
     st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(), cand=torch.from_numpy(cand0.copy()).cuda(),
-                        locked=torch.from_numpy(locked.copy()).cuda(), k_cache=kc, v_cache=vc)
+                        locked=torch.from_numpy(locked.copy()).cuda(), k_cache=kc, v_cache=vc, with_h_out=True)
     assert st.M_tot == M
     gi = torch.from_numpy(act.astype(np.int64)).cuda()
     st.logits[(t + 1) & 1].index_copy_(0, gi, dev(prev_st, "bf16"))
@@ -318,58 +441,29 @@ def test_full_model_late_step_32_layers():
     st.step(eps, gate, dm.mask_id, True, k_unmask)
     torch.cuda.synchronize()
     gz = host64(st.logits[t & 1].index_select(0, gi))
-    d = gz - z
-    rms = float(np.sqrt(np.mean(d * d)))
-    rel = float(np.linalg.norm(d) / np.linalg.norm(z))
-    say("32-layer late-step logits: rel L2 %.3e rms %.3e max %.3e" % (rel, rms, np.abs(d).max()))
-    assert rel <= 2.8e-2
-    assert np.abs(d).max() <= max(7 * rms, 2e-2)
-    keep = np.ones(dm.vocab, bool)
-    keep[dm.mask_id] = False
-    zk, gk = z[:, keep], gz[:, keep]
-    ia, ga = np.argmax(zk, 1), np.argmax(gk, 1)
-    top2 = np.sort(zk, 1)[:, -2:]
-    say("late-step argmax agreement %.4f" % float(np.mean(ia == ga)))
-    for i in np.flatnonzero(ia != ga):
-        assert top2[i, 1] - top2[i, 0] <= 2 * 7 * rms, "argmax mismatch at %d with margin %.3g" % (i, top2[i, 1] - top2[i, 0])
-    del zk, gk
+    gh = st.h_out[:M].cpu().numpy().astype(np.float64)
+    gv = E.check(gz, z, es, "late-step logits")
+    say("late-step logits: rel L2 %.3e (emulated %.3e) rms %.3e max %.3e (emulated %.3e)" % (
+        gv.rel_l2, es.rel_l2, gv.rms, gv.max, es.max))
+    _argmax_check(gz, z, dm.mask_id, E.bounds(es)[1], "late step")
+    _head_from_own_hidden_check(gz, gh, head64, dm.rms_eps, "late step")
     # locked rows' caches untouched in every layer
     assert torch.equal(kc[:, 0, lk], kc_lock0) and torch.equal(vc[:, 0, lk], vc_lock0)
-    kl, u = st.kl[:M].cpu().numpy(), st.u[:M].cpu().numpy()
+    kl = st.kl[:M].cpu().numpy()
     assert np.max(np.abs(kl - ref.kl)) <= KL_BAND
-    du = float(np.max(np.abs(u - ref.u)))
-    # exact against the GPU's own statistics: gate threshold, lock update, compaction
-    thr = float(st.gate_thr[0].item())
-    assert thr == np.sort(u)[int(np.floor(np.float32(gate) * (M - 1)))]
-    new = (cand0[act] != 0) & (kl <= np.float32(eps)) & (u <= thr)
-    want = locked.copy()
-    want[act[new]] = 1
+    # gate, lock, compaction and sampler on identical inputs: the GPU's logits, the same previous posterior
+    stg = O.posterior_stats(gz, prev64, dm.mask_id)
+    lr = O.lock_update(locked, act, off, B, N, stg.kl, stg.u, cand0, eps, gate, True)
     g_locked = st.locked.cpu().numpy()
-    np.testing.assert_array_equal(g_locked, want)
-    ri, ro = O.active_set(g_locked, B, N)
-    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
-    np.testing.assert_array_equal(st.act_idx[:int(ro[-1])].cpu().numpy(), ri)
-    # against the oracle: differing decisions only inside the band the u error allows
-    band = 2 * du + abs(thr - lr.gate_thr[0])
-    diff = np.flatnonzero(new != lr.new_lock)
-    say("late-step locks: gpu %d oracle %d differing %d (u error %.2e)" % (int(new.sum()), int(lr.new_lock.sum()),
-                                                                        len(diff), du))
-    assert np.all(np.abs(ref.u[diff] - lr.gate_thr[0]) <= band)
-    # sampler: the GPU's picks follow its own confidences; against the oracle only near-ties differ
-    gtok = st.tok.cpu().numpy()
-    gpu_picked = np.flatnonzero(gtok != tok0)
-    assert len(gpu_picked) == k_unmask and np.all(tok0[gpu_picked] == dm.mask_id)
-    conf_g = st.conf[:M].cpu().numpy()
-    masked_rows = np.flatnonzero(tok0[act] == dm.mask_id)
-    order = masked_rows[np.lexsort((act[masked_rows], -conf_g[masked_rows]))][:k_unmask]
-    np.testing.assert_array_equal(np.sort(act[order]), np.sort(gpu_picked))
-    g_am = st.argmax[:M].cpu().numpy()
-    np.testing.assert_array_equal(gtok[act[order]], g_am[order])
-    picked = O.sampler_unmask(tok0.copy(), cand0.copy(), act, off, N, ref.argmax, ref.conf, dm.mask_id, k_unmask)
-    kth = np.sort(ref.conf[masked_rows])[-k_unmask]
-    rowof = {int(p): i for i, p in enumerate(act)}
-    for gp in set(picked) ^ set(gpu_picked.tolist()):
-        assert abs(ref.conf[rowof[gp]] - kth) <= 0.1 * kth, "sampler pick %d not a near-tie" % gp
+    nd = compare_lock(dict(kl=kl, u=st.u[:M].cpu().numpy(), lse=st.lse[:M].cpu().numpy(),
+                           conf=st.conf[:M].cpu().numpy(), argmax=st.argmax[:M].cpu().numpy(),
+                           gate_thr=st.gate_thr.cpu().numpy(), locked=g_locked, act_idx=st.act_idx.cpu().numpy(),
+                           act_off=st.act_off.cpu().numpy(), M=int(st.act_off[1].item())),
+                      stg, lr, locked, act, off, B, N, eps, gate, True)
+    lr_own = O.lock_update(locked, act, off, B, N, ref.kl, ref.u, cand0, eps, gate, True)
+    say("late-step locks: gpu %d, oracle on the GPU's logits %d, oracle on its own logits %d; exempt "
+        "differences %d" % (int(g_locked.sum() - locked.sum()), int(lr.new_lock.sum()), int(lr_own.new_lock.sum()), nd))
+    _sampler_check(st.tok.cpu().numpy(), tok0, cand0, act, off, N, stg, dm.mask_id, k_unmask)
 
 
 # ------------------------------------------------------------------ tiny fp32 sampler loop (teacher-forced)
@@ -497,6 +591,56 @@ def test_tiny_loop_free_running_invariants():
     assert len(frozen) > 0
 
 
+@pytest.mark.parametrize("rule", ["surelock", "gate_only"])
+def test_tiny_loop_free_running_against_oracle(rule):
+    """The GPU loop and the oracle's loop both run free from the same start (2 sequences of the tiny
+    fp32 model, 16 steps, 3 unmasks per step).  One flipped decision changes every later step, so
+    the loops are compared step by step up to the first divergence of tokens, lock mask or active
+    list; that divergence, if any, must be an exempt near-threshold case (a lock decision with the
+    oracle's KL within 1e-3 of eps or u within 4e-6 of the gate threshold, or a sampler pick whose
+    confidence ties the k-th largest within 1e-5).  The step and the M_t trajectory are reported."""
+    sl = _sl()
+    dm = W.TINY
+    B, N, T, k = 2, 64, 16, 3
+    eps, gate, _ = LOOP_RULES[rule]
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    recs = O.run_loop(om, tok0, B, N, T, eps, gate, k)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+    first, Ms = None, []
+    for t in range(T):
+        say("free-running loop", rule, "step", t)
+        Ms.append(st.M_tot)
+        st.step(eps, gate, dm.mask_id, True, k)
+        torch.cuda.synchronize()
+        r = recs[t]
+        g_tok, g_locked = st.tok.cpu().numpy(), st.locked.cpu().numpy()
+        if first is None and not (np.array_equal(g_tok, r.tok) and np.array_equal(g_locked, r.locked)):
+            first = t
+            rows_seq = O.seq_of_rows(r.act_off)
+            glob = rows_seq * N + r.act_idx.astype(np.int64)
+            thr = O.lock_update(np.zeros(B * N, np.uint8), r.act_idx, r.act_off, B, N, r.stats.kl, r.stats.u,
+                                None, eps, gate, t > 0).gate_thr
+            for gp in np.flatnonzero(g_locked != r.locked):
+                i = int(np.flatnonzero(glob == gp)[0])
+                near = abs(r.stats.kl[i] - eps) <= KL_BAND or (
+                    gate >= 0 and abs(r.stats.u[i] - thr[rows_seq[i]]) <= GATE_BAND)
+                assert near, "free-running divergence at step %d: lock of %d is not near the threshold" % (t, gp)
+            for gp in np.flatnonzero(g_tok != r.tok):
+                i = int(np.flatnonzero(glob == gp)[0])
+                b = rows_seq[i]
+                rows = np.arange(r.act_off[b], r.act_off[b + 1])
+                masked = rows[recs[t - 1].tok[glob[rows]] == dm.mask_id] if t > 0 else rows[tok0[glob[rows]] == dm.mask_id]
+                kth = np.sort(r.stats.conf[masked])[-k]
+                zi = np.delete(r.logits[i], dm.mask_id)
+                top2 = np.sort(zi)[-2:]
+                near_pick = abs(r.stats.conf[i] - kth) <= 1e-5 * kth
+                near_token = top2[1] - top2[0] <= 1e-4          # both picked it, argmax near a tie
+                assert near_pick or near_token, "free-running divergence at step %d: pick %d" % (t, gp)
+    say("free-running %s: M_t %s; first divergence: %s" % (rule, Ms, "none" if first is None else "step %d" % first))
+
+
 def test_step_with_every_position_locked_is_a_no_op():
     """M_tot = 0 (every position locked): the step launches nothing and changes nothing."""
     sl = _sl()
@@ -595,15 +739,14 @@ def test_batched_ragged_step(dm, B, N, gate, ms):
     M = len(glob)
     kl = st.kl[:M].cpu().numpy()
     assert np.max(np.abs(kl - out.stats.kl)) <= KL_BAND
-    g_locked = st.locked.cpu().numpy()
-    diff = np.flatnonzero(g_locked != out.lock.locked)
-    for gp in diff:
-        i = int(np.flatnonzero(glob == gp)[0])
-        near = abs(out.stats.kl[i] - eps) <= KL_BAND or (gate >= 0 and abs(out.stats.u[i] - out.lock.gate_thr[rows_seq[i]]) <= GATE_BAND)
-        assert near
-    ri, ro = O.active_set(g_locked, B, N)
-    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
-    np.testing.assert_array_equal(st.act_idx[:st.M_tot].cpu().numpy(), ri)
+    # gate, lock and compaction on identical inputs: the GPU's logits and the same previous posterior
+    stg = O.posterior_stats(cur[glob], prev64[glob], -1)
+    lr = O.lock_update(locked, case.act_idx, case.act_off, B, N, stg.kl, stg.u, None, eps, gate, True)
+    nd = compare_lock(dict(kl=kl, u=st.u[:M].cpu().numpy(), lse=st.lse[:M].cpu().numpy(),
+                           gate_thr=st.gate_thr.cpu().numpy() if gate >= 0 else None, locked=st.locked.cpu().numpy(),
+                           act_idx=st.act_idx.cpu().numpy(), act_off=st.act_off.cpu().numpy(), M=st.M_tot),
+                      stg, lr, locked, case.act_idx, case.act_off, B, N, eps, gate, True)
+    say("batched step: new locks %d, exempt differences %d" % (int(lr.new_lock.sum()), nd))
 
 
 @pytest.mark.slow
@@ -613,12 +756,11 @@ def test_batched_step_full_shape_with_head():
     (eps 0.05, gate at each sequence's median u) and compaction in one sl_step at t = 1.
 
     Teacher-forced: the previous posterior is the oracle's own logits of this step plus N(0, 0.05^2)
-    drift, so every KL is near 0.00125 and the gate decides the locks.  Logits go through one layer of
-    bf16 intermediates, so they are held to the hidden-row bound (relative L2 1e-2, no element beyond
-    7 rms).  KL within 1e-3; u and lse within the bound their definitions give from the largest logit
-    error.  The gate, lock and compaction are checked exactly against the GPU's own statistics, and
-    against the oracle's decisions except where the gap between u and the gate threshold is inside
-    what the u error can move."""
+    drift, so every KL is near 0.00125 and the gate decides the locks.  Logits: within 1.25x the
+    bf16-storage emulation of the same step against the oracle, and the LM head alone within max-abs
+    2e-2 of the product of the GPU's own final hidden rows.  KL within 1e-3 of the oracle's.  Gate,
+    lock and compaction against the oracle's rules on identical inputs (the GPU's own logits and the
+    same previous posterior): bit-exact except |KL - eps| <= 1e-3 or |u - q| <= 4e-6."""
     sl = _sl()
     dm = W.LLADA_LAYER
     B, N, eps, gate = 8, 2048, 0.05, 0.5
@@ -628,6 +770,7 @@ def test_batched_step_full_shape_with_head():
     M = case.M_tot
     Wnp = W.layer_weights(dm, 0)
     head = W.lm_head_weights(dm)
+    head64 = O.widen(head, "bf16")
     locked = np.ones(B * N, np.uint8)
     for b in range(B):
         locked[b * N + case.act_idx[case.act_off[b]:case.act_off[b + 1]]] = 0
@@ -639,21 +782,24 @@ def test_batched_step_full_shape_with_head():
     ost = O.OracleState(B=B, N=N, t=0, locked=locked.copy(), kc=[O.widen(case.k_cache, "bf16")],
                         vc=[O.widen(case.v_cache, "bf16")], h_in=O.widen(case.h_in, "bf16"))
     h = O.step(O.OracleModel(od, 1, lambda l: W64), ost, 0.0, -1.0, do_lock=False).h
-    del W64, ost
-    z = O.rmsnorm(h, dm.rms_eps) @ O.widen(head, "bf16").T
+    del ost
+    z = O.rmsnorm(h, dm.rms_eps) @ head64.T
     prev_st = W.to_storage(z.astype(np.float32) + W.normal(W.rng(W.SEED_DRIFT, 4343), z.shape, 0.05), "bf16")
     prev64 = O.widen(prev_st, "bf16")
     ref = O.posterior_stats(z, prev64)
-    del prev64
-    lr = O.lock_update(locked, case.act_idx, case.act_off, B, N, ref.kl, ref.u, None, eps, gate, True)
-    say("oracle done: new locks %d" % int(lr.new_lock.sum()))
+    say("oracle done; bf16-storage emulation")
+    eh = E.step_rows(O.widen(case.h_in, "bf16")[glob], case.act_idx, case.act_off, lambda l: W64, 1,
+                     [O.widen(case.k_cache, "bf16")], [O.widen(case.v_cache, "bf16")], _edims(dm))
+    del W64
+    es = E.err_stats(E.logits(eh, head64, dm.rms_eps, f32=True), z)
+    del eh
     # GPU: the same step at t = 1 with that previous posterior in buffer 0
     model = _dev_model(dm, [Wnp], None, head, rope_n=N)
     H, Dh = dm.n_heads, dm.head_dim
     st = sl.DeviceState(model, B, N, locked=torch.from_numpy(locked).cuda(), h_in=dev(case.h_in, "bf16"),
                         k_cache=dev(case.k_cache, "bf16").reshape(1, B, N, H, Dh),
                         v_cache=dev(case.v_cache, "bf16").reshape(1, B, N, H, Dh),
-                        cand=torch.ones(B * N, dtype=torch.uint8, device="cuda"))
+                        cand=torch.ones(B * N, dtype=torch.uint8, device="cuda"), with_h_out=True)
     assert st.M_tot == M
     gi = torch.from_numpy(glob).cuda()
     st.logits[0].index_copy_(0, gi, dev(prev_st, "bf16"))
@@ -662,35 +808,24 @@ def test_batched_step_full_shape_with_head():
     st.step(eps, gate, -1, True, 0)
     torch.cuda.synchronize()
     cur = host64(st.logits[1].index_select(0, gi))
-    l2, rms, mx = check_hidden(cur, z, 1e-2, "logits")
-    say("logits: rel L2 %.3e rms %.3e max %.3e" % (l2, rms, mx))
-    dz = float(np.max(np.abs(cur - z)))
-    del cur, z
-    kl, u, lse = st.kl[:M].cpu().numpy(), st.u[:M].cpu().numpy(), st.lse[:M].cpu().numpy()
+    gv = E.check(cur, z, es, "logits")
+    say("logits: rel L2 %.3e (emulated %.3e) rms %.3e max %.3e (emulated %.3e)" % (
+        gv.rel_l2, es.rel_l2, gv.rms, gv.max, es.max))
+    del z
+    _head_from_own_hidden_check(cur, st.h_out[:M].cpu().numpy().astype(np.float64), head64, dm.rms_eps,
+                                "batched step")
+    kl = st.kl[:M].cpu().numpy()
     assert np.max(np.abs(kl - ref.kl)) <= KL_BAND
-    # lse moves by at most the largest logit error; u = 1 - exp(max z - lse) by at most twice that
-    assert np.max(np.abs(lse - ref.lse)) <= dz + 1e-4
-    du = float(np.max(np.abs(u - ref.u)))
-    assert du <= 2 * dz + 1e-5
-    # gate, lock and compaction, exactly, on the GPU's own statistics
-    thr = st.gate_thr.cpu().numpy()
+    lr_own = O.lock_update(locked, case.act_idx, case.act_off, B, N, ref.kl, ref.u, None, eps, gate, True)
+    del ref
+    # gate, lock and compaction on identical inputs: the GPU's logits and the same previous posterior
+    stg = O.posterior_stats(cur, prev64)
+    del cur, prev64
+    lr = O.lock_update(locked, case.act_idx, case.act_off, B, N, stg.kl, stg.u, None, eps, gate, True)
     g_locked = st.locked.cpu().numpy()
-    new = np.zeros(M, dtype=bool)
-    for b in range(B):
-        s_ = slice(case.act_off[b], case.act_off[b + 1])
-        kth = int(np.floor(np.float32(gate) * (Ms[b] - 1)))
-        assert thr[b] == np.sort(u[s_])[kth]
-        new[s_] = (kl[s_] <= np.float32(eps)) & (u[s_] <= thr[b])
-    want = locked.copy()
-    want[glob[new]] = 1
-    np.testing.assert_array_equal(g_locked, want)
-    ri, ro = O.active_set(g_locked, B, N)
-    np.testing.assert_array_equal(st.act_off.cpu().numpy(), ro)
-    np.testing.assert_array_equal(st.act_idx[:int(ro[-1])].cpu().numpy(), ri)
-    # against the oracle's decisions: a row may differ only where |u - q| is within what the errors allow
-    band = 2 * du + np.abs(thr - lr.gate_thr)[rows_seq]
-    diff = np.flatnonzero(new != lr.new_lock)
-    near = np.abs(ref.u - lr.gate_thr[rows_seq]) <= band
-    say("lock decisions: gpu %d oracle %d differing %d (u error %.2e)" % (int(new.sum()), int(lr.new_lock.sum()),
-                                                                       len(diff), du))
-    assert np.all(near[diff])
+    nd = compare_lock(dict(kl=kl, u=st.u[:M].cpu().numpy(), lse=st.lse[:M].cpu().numpy(),
+                           gate_thr=st.gate_thr.cpu().numpy(), locked=g_locked, act_idx=st.act_idx.cpu().numpy(),
+                           act_off=st.act_off.cpu().numpy(), M=int(st.act_off[B].item())),
+                      stg, lr, locked, case.act_idx, case.act_off, B, N, eps, gate, True)
+    say("lock decisions: gpu %d, oracle on the GPU's logits %d (exempt differences %d), oracle on its own "
+        "logits %d" % (int(g_locked.sum() - locked.sum()), int(lr.new_lock.sum()), nd, int(lr_own.new_lock.sum())))

@@ -24,6 +24,35 @@ from tests.dense_ref import dense_block, dense_logits, rope_complex
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kl_closed_forms.json")))
 
 
+# ------------------------------------------------------------------ storage widening
+# bfloat16 is the upper half of an IEEE binary32: sign, 8 exponent bits, 7 mantissa bits.  Hand
+# bit patterns and the values the format defines for them.
+BF16_PATTERNS = [
+    (0x3F80, 1.0), (0xC000, -2.0), (0x3F81, 1.0 + 2.0 ** -7), (0x4049, 3.140625),
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),        # largest finite, 3.3895e38
+    (0x0080, 2.0 ** -126),                            # smallest normal
+    (0x0001, 2.0 ** -133),                            # smallest subnormal
+    (0x8000, -0.0), (0x7F80, math.inf), (0xFF80, -math.inf),
+]
+
+
+def pin_widen_bf16():
+    bits = np.array([b for b, _ in BF16_PATTERNS], dtype=np.uint16)
+    got = O.widen(bits, "bf16")
+    assert got.dtype == np.float64
+    for (b, want), g in zip(BF16_PATTERNS, got):
+        assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), (hex(b), g, want)
+    nan = O.widen(np.array([0x7FC0, 0xFFC1], dtype=np.uint16), "bf16")
+    assert np.isnan(nan).all()
+    # f32 storage is the value itself
+    x = np.array([1.5, -2.25e-30, 3.0e38], dtype=np.float32)
+    assert np.array_equal(O.widen(x, "f32"), x.astype(np.float64))
+
+
+def test_widen_bf16_bit_patterns():
+    pin_widen_bf16()
+
+
 # ------------------------------------------------------------------ KL / u / LSE
 def pin_kl_closed_forms():
     for c in GOLD["cases"]:
@@ -384,6 +413,13 @@ def _expect_fail(fn):
 
 def test_planted_mistakes(monkeypatch):
     """Plausible oracle mistakes are caught by the pins above."""
+    good_widen = O.widen
+    for bad in (lambda a, dt: (np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64),
+                lambda a, dt: np.asarray(a, np.uint16).view(np.float16).astype(np.float64)):
+        monkeypatch.setattr(O, "widen", lambda a, dt, bad=bad: bad(a, dt) if dt == "bf16" else good_widen(a, dt))
+        _expect_fail(pin_widen_bf16)
+    monkeypatch.setattr(O, "widen", good_widen)
+
     good_stats = O.posterior_stats
 
     def reversed_kl(z, y, mask_id=-1, chunk=64):
