@@ -156,6 +156,22 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
 size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V);
 
 /*
+ * sl_kl_lock_noalloc — sl_kl_lock for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and limits as sl_kl_lock, without ws / ws_bytes: the partial sums of the vocabulary
+ * pass go to a 128 KiB device array inside the library (one per GPU, held until the process
+ * ends), which covers every size sl_kl_lock accepts.  No allocation, no memset; nothing in the
+ * array needs to start at zero.  Calls that overlap on one GPU (two streams at once) share that
+ * array and race: serialise them.  Returns SL_ERR_UNSUPPORTED if a size ever needed more scratch.
+ */
+sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logits_prev, int V,
+                             const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
+                             const uint8_t* cand, const sl_lock_params* params, uint8_t* locked,
+                             float* kl, float* u, float* lse, int32_t* argmax, float* conf,
+                             float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                             int32_t* m_tot_host, sl_stream stream);
+
+/*
  * sl_rope_table — cos/sin table of rotary position embeddings (rotate-half
  * form: pair j = (x_j, x_{j+Dh/2}) rotated by pos * theta^(-2j/Dh)), computed
  * on the device in double precision and stored as float pairs.

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/surelock.h"
 #include "internal.hpp"
 
@@ -107,6 +109,39 @@ sl_status check_model(const sl_model* m) {
   if (m->lm_head) {
     SL_REQUIRE(m->vocab > 0 && m->vocab % 128 == 0, SL_ERR_UNSUPPORTED, "vocab %% 128 != 0 (vocab = %d)", m->vocab);
   }
+  return SL_OK;
+}
+
+// Scratch memory of sl_kl_lock_noalloc: the vocabulary pass's per-segment partial sums live in this
+// file-scope device array instead of a caller workspace.  Every (M_tot, V) needs at most
+// (M_tot * ceil(2048 / M_tot)) * 32 < 4096 * 32 bytes of partials (one segment per row once
+// M_tot >= 2048), so 128 KiB covers every size sl_kl_lock accepts.  Each device holds its own
+// copy; host code reaches it only through the address hipGetSymbolAddress returns for the current
+// device (the array's name on the host is not a device address).
+constexpr size_t kNoAllocScratchBytes = 128 * 1024;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device.
+sl_status scratch_ptr(void** out) {
+  int dev = -1;
+  SL_TRY(hipGetDevice(&dev), "hipGetDevice");
+  SL_REQUIRE(dev >= 0 && dev < kMaxDevices, SL_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    SL_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    SL_REQUIRE(p != nullptr, SL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return SL_OK;
 }
 
@@ -231,6 +266,24 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
     SL_TRY(hipStreamSynchronize(s), "sl_kl_lock sync");
   }
   return SL_OK;
+}
+
+sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logits_prev, int V,
+                             const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
+                             const uint8_t* cand, const sl_lock_params* params, uint8_t* locked, float* kl,
+                             float* u, float* lse, int32_t* argmax, float* conf, float* gate_thr,
+                             int32_t* new_act_idx, int32_t* new_act_off, int32_t* m_tot_host, sl_stream stream) {
+  g_err[0] = 0;
+  SL_REQUIRE(B >= 1 && N >= 1 && V > 0 && M_tot >= 0, SL_ERR_INVALID, "bad size");
+  const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
+  SL_REQUIRE(need <= kNoAllocScratchBytes, SL_ERR_UNSUPPORTED,
+             "sl_kl_lock_noalloc: %zu bytes of partial sums exceed its %zu-byte scratch", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  sl_status st = scratch_ptr(&ws);
+  if (st != SL_OK) return st;
+  return sl_kl_lock(dtype, logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, params, locked, kl, u,
+                    lse, argmax, conf, gate_thr, new_act_idx, new_act_off, m_tot_host, ws, kNoAllocScratchBytes,
+                    stream);
 }
 
 sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_stream stream) {

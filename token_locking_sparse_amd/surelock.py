@@ -60,7 +60,7 @@ class sl_step_params(C.Structure):
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
            "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_step_workspace_min", "sl_gemm",
-           "sl_gemm_plan")
+           "sl_gemm_plan", "sl_kl_lock_noalloc")
 
 _lib = None
 
@@ -85,6 +85,8 @@ def lib():
         "sl_kl_lock": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
                            vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sl_kl_lock_workspace_size": (sz, [i, i, i, i]),
+        "sl_kl_lock_noalloc": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
+                                   vp, vp, vp, vp, vp, vp, vp]),
         "sl_rope_table": (i, [i, i, f, vp, vp]),
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
@@ -208,6 +210,29 @@ def sl_kl_lock(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, 
                           m_tot_host.ptr if m_tot_host else None, _ptr(ws, "ws"), ws.numel() * ws.element_size(),
                           _stream(stream))
     _check("sl_kl_lock", st)
+    return m_tot_host.value if m_tot_host else None
+
+
+def sl_kl_lock_noalloc(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, eps, gate_q, mask_id,
+                       have_prev, locked, kl, u, lse, argmax, conf, gate_thr, new_act_idx, new_act_off,
+                       m_tot_host: PinnedInt | None = None, stream=None):
+    """sl_kl_lock without a workspace argument (the library's own per-GPU scratch array)."""
+    dt = dtype_code(logits_cur.dtype)
+    p = sl_lock_params(float(eps), float(gate_q), int(mask_id), int(bool(have_prev)))
+    st = lib().sl_kl_lock_noalloc(dt, _ptr(logits_cur, "logits_cur", logits_cur.dtype),
+                                  _ptr(logits_prev, "logits_prev", logits_cur.dtype, optional=not have_prev), V,
+                                  _ptr(act_idx, "act_idx", torch.int32) if M_tot > 0 else None,
+                                  _ptr(act_off, "act_off", torch.int32), B, N, M_tot,
+                                  _ptr(cand, "cand", torch.uint8, optional=True), C.byref(p),
+                                  _ptr(locked, "locked", torch.uint8), _ptr(kl, "kl", torch.float32),
+                                  _ptr(u, "u", torch.float32), _ptr(lse, "lse", torch.float32),
+                                  _ptr(argmax, "argmax", torch.int32, optional=True),
+                                  _ptr(conf, "conf", torch.float32, optional=True),
+                                  _ptr(gate_thr, "gate_thr", torch.float32, optional=True),
+                                  _ptr(new_act_idx, "new_act_idx", torch.int32),
+                                  _ptr(new_act_off, "new_act_off", torch.int32),
+                                  m_tot_host.ptr if m_tot_host else None, _stream(stream))
+    _check("sl_kl_lock_noalloc", st)
     return m_tot_host.value if m_tot_host else None
 
 
