@@ -170,8 +170,8 @@ def gpu_part(args):
         evk[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_M = {M: float(np.mean([evs[i][M][0].elapsed_time(evs[i][M][1]) for i in range(args.warmup, n_it)])) for M in MS}
-    ms_kl = float(np.mean([evk[i][0].elapsed_time(evk[i][1]) for i in range(args.warmup, n_it)]))
+    ms_M = {M: float(np.median([evs[i][M][0].elapsed_time(evs[i][M][1]) for i in range(args.warmup, n_it)])) for M in MS}
+    ms_kl = float(np.median([evk[i][0].elapsed_time(evk[i][1]) for i in range(args.warmup, n_it)]))
     M_after = int(kl_nao[1].item())
 
     # ---------------- the no-KV-cache ablation on the same active sets: attention over the M
@@ -188,7 +188,7 @@ def gpu_part(args):
             e1.record()
             es.append((e0, e1))
         torch.cuda.synchronize()
-        ms_abl[M] = float(np.mean([a.elapsed_time(b) for a, b in es[args.warmup:]]))
+        ms_abl[M] = float(np.median([a.elapsed_time(b) for a, b in es[args.warmup:]]))
 
     # ---------------- dominant kernel alone: the FFN gate/up GEMM + SwiGLU at M = 1024
     Mg = 1024
@@ -203,7 +203,7 @@ def gpu_part(args):
         e1.record()
         kg.append((e0, e1))
     torch.cuda.synchronize()
-    ms_gu = float(np.mean([a.elapsed_time(b) for a, b in kg[args.warmup:]]))
+    ms_gu = float(np.median([a.elapsed_time(b) for a, b in kg[args.warmup:]]))
 
     # breakdown of the M=1024 layer step by GEMM (same kernels sl_step launches)
     h32 = torch.zeros(Mg, D, dtype=torch.float32, device=dev)
@@ -226,7 +226,7 @@ def gpu_part(args):
             e1.record()
             es.append((e0, e1))
         torch.cuda.synchronize()
-        br[name] = float(np.mean([a.elapsed_time(b) for a, b in es[args.warmup:]]))
+        br[name] = float(np.median([a.elapsed_time(b) for a, b in es[args.warmup:]]))
     br["gate_up_swiglu"] = ms_gu
 
     per_M = []
@@ -269,12 +269,14 @@ SURELOCK_RUNS = (("eps=0", 0.0, -1.0, False), ("eps=0.01", 0.01, -1.0, False), (
 ABLATION_RUNS = (("gate_only m=0.5", math.inf, 0.5, False), ("no_kv_cache eps=0.05", 0.05, -1.0, True))
 
 
-def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1):
+def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1, captured=False):
     """The whole sampler loop on a 32-layer LLaDA-8B-shaped model with random-init weights (d=4096,
     32 heads x 128, SwiGLU 12288, vocab 126464, bf16), B sequences of N=512 = 128 seeded prompt ids +
     384 [MASK]; 128 steps, 3 unmasks per sequence per step by confidence.  Each run is (name, eps,
     gate quantile or -1 for off, no-KV-cache ablation); eps = 0 is the dense reference (nothing
-    locks).  Reports per-step time against the active count M_t (summed over the batch)."""
+    locks).  Reports per-step time against the active count M_t (summed over the batch).
+    captured: the device-resident loop (the first step eager, then one HIP graph replay per step,
+    the active count never read back inside the loop) instead of the host-driven one."""
     import numpy as np
     import torch
 
@@ -302,17 +304,37 @@ def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1):
         st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).to(dev),
                             cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).to(dev))
         Ms, ms = [], []
+        loop, n_graphs = None, 0
+        if captured:
+            # the graphs of every capacity (multiples of 64 up to B*N) and both step parities are
+            # captured before the timed loop: capture is host work paid once per shape
+            loop = sl.CapturedLoop(st, eps, gate, dm.mask_id, unmask, no_kv, bucket=max(64, 16 * B))
+            loop.precapture()
+            m_hist = torch.full((steps,), -1, dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(steps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            Ms.append(st.M_tot)
+            if not captured:
+                Ms.append(st.M_tot)
             e0.record()
-            st.step(eps, gate, dm.mask_id, True, unmask, no_kv_cache=no_kv)
+            if captured and t > 0:
+                loop.step(m_hist)
+            else:
+                if captured:
+                    m_hist[0:1].copy_(st.act_off[B:B + 1])
+                st.step(eps, gate, dm.mask_id, True, unmask, no_kv_cache=no_kv)
+                if captured:
+                    loop.known_m = st.M_tot
             e1.record()
             ms.append((e0, e1))
+        if captured:
+            loop.finish()
+            n_graphs = len(loop.graphs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if captured:
+            Ms = m_hist.cpu().tolist()
         ms = [a.elapsed_time(b) for a, b in ms]
         # per row: the layers' projections and FFN, attention over N keys (over the M_t / B active
         # positions of its sequence when locked positions are not attended), and the LM head
@@ -325,9 +347,11 @@ def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1):
         if len(curve) > 12:
             curve = [curve[i] for i in np.linspace(0, len(curve) - 1, 12).round().astype(int)]
         out[name] = {"ms_total": round(wall * 1e3, 2), "ms_per_step_mean": round(wall * 1e3 / steps, 3),
-                               "tokens_per_s": round(B * (N - n_prompt) / wall, 1),
-                               "tflops": round(fl / wall / 1e12, 2), "M_first": Ms[0], "M_last": st.M_tot,
-                               "rows_computed": int(sum(Ms)), "flops": fl, "ms_vs_M": curve}
+                     "tokens_per_s": round(B * (N - n_prompt) / wall, 1),
+                     "tflops": round(fl / wall / 1e12, 2), "M_first": Ms[0], "M_last": st.M_tot,
+                     "rows_computed": int(sum(Ms)), "flops": fl, "ms_vs_M": curve}
+        if captured:
+            out[name]["graphs_captured"] = n_graphs
         del st
     dense = out.get("eps=0")
     for k, v in out.items():
@@ -340,7 +364,161 @@ def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1):
     return out
 
 
-def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
+def cache_layout_study(steps=50, warmup=10, Ms=(1024, 256, 64)):
+    """The K/V cache laid out token-major ([B][N][H][Dh], a position's K row is one 8 KB run: the
+    scatter writes whole rows, attention reads 256-byte slices 8 KB apart) against head-major
+    ([B][H][N][Dh], a head's keys are one contiguous run: attention streams it, the scatter writes
+    256-byte slices).  Only the fused QKV scatter and attention see the layout, so the layer step's
+    time difference is theirs.  LLaDA-8B layer shape, N = 1024, weights rotated over 3 copies;
+    medians of `steps` steps."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import token_locking_sparse_amd.surelock as S
+    import workloads as W
+
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    bf = torch.bfloat16
+
+    def randn(shape, std=1.0):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+
+    shapes = {"wq": (D, D), "wk": (D, D), "wv": (D, D), "wo": (D, D), "wg": (F, D), "wu": (F, D), "wd": (D, F)}
+    wsets = [{k: randn(sh, 0.02) for k, sh in shapes.items()} for _ in range(3)]
+    models = [sl.DeviceModel(dtype=bf, n_layers=1, d=D, n_heads=H, head_dim=DH, ffn=F, vocab=126464, rms_eps=1e-5,
+                             rope_theta=1e4, layers=[w], rope_n=N_LAYER) for w in wsets]
+    h_in = randn((N_LAYER, D))
+    kc_t = randn((1, 1, N_LAYER, H, DH))
+    vc_t = randn((1, 1, N_LAYER, H, DH))
+    caches = {False: (kc_t, vc_t),
+              True: (kc_t.permute(0, 1, 3, 2, 4).contiguous(), vc_t.permute(0, 1, 3, 2, 4).contiguous())}
+    p = S.sl_step_params(0.0, -1.0, -1, 0, 0)
+    out = {}
+    for M in Ms:
+        act = W.choose_active(N_LAYER, M, W.SEED_SETS, M)
+        locked = torch.from_numpy(W.locked_from_active(N_LAYER, act)).to(dev)
+        row = {}
+        for hm in (False, True):
+            kc, vc = caches[hm]
+            st = sl.DeviceState(models[0], 1, N_LAYER, locked=locked, h_in=h_in, k_cache=kc, v_cache=vc,
+                                with_h_out=True, kv_head_major=hm)
+            sst = st.struct()
+            es = []
+            for i in range(warmup + steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                S.sl_step(models[i % 3].s, sst, p, st.ws)
+                e1.record()
+                es.append((e0, e1))
+            torch.cuda.synchronize()
+            row["head_major" if hm else "token_major"] = round(float(np.median([a.elapsed_time(b) for a, b in es[warmup:]])), 4)
+            del st
+        out[str(M)] = row
+    del wsets, models, caches, kc_t, vc_t
+    torch.cuda.empty_cache()
+    return {"layer_step_ms": out, "config": "LLaDA-8B layer, N=1024, M in %s; medians of %d steps" % (list(Ms), steps)}
+
+
+def measured_peaks(reps=7):
+    """What this chip sustains: a register-only bf16 MFMA loop on every CU, and 16-byte non-temporal
+    streaming of 1 GiB (read only, and copy).  Medians of `reps` launches timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+
+    dev = "cuda"
+    sink = torch.zeros(256, device=dev)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        fn()
+        es = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    wg, iters = 2048, 2048
+    flops = sl.sl_peak_mfma(wg, iters, sink)
+    ms_mfma = timed(lambda: sl.sl_peak_mfma(wg, iters, sink))
+    ms_read = timed(lambda: sl.sl_peak_stream(src, None, 2048, sink))
+    ms_copy = timed(lambda: sl.sl_peak_stream(src, dst, 2048, sink))
+    nb = src.numel()
+    out = {"mfma_bf16_tflops": round(flops / (ms_mfma * 1e-3) / 1e12, 1),
+           "hbm_read_gbs": round(nb / (ms_read * 1e-3) / 1e9, 1),
+           "hbm_copy_gbs": round(2 * nb / (ms_copy * 1e-3) / 1e9, 1),
+           "how": "register-only v_mfma_f32_32x32x16_bf16 loop, %d workgroups x 4 waves x %d x 4 MFMAs; "
+                  "1 GiB streamed with 16-byte non-temporal loads (read) and loads + stores (copy, bytes "
+                  "read + written), each workgroup on a contiguous range; medians of %d launches" % (wg, iters, reps)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def tiny_loop(steps=16, B=1, N=64, n_prompt=16, unmask=3, eps=0.05, reps=5):
+    """The tiny fp32 sampler loop (2 layers, d=128, 4 heads x 32, SwiGLU 384, vocab 512, N=64 = 16
+    prompt ids + 48 [MASK], 16 steps, 3 unmasks per step, eps 0.05, gate off): ms per step (median
+    over `reps` loops) and the active count M_t per step, host-driven and device-resident."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import workloads as W
+
+    dm = W.TINY
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    layers = [W.layer_weights(dm, l) for l in range(dm.n_layers)]
+    model = sl.DeviceModel(dtype=torch.float32, n_layers=dm.n_layers, d=dm.d, n_heads=dm.n_heads,
+                           head_dim=dm.head_dim, ffn=dm.ffn, vocab=dm.vocab, rms_eps=dm.rms_eps,
+                           rope_theta=dm.rope_theta, layers=[{k: to_dev(v) for k, v in L.items()} for L in layers],
+                           embed=to_dev(W.embed_weights(dm)), lm_head=to_dev(W.lm_head_weights(dm)), rope_n=N)
+    tok0 = W.prompt_tokens(dm, B, N, n_prompt)
+    res = {}
+    for mode in ("host", "captured"):
+        walls, Ms = [], None
+        for r in range(reps + 1):
+            st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                                cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+            loop = None
+            if mode == "captured":
+                loop = sl.CapturedLoop(st, eps, -1.0, dm.mask_id, unmask, bucket=16)
+                loop.precapture()
+                m_hist = torch.full((steps,), -1, dtype=torch.int32, device="cuda")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "host":
+                ms_t = [st.M_tot]
+                for t in range(steps):
+                    st.step(eps, -1.0, dm.mask_id, True, unmask)
+                    ms_t.append(st.M_tot)
+                ms_t = ms_t[:steps]
+            else:
+                m_hist[0:1].copy_(st.act_off[B:B + 1])
+                st.step(eps, -1.0, dm.mask_id, True, unmask)
+                loop.known_m = st.M_tot
+                for t in range(1, steps):
+                    loop.step(m_hist)
+                loop.finish()
+            torch.cuda.synchronize()
+            if r > 0:                               # the first loop warms up
+                walls.append(time.perf_counter() - t0)
+            Ms = ms_t if mode == "host" else m_hist.cpu().tolist()
+        res[mode] = {"ms_per_step": round(float(np.median(walls)) * 1e3 / steps, 4), "M_t": Ms}
+    res["config"] = "tiny fp32 model (2 layers, d=128, 4x32 heads, FFN 384, V=512), B=%d, N=%d (%d prompt + %d [MASK]), " \
+                    "%d steps, %d unmasks per step, eps=%g, gate off" % (B, N, n_prompt, N - n_prompt, steps, unmask, eps)
+    return res
+
+
+def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
     """The batched ragged workload: 8 sequences x N=2048, active fraction per sequence uniform on
     [0.05, 0.8] (seeded), one LLaDA-8B-shaped layer + final norm + LM head (V=126464) + KL-lock
     (eps 0.05, gate at each sequence's median u) + compaction, all in one sl_step at t = 1.  The
@@ -382,7 +560,9 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
     st = sl.DeviceState(model, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc,
                         cand=torch.ones(B * N, dtype=torch.uint8, device=dev))
     st_l = sl.DeviceState(model_l, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc)
-    assert st.M_tot == M_tot and st_l.M_tot == M_tot
+    st_hm = sl.DeviceState(model_l, B, N, locked=locked0.clone(), h_in=h_in, kv_head_major=True,
+                           k_cache=kc.permute(0, 1, 3, 2, 4).contiguous(), v_cache=vc.permute(0, 1, 3, 2, 4).contiguous())
+    assert st.M_tot == M_tot and st_l.M_tot == M_tot and st_hm.M_tot == M_tot
     ai0, ao0 = st.act_idx.clone(), st.act_off.clone()
     # previous posterior: this step's logits (t = 0, no lock) plus drift, in buffer 0
     st.step(0.0, do_lock=False)
@@ -393,7 +573,9 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
     sst = st.struct()
     sst.m_tot_host = None                     # no host copy of M: nothing to wait for inside the timing
     p_full = S.sl_step_params(eps, gate, -1, 1, 0)
+    p_fused = S.sl_step_params(eps, gate, -1, 1, 0, 0, 0, 1)   # LM head computes the vocabulary statistics
     sst_l = st_l.struct()
+    sst_hm = st_hm.struct()
     p_layer = S.sl_step_params(0.0, -1.0, -1, 0, 0)
     x = randn((M_tot, D), 1.0)
     kl_o = {k: torch.empty(M_tot, device=dev) for k in ("kl", "u", "lse", "conf")}
@@ -412,7 +594,9 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
 
     calls = {
         "step": lambda: S.sl_step(model.s, sst, p_full, st.ws),
+        "step_fused": lambda: S.sl_step(model.s, sst, p_fused, st.ws),
         "layer": lambda: S.sl_step(model_l.s, sst_l, p_layer, st_l.ws),
+        "layer_head_major": lambda: S.sl_step(model_l.s, sst_hm, p_layer, st_hm.ws),
         "lm_head": lambda: sl.sl_gemm(sl.SL_EPI_LOGITS, x, M_tot, D, V, head, out0=st.logits[1], act_idx=ai0,
                                       act_off=ao0, B=B, N=N),
         "kl_lock": lambda: sl.sl_kl_lock(st.logits[1], st.logits[0], V, ai0, ao0, B, N, M_tot, None, eps, gate, -1,
@@ -430,7 +614,7 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
             e1.record()
             es.append((e0, e1))
         torch.cuda.synchronize()
-        ms[name] = float(np.mean([a.elapsed_time(b) for a, b in es[warmup:]]))
+        ms[name] = float(np.median([a.elapsed_time(b) for a, b in es[warmup:]]))
     restore()
     calls["step"]()
     torch.cuda.synchronize()
@@ -440,7 +624,9 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
     kb = kl_bytes(M_tot, N=B * N, V=V)
     head_plan = sl.sl_gemm_plan(bf, sl.SL_EPI_LOGITS, M_tot, D, V)
     out = {"B": B, "N": N, "M_b": Ms, "M_tot": M_tot, "M_after": M_after, "eps": eps, "gate": gate,
-           "ms_step": round(ms["step"], 4), "ms_layer": round(ms["layer"], 4), "ms_lm_head": round(ms["lm_head"], 4),
+           "ms_step": round(ms["step"], 4), "ms_step_fused_head_kl": round(ms["step_fused"], 4),
+           "ms_layer": round(ms["layer"], 4), "ms_layer_head_major_cache": round(ms["layer_head_major"], 4),
+           "ms_lm_head": round(ms["lm_head"], 4),
            "ms_kl_lock": round(ms["kl_lock"], 4),
            "step_tflops": round((fl_layer + fl_head) / (ms["step"] * 1e-3) / 1e12, 2),
            "layer_tflops": round(fl_layer / (ms["layer"] * 1e-3) / 1e12, 2),
@@ -449,7 +635,7 @@ def batched_step(steps=5, warmup=2, B=8, N=2048, eps=0.05, gate=0.5):
                        "frac_mfma_peak": round(fl_head / (ms["lm_head"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
            "kl": {"bound": "hbm", "bytes": kb, "gbs": round(kb / (ms["kl_lock"] * 1e-3) / 1e9, 1),
                   "frac_hbm_peak": round(kb / (ms["kl_lock"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
-    del st, st_l, model, model_l, layer, head, h_in, kc, vc, x
+    del st, st_l, st_hm, model, model_l, layer, head, h_in, kc, vc, x
     torch.cuda.empty_cache()
     return out
 
@@ -497,6 +683,33 @@ def profile_kernels():
           (Mg, sl.sl_gemm_plan(bf, sl.SL_EPI_SWIGLU, Mg, D, 2 * F), M_kl, src.numel()), flush=True)
 
 
+def profile_attention():
+    """Launch only the active-query attention at the LLaDA-8B layer shape (32 heads x 128, N=1024),
+    M = 1024 and M = 256 (bf16, each 3 times), for rocprofv3 --pmc counter runs."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+    import workloads as W
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    kc = torch.randn((1, N_LAYER, H, DH), generator=g, device=dev).to(bf)
+    vc = torch.randn((1, N_LAYER, H, DH), generator=g, device=dev).to(bf)
+    for M in (1024, 256):
+        q = torch.randn((M, H, DH), generator=g, device=dev).to(bf)
+        out = torch.empty(M, H * DH, dtype=bf, device=dev)
+        off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        ws = torch.empty(max(1, sl.sl_attn_workspace_size(1, N_LAYER, M, H, DH)), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            sl.sl_attn_active(q, kc, vc, off, 1, N_LAYER, M, H, DH, 1.0 / math.sqrt(DH), out, ws)
+    torch.cuda.synchronize()
+    print("profiled: attention at M = 1024 and 256, N = %d, %d heads x %d" % (N_LAYER, H, DH), flush=True)
+
+
 def cpu_part(seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload, on the host cores."""
     import numpy as np
@@ -530,10 +743,79 @@ def cpu_part(seconds: float):
                                                                    platform.machine(), os.cpu_count())}
 
 
+def _host_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # pragma: no cover
+        cores, blas = os.cpu_count(), "?"
+    return int(cores), blas
+
+
+def cpu_configs():
+    """The oracle as it stands on bounded samples of the other workloads, on the host cores; each
+    figure is scaled from its sample to the whole workload by rows (the oracle's cost is linear in
+    the active rows)."""
+    import numpy as np
+
+    import oracle.surelock_oracle as O
+    import workloads as W
+    cores, blas = _host_info()
+    out = {"cores": cores, "blas": blas, "host": platform.processor() or platform.machine(),
+           "os_cpu_count": os.cpu_count()}
+    # KL-lock pass: posterior statistics and lock update of 256 active rows at V = 126464
+    case = W.kl_lock_case(N=640, V=V_KL, B=1, locked_frac=0.6, key=640)
+    z, y = O.widen(case.cur, "bf16"), O.widen(case.prev, "bf16")
+    t0 = time.perf_counter()
+    st = O.posterior_stats(z, y)
+    O.lock_update(case.locked, case.act_idx, case.act_off, 1, case.N, st.kl, st.u, None, EPS_KL, GATE_KL, True)
+    t = (time.perf_counter() - t0) * 1639 / case.M_tot
+    out["kl_lock_pass"] = {"value": round(kl_bytes(1639) / t / 1e9, 3), "unit": "GB/s", "ms": round(t * 1e3, 1),
+                           "sample": "float64 posterior statistics + lock update of %d rows x V=%d (scaled to "
+                                     "M=1639)" % (case.M_tot, V_KL)}
+    del z, y, case
+    # batched ragged step: one layer + final norm + LM head + statistics of the smallest sequence
+    dm = W.LLADA_LAYER
+    Ms = W.ragged_ms(8, 2048, key=8 * 2048)
+    b = int(np.argmin(Ms))
+    od = O.OracleDims(dm.d, dm.n_heads, dm.head_dim, dm.ffn, dm.vocab, dm.rms_eps, dm.rope_theta)
+    Wl = {k: O.widen(v, "bf16") for k, v in W.layer_weights(dm, 0).items()}
+    head = O.widen(W.lm_head_weights(dm), "bf16")
+    lc = W.layer_case(dm, 2048, [Ms[b]], key=5)
+    h = O.widen(lc.h_in, "bf16")[lc.act_idx]
+    K, V = O.widen(lc.k_cache, "bf16")[0], O.widen(lc.v_cache, "bf16")[0]
+    t0 = time.perf_counter()
+    hh = O.layer_forward(h, lc.act_idx, Wl, K, V, od)
+    zz = O.rmsnorm(hh, dm.rms_eps) @ head.T
+    O.posterior_stats(zz, zz)
+    t = (time.perf_counter() - t0) * sum(Ms) / Ms[b]
+    fl = layer_flops(sum(Ms), N=2048) + 2.0 * sum(Ms) * D * V_KL
+    out["batched_step"] = {"value": round(fl / t / 1e12, 4), "unit": "TFLOP/s", "ms": round(t * 1e3, 1),
+                           "sample": "float64 layer + LM head + statistics of one sequence (M_b=%d of 2048), scaled "
+                                     "to the 8-sequence step (sum M_b=%d)" % (Ms[b], sum(Ms))}
+    del Wl, head, hh, zz
+    # tiny sampler loop, whole
+    tdm = W.TINY
+    tod = O.OracleDims(tdm.d, tdm.n_heads, tdm.head_dim, tdm.ffn, tdm.vocab, tdm.rms_eps, tdm.rope_theta)
+    L64 = [{k: O.widen(v, "f32") for k, v in W.layer_weights(tdm, l).items()} for l in range(tdm.n_layers)]
+    om = O.OracleModel(tod, tdm.n_layers, lambda l: L64[l], O.widen(W.embed_weights(tdm), "f32"),
+                       O.widen(W.lm_head_weights(tdm), "f32"))
+    tok0 = W.prompt_tokens(tdm, 1, 64, 16)
+    t0 = time.perf_counter()
+    recs = O.run_loop(om, tok0, 1, 64, 16, 0.05, -1.0, 3)
+    t = time.perf_counter() - t0
+    out["tiny_loop"] = {"value": round(t * 1e3 / 16, 3), "unit": "ms/step", "M_t": [r.M for r in recs],
+                        "sample": "the whole 16-step loop of the tiny model in float64 (the oracle evaluates in "
+                                  "float64 only)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
@@ -541,9 +823,14 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the batched ragged step")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the roofline kernels and a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--profile-attention", action="store_true",
+                    help="only launch the attention at M = 1024 and 256 (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.profile_kernels:
         profile_kernels()
+        return
+    if args.profile_attention:
+        profile_attention()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -552,6 +839,7 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     res = gpu_part(args)
+    peaks = measured_peaks()
     line = {
         "metric": METRIC,
         "value": res["value"],
@@ -575,11 +863,27 @@ def main():
         "ablation_no_kv_cache_ms": res["ablation_no_kv_cache_ms"],
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
+        "measured_peaks": peaks,
+        "cache_layout": cache_layout_study(),
         "batched_step": None if args.no_batched else batched_step(),
+        "tiny_loop": tiny_loop(),
         "e2e_loop": None if args.no_e2e else e2e_loop(runs=SURELOCK_RUNS + ABLATION_RUNS),
         "e2e_loop_b8": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[0], SURELOCK_RUNS[2]), B=8),
-        "cpu_baseline": None if args.no_cpu else cpu_part(args.cpu_seconds),
+        "e2e_loop_captured": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[2],), captured=True),
+        "e2e_loop_b8_captured": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[2],), B=8, captured=True),
+        "cpu_baseline": None,
     }
+    # fractions of the measured ceilings, beside the vendor ones
+    line["roofline"]["frac_of_measured_peak"] = round(line["roofline"]["achieved"] / peaks["mfma_bf16_tflops"], 4)
+    line["roofline"]["measured_peak"] = peaks["mfma_bf16_tflops"]
+    line["roofline_kl"]["frac_of_measured_peak"] = round(line["roofline_kl"]["achieved"] / peaks["hbm_read_gbs"], 4)
+    line["roofline_kl"]["measured_peak"] = peaks["hbm_read_gbs"]
+    for r in line["per_M"]:
+        r["frac_measured_mfma_peak"] = round(r["tflops"] / peaks["mfma_bf16_tflops"], 4)
+    if not args.no_cpu:
+        cb = cpu_part(args.cpu_seconds)
+        cb["per_config"] = cpu_configs()
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

@@ -265,6 +265,13 @@ typedef struct {
   float* gate_thr;       /* [B] or NULL */
   int32_t* lock_step;    /* [B*N] or NULL: step at which each position locked */
   int32_t* m_tot_host;   /* host int32* or NULL: receives M_{t+1} (synchronises) */
+  int32_t* t_dev;        /* device int32 or NULL: step index that lock_step records instead of t;
+                            the step adds one to it when it runs the lock update */
+  int kv_head_major;     /* 0: caches token-major [n_layers][B][N][H][Dh] (a position's K or V row
+                            is one run of d elements); 1: head-major [n_layers][B][H][N][Dh] (a
+                            head's keys are one run of N * Dh elements).  The cache-layout study of
+                            gist.science/nl §5 (optimised cache layouts); sl_attn_active and
+                            sl_cache_scatter take token-major caches. */
 } sl_state;
 
 typedef struct {
@@ -276,6 +283,19 @@ typedef struct {
   int no_kv_cache; /* 0: SureLock (locked positions attended through their cached K/V);
                       1: the notes page's "no KV cache" ablation (消融实验): positions
                       locked before this step are not attended */
+  int device_m;    /* 0: state->M_tot is the active count (as the last compaction left it).
+                      1: the active count stays on the device: every kernel reads act_off[B]
+                      and state->M_tot is only an upper bound on it (any earlier step's count
+                      serves, since A_t only shrinks), which sizes the grids.  A step can then
+                      be enqueued, or captured into a HIP graph and replayed, without the host
+                      reading the count back; launches past the live count exit at once. */
+  int fuse_head_kl; /* 1: the LM head's epilogue also computes, from the logits it stores, each
+                       row's statistics over its column tiles against the previous posterior,
+                       so the vocabulary pass does not read the current logits back (the
+                       pages' fused-kernel direction, gist.science/nl §5); a short merge pass
+                       then finishes the rows.  Used from the second step on (a previous
+                       posterior must exist); same results as 0 up to the order of the fp32
+                       additions. */
 } sl_step_params;
 
 /*
@@ -313,6 +333,21 @@ size_t sl_step_workspace_size(const sl_model* model, int B, int N, int M_tot);
 /* The smallest workspace sl_step accepts for every step with at most M_tot active
  * rows: the fixed buffers only (split-K residual projections then use fp32 atomics). */
 size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot);
+
+/*
+ * Measurement helpers (not part of the SureLock step): the ceilings this chip sustains, which
+ * the step's roofline fractions are reported against beside the vendor figures.
+ * sl_peak_mfma       `workgroups` x 4 waves, each running `iters` rounds of 4 independent
+ *                    v_mfma_f32_32x32x16_bf16 on register operands; sl_peak_mfma_flops gives
+ *                    the FLOPs of such a launch.  sink: device float[256], never written in
+ *                    practice (it keeps the work alive).
+ * sl_peak_stream     streams `bytes` (a multiple of 16) from src with 16-byte non-temporal loads,
+ *                    each workgroup over one contiguous range; dst != NULL: copies them there,
+ *                    dst == NULL: only reads.  sink as above.
+ */
+sl_status sl_peak_mfma(int workgroups, int iters, float* sink, sl_stream stream);
+double sl_peak_mfma_flops(int workgroups, int iters);
+sl_status sl_peak_stream(const void* src, void* dst, size_t bytes, int workgroups, float* sink, sl_stream stream);
 
 #ifdef __cplusplus
 }

@@ -518,10 +518,12 @@ def _step_compare(st, ost_before, out, dm, B, N, eps, gate_q, tol_logit):
 # lock rules: SureLock (KL test, gate off); the notes page's ablations (消融实验): confidence gate
 # only (eps = +inf, gate at the median) and no KV cache (locked positions not attended)
 LOOP_RULES = {"surelock": (0.05, -1.0, False), "gate_only": (math.inf, 0.5, False), "no_kv_cache": (0.05, -1.0, True)}
+# the same loops with the vocabulary statistics computed in the LM head's epilogue
+FUSED_RULES = {"surelock": True, "gate_only": True, "no_kv_cache": False}
 
 
-@pytest.mark.parametrize("rule", list(LOOP_RULES))
-def test_tiny_loop_teacher_forced(rule):
+@pytest.mark.parametrize("rule,fuse", [(r, f) for r in LOOP_RULES for f in ((False, True) if FUSED_RULES[r] else (False,))])
+def test_tiny_loop_teacher_forced(rule, fuse):
     """2-layer fp32 model, d=128, 4x32 heads, FFN 384, V=512, N=64 (16 prompt + 48 masked),
     16 steps, 3 unmasks per step; eps=0.05 with the gate off, or one of the ablations."""
     sl = _sl()
@@ -548,7 +550,7 @@ def test_tiny_loop_teacher_forced(rule):
         tok_o = ost.tok.copy()
         O.sampler_unmask(ost.tok, ost.cand, out.act_idx, out.act_off, N, out.stats.argmax, out.stats.conf,
                          dm.mask_id, 3)
-        p = sl.surelock.sl_step_params(eps, gate, dm.mask_id, 1, 3, int(no_kv))
+        p = sl.surelock.sl_step_params(eps, gate, dm.mask_id, 1, 3, int(no_kv), 0, int(fuse))
         sl.sl_step(model.s, st.struct(), p, st.ws)
         torch.cuda.synchronize()
         total_mismatch += _step_compare(st, None, out, dm, B, N, eps, gate, 1e-4)
@@ -691,7 +693,8 @@ def test_tiny_loop_is_deterministic():
     # one sequence fully locked (no active row) between two active ones
     (W.Dims(n_layers=1, d=256, n_heads=2, head_dim=128, ffn=512, vocab=1024, dtype="bf16"), 3, 128, 0.5, [40, 0, 100]),
 ])
-def test_batched_ragged_step(dm, B, N, gate, ms):
+@pytest.mark.parametrize("fuse", [False, True])
+def test_batched_ragged_step(dm, B, N, gate, ms, fuse):
     sl = _sl()
     say("batched step", B, N, gate, ms)
     eps = 0.05
@@ -730,7 +733,7 @@ def test_batched_ragged_step(dm, B, N, gate, ms):
                         k_cache=kc, v_cache=vc)
     st.logits[0].copy_(dev(prev_st, dm.dtype))     # buffer (t+1)%2 = 0 holds p_{t-1} at t = 1
     st.t = 1
-    p = sl.surelock.sl_step_params(eps, gate, -1, 1, 0)
+    p = sl.surelock.sl_step_params(eps, gate, -1, 1, 0, 0, 0, int(fuse))
     sl.sl_step(model.s, st.struct(), p, st.ws)
     torch.cuda.synchronize()
     st.M_tot = st.m_host.value
@@ -829,3 +832,20 @@ def test_batched_step_full_shape_with_head():
                       stg, lr, locked, case.act_idx, case.act_off, B, N, eps, gate, True)
     say("lock decisions: gpu %d, oracle on the GPU's logits %d (exempt differences %d), oracle on its own "
         "logits %d" % (int(g_locked.sum() - locked.sum()), int(lr.new_lock.sum()), nd, int(lr_own.new_lock.sum())))
+    # the same step with the vocabulary statistics computed in the LM head's epilogue: the same logits,
+    # and the same comparison with the oracle's gate / lock / compaction on those logits
+    cur_t = st.logits[1].index_select(0, gi).clone()
+    st.locked.copy_(torch.from_numpy(locked).cuda())
+    st.M_tot = sl.sl_compact(st.locked, B, N, st.act_idx, st.act_off, st.m_host)
+    st.logits[1].zero_()
+    st.t = 1
+    st.step(eps, gate, -1, True, 0, fuse_head_kl=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st.logits[1].index_select(0, gi), cur_t)
+    g_locked_f = st.locked.cpu().numpy()
+    ndf = compare_lock(dict(kl=st.kl[:M].cpu().numpy(), u=st.u[:M].cpu().numpy(), lse=st.lse[:M].cpu().numpy(),
+                            gate_thr=st.gate_thr.cpu().numpy(), locked=g_locked_f, act_idx=st.act_idx.cpu().numpy(),
+                            act_off=st.act_off.cpu().numpy(), M=int(st.act_off[B].item())),
+                       stg, lr, locked, case.act_idx, case.act_off, B, N, eps, gate, True)
+    say("fused LM head + statistics: locks %d (exempt differences from the oracle %d); unfused and fused masks "
+        "differ at %d positions" % (int(g_locked_f.sum() - locked.sum()), ndf, int((g_locked_f != g_locked).sum())))

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsurelock.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["abi.hip", "kl_lock.hip", "attn.hip", "gemm.hip", "rows.hip"]
+SOURCES = ["abi.hip", "kl_lock.hip", "attn.hip", "gemm.hip", "rows.hip", "peak.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -41,6 +41,14 @@ sl_status hip_check(hipError_t e, const char* what) {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline int elem_bytes(int dtype) { return dtype == SL_BF16 ? 2 : 4; }
 
+// Column tiles of the LM head's plan at M rows when it also computes the row statistics
+// (EPI_LOGITS_KL): one stored partial per (tile, row).
+int head_kl_tiles(const sl_model* m, int M) {
+  int bm = 0, bn = 0, sp = 0;
+  sl::gemm_plan(m->dtype, sl::EPI_LOGITS_KL, M > 0 ? M : 1, m->d, m->vocab, &bm, &bn, &sp, nullptr);
+  return bn > 0 ? m->vocab / bn : 0;
+}
+
 // Workspace layout of sl_step (contents need no initialisation).
 struct StepLayout {
   size_t kl_part, h32, x, q, o, act, attn, total;
@@ -48,7 +56,13 @@ struct StepLayout {
     const int eb = elem_bytes(m->dtype);
     const size_t M = (size_t)(M_tot > 0 ? M_tot : 1);
     size_t off = 0;
-    kl_part = off; off += align256(m->lm_head ? sl::kl_part_bytes(M_tot, m->vocab, eb) : 256);
+    // the vocabulary pass's partials, or the fused LM head's per-tile row statistics
+    size_t klb = m->lm_head ? sl::kl_part_bytes(M_tot, m->vocab, eb) : 256;
+    if (m->lm_head) {
+      const size_t fused = M * (size_t)head_kl_tiles(m, M_tot) * sl::kKlPartBytes;
+      if (fused > klb) klb = fused;
+    }
+    kl_part = off; off += align256(klb);
     h32 = off; off += align256(M * m->d * 4);
     x = off; off += align256(M * m->d * eb);
     q = off; off += align256(M * m->d * eb);
@@ -368,6 +382,8 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
              "M_tot = %d active rows exceed the GEMMs' 4 GiB A operand", M);
   const bool head = m->lm_head != nullptr;
   const bool lock = head && p->do_lock;
+  // the LM head computes the vocabulary statistics in its epilogue (needs a previous posterior)
+  const bool fuse = lock && p->fuse_head_kl && st->t > 0 && head_kl_tiles(m, M) > 0;
   if (head) SL_REQUIRE(st->logits[0] && st->logits[1], SL_ERR_INVALID, "logits buffers missing");
   if (lock) {
     SL_REQUIRE(st->kl && st->u && st->lse, SL_ERR_INVALID, "kl / u / lse missing");
@@ -399,10 +415,12 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
   const float scale = 1.f / sqrtf((float)Dh);
   // no-KV-cache ablation: the positions locked before this step are not attended
   const uint8_t* key_excl = p->no_kv_cache ? st->locked : nullptr;
+  // device-resident row count: M is then a capacity, every kernel reads the live count act_off[B]
+  const int32_t* m_dev = p->device_m ? st->act_off + B : nullptr;
 
   if (M > 0) {
     SL_TRY(sl::launch_gather_norm(dt, st->h_in, m->embed, st->tok, st->act_idx, st->act_off, B, N, M, d,
-                                  m->rms_eps, h32, x, s),
+                                  m->rms_eps, h32, x, s, m_dev),
            "gather");
     for (int l = 0; l < m->n_layers; ++l) {
       const sl_layer_weights& W = m->layers[l];
@@ -411,11 +429,14 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       sl::GemmArgs g{};
       g.act_idx = st->act_idx; g.act_off = st->act_off; g.B = B; g.N = N; g.M = M; g.d = d; g.Dh = Dh;
       g.split_k = 1;
+      g.m_dev = m_dev;
+      g.kv_hm = st->kv_head_major ? 1 : 0;
       // QKV + RoPE + K/V scatter into the layer cache
       g.A = x; g.K = d; g.Nv = 3 * d; g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
       g.out0 = q; g.out1 = kc; g.out2 = vc; g.rope = m->rope;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_QKV, g, s), "qkv gemm");
-      SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, key_excl, B, N, M, H, Dh, scale, o, attn_ws, s),
+      SL_TRY(sl::launch_attn(dt, q, kc, vc, st->act_off, key_excl, B, N, M, H, Dh, scale, o, attn_ws, s, m_dev,
+                             st->kv_head_major ? 1 : 0),
              "attention");
       // O projection + residual, then the pre-FFN RMSNorm (fused with the partial sums' reduce
       // when the projection is split over K)
@@ -423,9 +444,9 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       g.A = o; g.K = d; g.Nv = d; g.w0 = W.wo; g.w1 = g.w2 = nullptr; g.out0 = h32; g.part = part;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "o gemm");
       if (part && ns > 1)
-        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, x, s), "residual + norm");
+        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, x, s, m_dev), "residual + norm");
       else
-        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s), "norm");
+        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, x, s, m_dev), "norm");
       // SwiGLU FFN + residual, then the next block's RMSNorm (none after the last layer without a head)
       g.A = x; g.K = d; g.Nv = 2 * F; g.w0 = W.wg; g.w1 = W.wu; g.out0 = act; g.part = nullptr;
       SL_TRY(sl::launch_gemm(dt, sl::EPI_SWIGLU, g, s), "gate/up gemm");
@@ -433,16 +454,22 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
       SL_TRY(sl::launch_gemm(dt, sl::EPI_RESID, g, s, &ns), "down gemm");
       void* xn = (head || l + 1 < m->n_layers) ? x : nullptr;
       if (part && ns > 1)
-        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, xn, s), "residual + norm");
+        SL_TRY(sl::launch_resid_norm(dt, part, ns, h32, M, d, m->rms_eps, xn, s, m_dev), "residual + norm");
       else if (xn)
-        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, xn, s), "norm");
+        SL_TRY(sl::launch_norm(dt, h32, M, d, m->rms_eps, xn, s, m_dev), "norm");
     }
     if (head) {
       sl::GemmArgs g{};
       g.act_idx = st->act_idx; g.act_off = st->act_off; g.B = B; g.N = N; g.M = M; g.d = d; g.Dh = Dh;
       g.split_k = 1;
+      g.m_dev = m_dev;
       g.A = x; g.K = d; g.Nv = m->vocab; g.w0 = m->lm_head; g.out0 = st->logits[st->t & 1];
-      SL_TRY(sl::launch_gemm(dt, sl::EPI_LOGITS, g, s), "lm head gemm");
+      if (fuse) {
+        g.prev = st->logits[(st->t + 1) & 1];
+        g.klp = (float*)(w + L.kl_part);
+        g.mask_id = p->mask_id;
+      }
+      SL_TRY(sl::launch_gemm(dt, fuse ? sl::EPI_LOGITS_KL : sl::EPI_LOGITS, g, s), "lm head gemm");
     }
   }
   if (lock) {
@@ -450,13 +477,18 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
                        st->lse, st->argmax, st->conf};
     sl::TailParams tp{};
     tp.B = B; tp.N = N; tp.M_tot = M;
+    tp.m_dev = m_dev; tp.t_dev = st->t_dev;
     tp.eps = p->eps; tp.gate_q = p->gate_q; tp.mask_id = p->mask_id; tp.have_prev = st->t > 0; tp.t = st->t;
     tp.act_idx = st->act_idx; tp.act_off = st->act_off; tp.cand = st->cand; tp.locked = st->locked;
     tp.lock_step = st->lock_step; tp.kl = st->kl; tp.u = st->u; tp.conf = st->conf; tp.argmax = st->argmax;
     tp.gate_thr = st->gate_thr; tp.tok = st->tok; tp.cand_out = st->cand;
     tp.unmask_k = p->unmask_k > 0 ? p->unmask_k : 0;
     tp.new_act_idx = st->act_idx; tp.new_act_off = st->act_off;
-    SL_TRY(sl::launch_kl_lock(dt, rp, tp, (float*)(w + L.kl_part), s), "kl lock");
+    if (fuse)
+      SL_TRY(sl::launch_kl_merge_tail(dt, rp, tp, (const float*)(w + L.kl_part), head_kl_tiles(m, M), s),
+             "kl merge + lock");
+    else
+      SL_TRY(sl::launch_kl_lock(dt, rp, tp, (float*)(w + L.kl_part), s), "kl lock");
     if (st->m_tot_host) {
       SL_TRY(hipMemcpyAsync(st->m_tot_host, st->act_off + B, 4, hipMemcpyDeviceToHost, s), "M copy");
       SL_TRY(hipStreamSynchronize(s), "M sync");

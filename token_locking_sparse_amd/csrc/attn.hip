@@ -86,7 +86,7 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
             const int32_t* __restrict__ act_off, const uint8_t* __restrict__ key_excl, int B, int N, int H,
             float scale_log2,
             int nsplit, int tiles_per_split, T* __restrict__ out, float* __restrict__ part_o,
-            float* __restrict__ part_ml, int M_tot) {
+            float* __restrict__ part_ml, int M_tot, int kv_hm) {
   using C = AttnCfg<T, Dh>;
   constexpr int E = C::E;
   __shared__ __attribute__((aligned(16))) char smem[C::Smem];
@@ -125,9 +125,12 @@ attn_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restri
     for (int kk = 0; kk < C::nKK; ++kk) qf[kk] = ld16(qr + (2 * kk + hl) * 16);
   }
 
-  const char* kbase = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
-  const char* vbase = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
-  const size_t krow_stride = (size_t)HD * sizeof(T);
+  // token-major cache [B][N][H][Dh]: a head's key rows are Dh-element slices HD apart;
+  // head-major [B][H][N][Dh]: they are contiguous
+  const size_t kv0 = kv_hm ? ((size_t)b * H + h) * N * Dh : ((size_t)b * N * H + h) * Dh;
+  const char* kbase = (const char*)(kc + kv0);
+  const char* vbase = (const char*)(vc + kv0);
+  const size_t krow_stride = (size_t)(kv_hm ? Dh : HD) * sizeof(T);
   const uint8_t* excl_row = EXCL ? key_excl + (size_t)b * N : nullptr;
 
   u32x4 kreg[C::KLoads];
@@ -404,7 +407,7 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
                const int32_t* __restrict__ act_off, const uint8_t* __restrict__ key_excl, int B, int N, int H,
                float scale_log2, int nsplit,
                int tiles_per_split, bf16* __restrict__ out, float* __restrict__ part_o,
-               float* __restrict__ part_ml, int M_tot) {
+               float* __restrict__ part_ml, int M_tot, int kv_hm) {
   using C = TrCfg<QW, G, BKV>;
   constexpr int Dh = kTrDh, E = 8, nKK = Dh / 16;
   __shared__ __attribute__((aligned(1024))) char smem[C::kSmem];
@@ -442,9 +445,11 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
 
   // direct-load sources: load j of wave wq of a group fills LDS bytes [(QW j + wq) KB, +1 KB)
   // of its tile = key rows 4 (QW j + wq) + lane / 16, stored position lane % 16
-  const size_t krow = (size_t)HD * 2;
-  const char* kb0 = (const char*)(kc + ((size_t)b * N * H + h) * Dh);
-  const char* vb0 = (const char*)(vc + ((size_t)b * N * H + h) * Dh);
+  // key row stride and the head's first row: token-major [B][N][H][Dh] or head-major [B][H][N][Dh]
+  const size_t krow = (size_t)(kv_hm ? Dh : HD) * 2;
+  const size_t kv0 = kv_hm ? ((size_t)b * H + h) * N * Dh : ((size_t)b * N * H + h) * Dh;
+  const char* kb0 = (const char*)(kc + kv0);
+  const char* vb0 = (const char*)(vc + kv0);
   uint32_t koff[C::kDma], voff[C::kDma];
 #pragma unroll
   for (int j = 0; j < C::kDma; ++j) {
@@ -662,10 +667,10 @@ constexpr int kCombineBatch = 8;
 template <typename T, int Dh>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit,
-                    int M_tot, int H, T* __restrict__ out) {
+                    int M_tot, int H, T* __restrict__ out, const int32_t* __restrict__ m_dev) {
   constexpr int PER = (Dh + 63) / 64;   // output elements per lane
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (w >= M_tot * H) return;
+  if (w >= rows_live(M_tot, m_dev) * H) return;   // M_tot: capacity and stride of the partials
   const int m = w / H, h = w % H;
   const size_t stride_ml = (size_t)M_tot * H * 2, stride_o = (size_t)M_tot * H * Dh;
   const float* ml0 = part_ml + ((size_t)m * H + h) * 2;
@@ -760,7 +765,7 @@ size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh) {
 template <typename T, int Dh, bool EXCL>
 static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, const int32_t* act_off,
                                 const uint8_t* key_excl, int B, int N, int M_tot, int H, float scale, void* out,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, const int32_t* m_dev, int kv_hm) {
   const bool tr = sizeof(T) == 2 && Dh == kTrDh;
   const AttnPlan p = attn_plan(B, N, M_tot, H, tr);
   const int nsplit = p.nsplit, tps = p.tps;
@@ -771,18 +776,18 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
   if (tr && p.shape == 0)
     hipLaunchKernelGGL((attn_tr_kernel<4, 2, 64, EXCL>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
                        (const bf16*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml,
-                       M_tot);
+                       M_tot, kv_hm);
   else if (tr)
     hipLaunchKernelGGL((attn_tr_kernel<2, 4, 32, EXCL>), grid, dim3(512), 0, s, (const bf16*)q, (const bf16*)kc,
                        (const bf16*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (bf16*)out, part_o, part_ml,
-                       M_tot);
+                       M_tot, kv_hm);
   else
     hipLaunchKernelGGL((attn_kernel<T, Dh, EXCL>), grid, dim3(kAttnThreads), 0, s, (const T*)q, (const T*)kc,
-                       (const T*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (T*)out, part_o, part_ml, M_tot);
+                       (const T*)vc, act_off, key_excl, B, N, H, sl2, nsplit, tps, (T*)out, part_o, part_ml, M_tot, kv_hm);
   if (nsplit > 1) {
     const int waves = M_tot * H;
     hipLaunchKernelGGL((attn_combine_kernel<T, Dh>), dim3((waves + 3) / 4), dim3(256), 0, s, part_o,
-                       part_ml, nsplit, M_tot, H, (T*)out);
+                       part_ml, nsplit, M_tot, H, (T*)out, m_dev);
   }
   return hipGetLastError();
 }
@@ -790,23 +795,25 @@ static hipError_t attn_launch_t(const void* q, const void* kc, const void* vc, c
 template <typename T, int Dh>
 static hipError_t attn_launch_excl(const void* q, const void* kc, const void* vc, const int32_t* act_off,
                                    const uint8_t* key_excl, int B, int N, int M_tot, int H, float scale, void* out,
-                                   void* ws, hipStream_t s) {
-  return key_excl ? attn_launch_t<T, Dh, true>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s)
-                  : attn_launch_t<T, Dh, false>(q, kc, vc, act_off, nullptr, B, N, M_tot, H, scale, out, ws, s);
+                                   void* ws, hipStream_t s, const int32_t* m_dev, int kv_hm) {
+  return key_excl ? attn_launch_t<T, Dh, true>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev,
+                                               kv_hm)
+                  : attn_launch_t<T, Dh, false>(q, kc, vc, act_off, nullptr, B, N, M_tot, H, scale, out, ws, s,
+                                                m_dev, kv_hm);
 }
 
 hipError_t launch_attn(int dtype, const void* q, const void* kc, const void* vc,
                        const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H, int Dh,
-                       float scale, void* out, void* ws, hipStream_t s) {
+                       float scale, void* out, void* ws, hipStream_t s, const int32_t* m_dev, int kv_hm) {
   if (M_tot <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (Dh == 128) return attn_launch_excl<bf16, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 64) return attn_launch_excl<bf16, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 32) return attn_launch_excl<bf16, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 128) return attn_launch_excl<bf16, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
+    if (Dh == 64) return attn_launch_excl<bf16, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
+    if (Dh == 32) return attn_launch_excl<bf16, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
   } else {
-    if (Dh == 128) return attn_launch_excl<float, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 64) return attn_launch_excl<float, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
-    if (Dh == 32) return attn_launch_excl<float, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s);
+    if (Dh == 128) return attn_launch_excl<float, 128>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
+    if (Dh == 64) return attn_launch_excl<float, 64>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
+    if (Dh == 32) return attn_launch_excl<float, 32>(q, kc, vc, act_off, key_excl, B, N, M_tot, H, scale, out, ws, s, m_dev, kv_hm);
   }
   return hipErrorInvalidValue;
 }

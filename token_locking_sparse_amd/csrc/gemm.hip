@@ -9,7 +9,10 @@
 //              the layer's cache rows b*N + pos (locked rows untouched);
 //   EPI_RESID  h += C in the fp32 residual stream (atomic when split over K);
 //   EPI_SWIGLU SiLU(gate) * up;
-//   EPI_LOGITS logits written to rows b*N + pos of the posterior buffer.
+//   EPI_LOGITS logits written to rows b*N + pos of the posterior buffer;
+//   EPI_LOGITS_KL the same, plus each row's posterior statistics over the tile's
+//              columns against the previous posterior (the vocabulary pass done
+//              in place, so the logits are not read back).
 // Paired epilogues (RoPE halves, gate/up) use a "pair layout": in every wave's
 // N-range the first half of the columns holds the first element of each pair
 // and the second half its partner, so both land in the same lane and register.
@@ -19,6 +22,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "klpart.hpp"
 
 namespace sl {
 
@@ -111,6 +115,26 @@ __device__ __forceinline__ void store8(T* dst, const float* y) {
   }
 }
 
+// 8 consecutive elements of the storage type as floats.
+template <typename T>
+__device__ __forceinline__ void load8(const T* src, float* y) {
+  if (sizeof(T) == 2) {
+    Chunk<bf16>::unpack(ld16(src), y);
+  } else {
+    Chunk<float>::unpack(ld16(src), y);
+    Chunk<float>::unpack(ld16((const float*)src + 4), y + 4);
+  }
+}
+
+// A partial from lane (l ^ o).
+__device__ __forceinline__ Part shfl_xor_part(const Part& p, int o) {
+  Part q;
+  q.ma = __shfl_xor(p.ma, o, 64); q.sa = __shfl_xor(p.sa, o, 64); q.ta = __shfl_xor(p.ta, o, 64);
+  q.mb = __shfl_xor(p.mb, o, 64); q.sb = __shfl_xor(p.sb, o, 64);
+  q.best = __shfl_xor(p.best, o, 64); q.bidx = __shfl_xor(p.bidx, o, 64);
+  return q;
+}
+
 __device__ __forceinline__ void lds8(const float* p, float* y) {
   const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
 #pragma unroll
@@ -121,7 +145,7 @@ __device__ __forceinline__ void lds8(const float* p, float* y) {
 // Paired epilogues: output pair p of the tile takes its first element from
 // tile column (p / (TN/2)) * TN + p % (TN/2) and its partner TN/2 further.
 template <typename T, int EPI, int BN, int TN, int LDW, int PR, int NT>
-__device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int mrow0, int n0) {
+__device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int mrow0, int n0, int Mr) {
   const int tid = threadIdx.x;
   if (EPI == EPI_RESID) {
     if (a.split_k > 1 && a.part) {
@@ -131,33 +155,75 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       for (int id = tid; id < PR * CPR; id += NT) {
         const int r = id / CPR, c = (id % CPR) * 4;
         const int m = mrow0 + r;
-        if (m < a.M) *(f32x4*)(plane + (size_t)m * a.Nv + n0 + c) = *(const f32x4*)(tile + r * LDW + c);
+        if (m < Mr) *(f32x4*)(plane + (size_t)m * a.Nv + n0 + c) = *(const f32x4*)(tile + r * LDW + c);
       }
     } else if (a.split_k > 1) {
       // fp32 atomics, consecutive lanes on consecutive floats of a row
       for (int id = tid; id < PR * BN; id += NT) {
         const int r = id / BN, c = id % BN;
         const int m = mrow0 + r;
-        if (m < a.M) unsafeAtomicAdd((float*)a.out0 + (size_t)m * a.Nv + n0 + c, tile[r * LDW + c]);
+        if (m < Mr) unsafeAtomicAdd((float*)a.out0 + (size_t)m * a.Nv + n0 + c, tile[r * LDW + c]);
       }
     } else {
       constexpr int CPR = BN / 4;
       for (int id = tid; id < PR * CPR; id += NT) {
         const int r = id / CPR, c = (id % CPR) * 4;
         const int m = mrow0 + r;
-        if (m >= a.M) continue;
+        if (m >= Mr) continue;
         float* h = (float*)a.out0 + (size_t)m * a.Nv + n0 + c;
         f32x4 y = *(const f32x4*)h;
         y += *(const f32x4*)(tile + r * LDW + c);
         *(f32x4*)h = y;
       }
     }
+  } else if (EPI == EPI_LOGITS_KL) {
+    // The logits as EPI_LOGITS, then, from the stored values a (rounded to the storage type, as a
+    // later pass would read them) and the previous posterior's b, each row's statistics over this
+    // tile's BN columns: max a, sum e^(a - max a), sum e^(a - max a) (a - b), max b, sum e^(b - max b),
+    // and the largest a other than the [MASK] id with its lowest id.  A row's CPR chunks sit on CPR
+    // consecutive lanes (ids are consecutive, CPR divides 64), combined by lane shuffles.
+    constexpr int CPR = BN / 8;
+    static_assert(EPI != EPI_LOGITS_KL || CPR == 8 || CPR == 16 || CPR == 32, "fused statistics need BN in {64, 128, 256}");
+    const int vt = n0 / BN;
+    for (int id = tid; id < PR * CPR; id += NT) {
+      const int r = id / CPR, c = (id % CPR) * 8;
+      const int m = mrow0 + r;
+      if (m >= Mr) continue;   // uniform over the row's lanes
+      const int b = seq_of_row(a.act_off, a.B, m);
+      const size_t g = (size_t)b * a.N + a.act_idx[m];
+      float y[8], bv[8];
+      lds8(tile + r * LDW + c, y);
+      store8<T>((T*)a.out0 + g * a.Nv + n0 + c, y);
+      load8<T>((const T*)a.prev + g * a.Nv + n0 + c, bv);
+      if (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (float)(bf16)y[i];
+      }
+      Part p = empty_part();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p.ma = fmaxf(p.ma, y[i]);
+        p.mb = fmaxf(p.mb, bv[i]);
+        if (y[i] > p.best && n0 + c + i != a.mask_id) { p.best = y[i]; p.bidx = n0 + c + i; }
+      }
+      const float mal = p.ma * kLog2e, mbl = p.mb * kLog2e;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(y[i], kLog2e, -mal));
+        p.sa += e;
+        p.ta = fmaf(e, y[i] - bv[i], p.ta);
+        p.sb += __builtin_amdgcn_exp2f(fmaf(bv[i], kLog2e, -mbl));
+      }
+#pragma unroll
+      for (int o = CPR / 2; o >= 1; o >>= 1) p = combine(p, shfl_xor_part(p, o));
+      if (id % CPR == 0) store_part(a.klp + ((size_t)vt * a.M + m) * kPartWords, p);
+    }
   } else if (EPI == EPI_LOGITS) {
     constexpr int CPR = BN / 8;
     for (int id = tid; id < PR * CPR; id += NT) {
       const int r = id / CPR, c = (id % CPR) * 8;
       const int m = mrow0 + r;
-      if (m >= a.M) continue;
+      if (m >= Mr) continue;
       const int b = seq_of_row(a.act_off, a.B, m);
       const size_t g = (size_t)b * a.N + a.act_idx[m];
       float y[8];
@@ -169,7 +235,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     for (int id = tid; id < PR * CPR; id += NT) {
       const int r = id / CPR, p0 = (id % CPR) * 8;
       const int m = mrow0 + r;
-      if (m >= a.M) continue;
+      if (m >= Mr) continue;
       const int c1 = (p0 / (TN / 2)) * TN + p0 % (TN / 2);
       float x1[8], x2[8];
       lds8(tile + r * LDW + c1, x1);
@@ -203,14 +269,20 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
           }
         }
         T* dst;
+        int c0 = col;
         if (mat == 0) {
           dst = (T*)a.out0 + (size_t)m * a.d;
+        } else if (a.kv_hm) {   // head-major cache: this head's row of Dh elements at (b, h, pos)
+          const int b = seq_of_row(a.act_off, a.B, m);
+          const int H = a.d / a.Dh, hd = col / a.Dh;
+          dst = (T*)(mat == 1 ? a.out1 : a.out2) + (((size_t)b * H + hd) * a.N + pos) * a.Dh;
+          c0 = col - hd * a.Dh;
         } else {
           const int b = seq_of_row(a.act_off, a.B, m);
           dst = (T*)(mat == 1 ? a.out1 : a.out2) + ((size_t)b * a.N + pos) * a.d;
         }
-        store8<T>(dst + col, x1);
-        store8<T>(dst + col + hh, x2);
+        store8<T>(dst + c0, x1);
+        store8<T>(dst + c0 + hh, x2);
       }
     }
   }
@@ -258,6 +330,8 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   if ((nb & 7) == 0) lid = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   const int bm = lid % MT, bn = lid / MT;
   const int m0 = bm * BM, n0 = bn * BN;
+  const int Mr = rows_live(a.M, a.m_dev);   // rows to compute (a.M is their capacity and plane stride)
+  if (m0 >= Mr) return;                     // uniform over the workgroup, before any barrier
   const int split = blockIdx.z;
   const int KI = a.K * (int)sizeof(T) / RB;
   const int kt0 = split * k_iters_per_split;
@@ -273,7 +347,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
 #pragma unroll
   for (int i = 0; i < C::ADma; ++i) {
     const int r = (i * C::NW + wid) * (1024 / RB) + lrow;
-    aoff[i] = (uint32_t)((size_t)min(m0 + r, a.M - 1) * arb) + swz<RB>(r, lpos) * 16;
+    aoff[i] = (uint32_t)((size_t)min(m0 + r, Mr - 1) * arb) + swz<RB>(r, lpos) * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::BDma; ++i) {
@@ -430,7 +504,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
           tile[(rb + (v >> 2) * 8 + 4 * hl + (v & 3)) * LDW + wn * C::TN + j * 32 + l32] = acc[i][j][v];
     }
     __syncthreads();
-    epilogue_pass<T, EPI, BN, C::TN, LDW, PR, C::NT>(a, tile, m0 + r_lo, n0);
+    epilogue_pass<T, EPI, BN, C::TN, LDW, PR, C::NT>(a, tile, m0 + r_lo, n0, Mr);
     __syncthreads();
   }
 }
@@ -456,6 +530,12 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
     case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID, VB>), grid, block, 0, s, b, MT, NT, kps); break;
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_SWIGLU, VB>), grid, block, 0, s, b, MT, NT, kps); break;
     case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS, VB>), grid, block, 0, s, b, MT, NT, kps); break;
+    case EPI_LOGITS_KL:
+      if constexpr (BN == 64 || BN == 128 || BN == 256)
+        hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS_KL, VB>), grid, block, 0, s, b, MT, NT, kps);
+      else
+        return hipErrorInvalidValue;
+      break;
   }
   return hipGetLastError();
 }
@@ -528,6 +608,7 @@ static void pick_cfg(const GemmArgs& a, EpiKind epi, int eb, bool part, int& cfg
     const TileCfg& g = kCfgs[c];
     if (a.Nv % g.BN || (a.K * eb) % g.RB) continue;
     if (g.vb && eb != 2) continue;   // the register path is calibrated for bf16 only
+    if (epi == EPI_LOGITS_KL && g.BN != 64 && g.BN != 128 && g.BN != 256) continue;   // lane groups of a row
     const int KI = a.K * eb / g.RB;
     for (int sp = 1; sp <= 8; sp *= 2) {
       if (sp > 1 && (epi != EPI_RESID || KI / sp < 8 || g.vb)) break;   // the register path streams whole K

@@ -7,9 +7,21 @@
 
 namespace sl {
 
+// Device-resident row count.  Every launcher below takes the row count M_tot
+// from the host; when m_dev is given, M_tot is only a capacity (an upper bound
+// that sizes grids, workspaces and strides) and the kernels process the first
+// min(M_tot, *m_dev) rows, reading the count from device memory.  A step can
+// then be launched, or captured in a graph, without the host knowing how many
+// rows the previous step left active.
+__device__ __forceinline__ int rows_live(int M_cap, const int32_t* m_dev) {
+  return m_dev ? min(M_cap, *m_dev) : M_cap;
+}
+
 // Parameters of the lock / sampler tail that runs after the vocabulary pass.
 struct TailParams {
   int B, N, M_tot;
+  const int32_t* m_dev;  // device row count (M_tot is then a capacity), or NULL
+  int32_t* t_dev;        // device step index for lock_step, advanced after the step, or NULL (use t)
   float eps, gate_q;
   int mask_id, have_prev;
   int t;                 // step index recorded in lock_step
@@ -43,9 +55,14 @@ struct KLRowParams {
 
 // Workspace of the vocabulary pass: per-segment partials of split rows.
 size_t kl_part_bytes(int M_tot, int V, int elem_bytes);
+constexpr int kKlPartBytes = 32;   // one stored row partial (8 words)
 hipError_t launch_compact(const uint8_t* locked, int B, int N, int32_t* act_idx, int32_t* act_off,
                           hipStream_t s);
 hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s);
+// The vocabulary pass when the LM head produced its statistics (EPI_LOGITS_KL): merge the n_vt
+// column-tile partials of every row (klp as GemmArgs::klp, stride tp.M_tot), then the tail.
+hipError_t launch_kl_merge_tail(int dtype, const KLRowParams& rp, const TailParams& tp, const float* klp, int n_vt,
+                                hipStream_t s);
 
 hipError_t launch_cache_scatter(int dtype, void* kc, void* vc, const void* kn, const void* vn,
                                 const int32_t* act_idx, const int32_t* act_off, int B, int N,
@@ -55,24 +72,26 @@ size_t attn_ws_bytes(int B, int N, int M_tot, int H, int Dh);
 // key_excl: [B*N] flags or NULL; nonzero = that position is not attended.
 hipError_t launch_attn(int dtype, const void* q, const void* kc, const void* vc,
                        const int32_t* act_off, const uint8_t* key_excl, int B, int N, int M_tot, int H, int Dh,
-                       float scale, void* out, void* ws, hipStream_t s);
+                       float scale, void* out, void* ws, hipStream_t s, const int32_t* m_dev = nullptr,
+                       int kv_hm = 0);   // kv_hm: caches head-major [B][H][N][Dh] instead of [B][N][H][Dh]
 
 hipError_t launch_rope_table(int n_pos, int Dh, float theta, float* table, hipStream_t s);
 
 // Row gather / RMSNorm.
 hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, const int32_t* tok,
                               const int32_t* act_idx, const int32_t* act_off, int B, int N,
-                              int M_tot, int d, float eps, float* h32, void* x, hipStream_t s);
+                              int M_tot, int d, float eps, float* h32, void* x, hipStream_t s,
+                              const int32_t* m_dev = nullptr);
 // Split-K residual: h32 += the nsplit partial planes of part, then x = RMSNorm(h32) in the
 // storage type (x NULL: no norm).  d % 4 == 0, d <= kResidMaxD, 2 <= nsplit <= 8.
 constexpr int kResidMaxD = 4096;
 hipError_t launch_resid_norm(int dtype, const float* part, int nsplit, float* h32, int M_tot, int d, float eps,
-                             void* x, hipStream_t s);
+                             void* x, hipStream_t s, const int32_t* m_dev = nullptr);
 hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x,
-                       hipStream_t s);
+                       hipStream_t s, const int32_t* m_dev = nullptr);
 
 // GEMM family: C[m][n] = sum_k A[m][k] * W[n][k] with fused epilogues.
-enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_LOGITS_KL = 4 };
 struct GemmArgs {
   const void* A;       // [M][K]
   int M, K;
@@ -93,6 +112,13 @@ struct GemmArgs {
   int split_k;         // RESID only: K splits (set by the launcher)
   float* part;         // RESID split over K: [splits][M][Nv] fp32 partial sums written with plain stores
                        // (added into out0 by launch_resid_norm), or NULL: fp32 atomics into out0
+  const int32_t* m_dev;  // device row count (M is then a capacity), or NULL
+  // LOGITS_KL: the logits as LOGITS, plus each row's statistics over every tile of BN columns
+  // against the previous posterior: klp[(n0 / BN) * M + m] (kPartWords floats each)
+  const void* prev;      // [B*N][Nv] previous posterior, rows b*N + pos
+  float* klp;
+  int mask_id;           // id left out of the argmax (-1: none)
+  int kv_hm;             // QKV: caches head-major [B][H][N][Dh] (0: token-major [B][N][H][Dh])
 };
 // nsplit (may be NULL) receives the number of K splits launched.
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit = nullptr);

@@ -14,11 +14,11 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "klpart.hpp"
 
 namespace sl {
 
 constexpr int kKLThreads = 512;
-constexpr int kPartWords = 8;
 constexpr int kTailThreads = 1024;
 
 // ------------------------------------------------------------------ compaction
@@ -225,6 +225,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
   const int bd = blockDim.x;
   const bool gate = p.gate_q >= 0.f;
   const bool can_lock = p.eps > 0.f && p.have_prev;
+  const int t_now = p.t_dev ? p.t_dev[0] : p.t;   // step index recorded in lock_step
   for (int b = 0; b < p.B; ++b) {
     const int o0 = p.act_off[b], o1 = p.act_off[b + 1];
     const int n = o1 - o0;
@@ -263,7 +264,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
         for (int i = 0; i < kRegSel; ++i) {
           if (ok[i]) {
             p.locked[gb + pv[i]] = 1;
-            if (p.lock_step) p.lock_step[gb + pv[i]] = p.t;
+            if (p.lock_step) p.lock_step[gb + pv[i]] = t_now;
           }
         }
       } else {
@@ -274,7 +275,7 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
           if (gate) ok = ok && (p.u[m] <= thr);
           if (ok) {
             p.locked[g] = 1;
-            if (p.lock_step) p.lock_step[g] = p.t;
+            if (p.lock_step) p.lock_step[g] = t_now;
           }
         }
       }
@@ -319,32 +320,6 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
 
 
 // ------------------------------------------------------------------ row pass
-struct Part {
-  float ma, sa, ta;  // running max of cur (all ids), sum e^(a-ma), sum e^(a-ma) (a-b)
-  float mb, sb;      // running max of prev, sum e^(b-mb)
-  float best;        // max of cur over ids != mask
-  int bidx;          // chunk holding `best` (lowest on ties)
-};
-
-__device__ __forceinline__ float scale_to(float m_old, float m_new) {
-  return (m_old > -INFINITY) ? __builtin_amdgcn_exp2f((m_old - m_new) * kLog2e) : 0.f;
-}
-
-__device__ __forceinline__ Part combine(const Part& x, const Part& y) {
-  Part r;
-  r.ma = fmaxf(x.ma, y.ma);
-  const float ex = scale_to(x.ma, r.ma), ey = scale_to(y.ma, r.ma);
-  r.sa = x.sa * ex + y.sa * ey;
-  r.ta = x.ta * ex + y.ta * ey;
-  r.mb = fmaxf(x.mb, y.mb);
-  const float fx = scale_to(x.mb, r.mb), fy = scale_to(y.mb, r.mb);
-  r.sb = x.sb * fx + y.sb * fy;
-  const bool take_y = (y.best > x.best) || (y.best == x.best && y.bidx < x.bidx);
-  r.best = take_y ? y.best : x.best;
-  r.bidx = take_y ? y.bidx : x.bidx;
-  return r;
-}
-
 // Lane (l - shift) within the row of 16, or the identity partial where that
 // lane lies outside the row / the row is masked off (DPP, no LDS round trip).
 template <int CTRL, int RM>
@@ -411,24 +386,6 @@ __device__ void finish_row(const KLRowParams& rp, const Part& t, int r) {
   if (rp.conf) rp.conf[r] = __expf(t.best - t.ma) / t.sa;
 }
 
-// Segment partials: 8 words per (segment, row), segment-major, so the tail
-// reads one segment of consecutive rows with consecutive lanes.
-__device__ __forceinline__ void store_part(float* pp, const Part& t) {
-  f32x4 x0, x1;
-  x0[0] = t.ma; x0[1] = t.sa; x0[2] = t.ta; x0[3] = t.mb;
-  x1[0] = t.sb; x1[1] = t.best; x1[2] = __int_as_float(t.bidx); x1[3] = 0.f;
-  reinterpret_cast<f32x4*>(pp)[0] = x0;
-  reinterpret_cast<f32x4*>(pp)[1] = x1;
-}
-__device__ __forceinline__ Part load_part(const float* pp) {
-  const f32x4 x0 = reinterpret_cast<const f32x4*>(pp)[0];
-  const f32x4 x1 = reinterpret_cast<const f32x4*>(pp)[1];
-  Part t;
-  t.ma = x0[0]; t.sa = x0[1]; t.ta = x0[2]; t.mb = x0[3];
-  t.sb = x1[0]; t.best = x1[1]; t.bidx = __float_as_int(x1[2]);
-  return t;
-}
-
 // Row pass: workgroup (row r, segment) streams its slice of the current and
 // previous logits once.  With one segment per row it finishes the row itself;
 // otherwise it stores its partial for the tail kernel.  No inter-workgroup
@@ -440,6 +397,7 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
   __shared__ Part s_part[kKLThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x / n_seg, seg = blockIdx.x - r * n_seg;
+  if (r >= rows_live(tp.M_tot, tp.m_dev)) return;   // uniform over the workgroup, before any barrier
   const int b = seq_of_row(tp.act_off, tp.B, r);
   const int64_t g = (int64_t)b * tp.N + tp.act_idx[r];
   const size_t rowbytes = (size_t)rp.V * sizeof(T);
@@ -627,7 +585,7 @@ template <typename T, bool PREV>
 __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n_seg, const float* part,
                               TailShared& sh, TailLds& ls) {
   const int tid = threadIdx.x, bd = blockDim.x;
-  const int P = tp.B * tp.N, Mt = tp.M_tot;
+  const int P = tp.B * tp.N, Mt = rows_live(tp.M_tot, tp.m_dev), Mcap = tp.M_tot;
   const int p0 = 16 * tid;
   // every global load first
   const u32x4 lkv = load_flags16(tp.locked, p0, P, 0x01010101u);
@@ -644,13 +602,13 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
     }
   }
   Part x[kMergeRows][kMaxSeg];
-  if (n_seg > 1) {   // n_seg > 1 only when M_tot < kMergeRows * blockDim: one round
+  if (n_seg > 1 && Mt > 0) {   // n_seg > 1 only when M_tot < kMergeRows * blockDim: one round
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
       const int r = min(tid + k * bd, Mt - 1);   // clamped: loads stay in bounds
 #pragma unroll
       for (int s2 = 0; s2 < kMaxSeg; ++s2)
-        if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * Mt + r) * kPartWords);
+        if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * Mcap + r) * kPartWords);
     }
   }
   // LDS copies
@@ -664,7 +622,7 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
     ls.ai[m] = ai[j];
     if (n_seg == 1) { ls.u[m] = uu[j]; ls.kl[m] = kk[j]; }
   }
-  if (n_seg > 1) {
+  if (n_seg > 1 && Mt > 0) {
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
       Part t = x[k][0];
@@ -681,6 +639,8 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
   }
   __syncthreads();
   TailParams q = tp;
+  q.M_tot = Mt;
+  q.m_dev = nullptr;
   q.locked = ls.lk;
   q.cand = tp.cand ? ls.cd : nullptr;
   q.u = ls.u;
@@ -703,34 +663,43 @@ __global__ void __launch_bounds__(kTailThreads)
 kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   __shared__ TailShared sh;
   __shared__ __attribute__((aligned(16))) TailLds ls;
-  if ((long)tp.B * tp.N <= kTailPos && tp.M_tot <= kTailRows && tp.M_tot > 0) {
+  const int Mt = rows_live(tp.M_tot, tp.m_dev);   // tp.M_tot: capacity and stride of the partials
+  if ((long)tp.B * tp.N <= kTailPos && tp.M_tot <= kTailRows && Mt > 0) {
     tail_from_lds<T, PREV>(rp, tp, n_seg, part, sh, ls);
-    return;
-  }
-  if (n_seg > 1 && tp.M_tot > 0) {
-    const int bd = blockDim.x;
-    for (int r0 = 0; r0 < tp.M_tot; r0 += kMergeRows * bd) {
-      Part x[kMergeRows][kMaxSeg];
+  } else {
+    if (n_seg > 1 && Mt > 0) {
+      const int bd = blockDim.x;
+      for (int r0 = 0; r0 < Mt; r0 += kMergeRows * bd) {
+        Part x[kMergeRows][kMaxSeg];
 #pragma unroll
-      for (int k = 0; k < kMergeRows; ++k) {
-        const int r = min(r0 + (int)threadIdx.x + k * bd, tp.M_tot - 1);   // clamped: loads stay in bounds
+        for (int k = 0; k < kMergeRows; ++k) {
+          const int r = min(r0 + (int)threadIdx.x + k * bd, Mt - 1);   // clamped: loads stay in bounds
 #pragma unroll
-        for (int s2 = 0; s2 < kMaxSeg; ++s2)
-          if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * tp.M_tot + r) * kPartWords);
+          for (int s2 = 0; s2 < kMaxSeg; ++s2)
+            if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * tp.M_tot + r) * kPartWords);
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeRows; ++k) {
+          Part t = x[k][0];
+#pragma unroll
+          for (int s2 = 1; s2 < kMaxSeg; ++s2)
+            if (s2 < n_seg) t = combine(t, x[k][s2]);
+          const int r = r0 + (int)threadIdx.x + k * bd;
+          if (r < Mt) finish_row<PREV>(rp, t, r);
+        }
       }
-#pragma unroll
-      for (int k = 0; k < kMergeRows; ++k) {
-        Part t = x[k][0];
-#pragma unroll
-        for (int s2 = 1; s2 < kMaxSeg; ++s2)
-          if (s2 < n_seg) t = combine(t, x[k][s2]);
-        const int r = r0 + (int)threadIdx.x + k * bd;
-        if (r < tp.M_tot) finish_row<PREV>(rp, t, r);
-      }
+      __syncthreads();
     }
-    __syncthreads();
+    TailParams q = tp;
+    q.M_tot = Mt;
+    q.m_dev = nullptr;
+    tail_phase(q, sh);
   }
-  tail_phase(tp, sh);
+  // advance the device step index once every use of it in this step is done
+  if (tp.t_dev) {
+    __syncthreads();
+    if (threadIdx.x == 0) tp.t_dev[0] = tp.t_dev[0] + 1;
+  }
 }
 
 static int kl_nseg(int M_tot, int V, int elem_bytes) {
@@ -760,6 +729,46 @@ static void kl_launch_t(const KLRowParams& rp, const TailParams& tp, float* part
   }
   hipLaunchKernelGGL((kl_tail_kernel<T, PREV>), dim3(1), dim3(kTailThreads), 0, s, rp, tp,
                      tp.M_tot > 0 ? n_seg : 1, (const float*)part);
+}
+
+// Merge of the LM head's per-tile row statistics (EPI_LOGITS_KL): one wave per row combines the
+// row's n_vt partials (lane v takes tiles v, v + 64, ...; every load of a lane issued before use),
+// then the row's statistics as the row pass would finish them.
+constexpr int kMergeLoads = 8;
+
+__global__ void __launch_bounds__(256)
+kl_merge_kernel(KLRowParams rp, int M_cap, const int32_t* __restrict__ m_dev, int n_vt, const float* __restrict__ klp) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= rows_live(M_cap, m_dev)) return;   // uniform over the wave
+  Part acc = empty_part();
+  for (int v0 = lane; v0 < n_vt; v0 += 64 * kMergeLoads) {
+    Part x[kMergeLoads];
+#pragma unroll
+    for (int k = 0; k < kMergeLoads; ++k) {
+      const int v = min(v0 + 64 * k, n_vt - 1);   // clamped: loads stay in bounds
+      x[k] = load_part(klp + ((size_t)v * M_cap + m) * kPartWords);
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeLoads; ++k)
+      if (v0 + 64 * k < n_vt) acc = combine(acc, x[k]);
+  }
+  acc = wave_reduce_part(acc);
+  if (lane == 0) finish_row<true>(rp, acc, m);
+}
+
+template <typename T>
+static void kl_merge_tail_t(const KLRowParams& rp, const TailParams& tp, const float* klp, int n_vt, hipStream_t s) {
+  if (tp.M_tot > 0)
+    hipLaunchKernelGGL(kl_merge_kernel, dim3((tp.M_tot + 3) / 4), dim3(256), 0, s, rp, tp.M_tot, tp.m_dev, n_vt, klp);
+  hipLaunchKernelGGL((kl_tail_kernel<T, true>), dim3(1), dim3(kTailThreads), 0, s, rp, tp, 1, (const float*)nullptr);
+}
+
+hipError_t launch_kl_merge_tail(int dtype, const KLRowParams& rp, const TailParams& tp, const float* klp, int n_vt,
+                                hipStream_t s) {
+  if (!tp.have_prev || n_vt < 1) return hipErrorInvalidValue;
+  if (dtype == 0) kl_merge_tail_t<bf16>(rp, tp, klp, n_vt, s);
+  else kl_merge_tail_t<float>(rp, tp, klp, n_vt, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s) {

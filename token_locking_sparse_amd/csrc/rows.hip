@@ -98,9 +98,10 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 gather_norm_kernel(const T* __restrict__ h_in, const T* __restrict__ embed, const int32_t* __restrict__ tok,
                    const int32_t* __restrict__ act_idx, const int32_t* __restrict__ act_off, int B, int N,
-                   int M_tot, int d, float eps, float* __restrict__ h32, T* __restrict__ x) {
+                   int M_tot, int d, float eps, float* __restrict__ h32, T* __restrict__ x,
+                   const int32_t* __restrict__ m_dev) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M_tot) return;
+  if (m >= rows_live(M_tot, m_dev)) return;
   const int b = seq_of_row(act_off, B, m);
   const int64_t g = (int64_t)b * N + act_idx[m];
   const T* src = h_in ? h_in + g * d : embed + (int64_t)tok[g] * d;
@@ -109,23 +110,25 @@ gather_norm_kernel(const T* __restrict__ h_in, const T* __restrict__ embed, cons
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-norm_kernel(const float* __restrict__ h32, int M_tot, int d, float eps, T* __restrict__ x) {
+norm_kernel(const float* __restrict__ h32, int M_tot, int d, float eps, T* __restrict__ x,
+            const int32_t* __restrict__ m_dev) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M_tot) return;
+  if (m >= rows_live(M_tot, m_dev)) return;
   norm_row<float, T, false>(h32 + (size_t)m * d, d, eps, nullptr, x + (size_t)m * d, lane);
 }
 
 hipError_t launch_gather_norm(int dtype, const void* h_in, const void* embed, const int32_t* tok,
                               const int32_t* act_idx, const int32_t* act_off, int B, int N,
-                              int M_tot, int d, float eps, float* h32, void* x, hipStream_t s) {
+                              int M_tot, int d, float eps, float* h32, void* x, hipStream_t s,
+                              const int32_t* m_dev) {
   if (M_tot <= 0) return hipSuccess;
   const dim3 grid((M_tot + 3) / 4), block(256);
   if (dtype == 0)
     hipLaunchKernelGGL(gather_norm_kernel<bf16>, grid, block, 0, s, (const bf16*)h_in, (const bf16*)embed,
-                       tok, act_idx, act_off, B, N, M_tot, d, eps, h32, (bf16*)x);
+                       tok, act_idx, act_off, B, N, M_tot, d, eps, h32, (bf16*)x, m_dev);
   else
     hipLaunchKernelGGL(gather_norm_kernel<float>, grid, block, 0, s, (const float*)h_in, (const float*)embed,
-                       tok, act_idx, act_off, B, N, M_tot, d, eps, h32, (float*)x);
+                       tok, act_idx, act_off, B, N, M_tot, d, eps, h32, (float*)x, m_dev);
   return hipGetLastError();
 }
 
@@ -140,8 +143,9 @@ constexpr int kResidThreads = 256, kResidCPT = kResidMaxD / 4 / kResidThreads;
 template <typename T, int S>
 __global__ void __launch_bounds__(kResidThreads)
 resid_norm_kernel(const float* __restrict__ part, float* __restrict__ h32, int M_tot, int d, float eps,
-                  T* __restrict__ x) {
+                  T* __restrict__ x, const int32_t* __restrict__ m_dev) {
   const int m = blockIdx.x, tid = threadIdx.x;
+  if (m >= rows_live(M_tot, m_dev)) return;   // uniform over the workgroup
   const int nc = d / 4;
   float* hrow = h32 + (size_t)m * d;
   f32x4 acc[kResidCPT], pv[S][kResidCPT];
@@ -188,34 +192,35 @@ resid_norm_kernel(const float* __restrict__ part, float* __restrict__ h32, int M
 
 template <typename T>
 static hipError_t resid_norm_t(const float* part, int nsplit, float* h32, int M_tot, int d, float eps, T* x,
-                               hipStream_t s) {
+                               hipStream_t s, const int32_t* m_dev) {
   const dim3 grid(M_tot), block(kResidThreads);
   switch (nsplit) {
-    case 2: hipLaunchKernelGGL((resid_norm_kernel<T, 2>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 3: hipLaunchKernelGGL((resid_norm_kernel<T, 3>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 4: hipLaunchKernelGGL((resid_norm_kernel<T, 4>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 5: hipLaunchKernelGGL((resid_norm_kernel<T, 5>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 6: hipLaunchKernelGGL((resid_norm_kernel<T, 6>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 7: hipLaunchKernelGGL((resid_norm_kernel<T, 7>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
-    case 8: hipLaunchKernelGGL((resid_norm_kernel<T, 8>), grid, block, 0, s, part, h32, M_tot, d, eps, x); break;
+    case 2: hipLaunchKernelGGL((resid_norm_kernel<T, 2>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 3: hipLaunchKernelGGL((resid_norm_kernel<T, 3>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 4: hipLaunchKernelGGL((resid_norm_kernel<T, 4>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 5: hipLaunchKernelGGL((resid_norm_kernel<T, 5>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 6: hipLaunchKernelGGL((resid_norm_kernel<T, 6>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 7: hipLaunchKernelGGL((resid_norm_kernel<T, 7>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
+    case 8: hipLaunchKernelGGL((resid_norm_kernel<T, 8>), grid, block, 0, s, part, h32, M_tot, d, eps, x, m_dev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_resid_norm(int dtype, const float* part, int nsplit, float* h32, int M_tot, int d, float eps,
-                             void* x, hipStream_t s) {
+                             void* x, hipStream_t s, const int32_t* m_dev) {
   if (M_tot <= 0) return hipSuccess;
   if (d % 4 || d > kResidMaxD || d < 4) return hipErrorInvalidValue;
-  return dtype == 0 ? resid_norm_t<bf16>(part, nsplit, h32, M_tot, d, eps, (bf16*)x, s)
-                    : resid_norm_t<float>(part, nsplit, h32, M_tot, d, eps, (float*)x, s);
+  return dtype == 0 ? resid_norm_t<bf16>(part, nsplit, h32, M_tot, d, eps, (bf16*)x, s, m_dev)
+                    : resid_norm_t<float>(part, nsplit, h32, M_tot, d, eps, (float*)x, s, m_dev);
 }
 
-hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x, hipStream_t s) {
+hipError_t launch_norm(int dtype, const float* h32, int M_tot, int d, float eps, void* x, hipStream_t s,
+                       const int32_t* m_dev) {
   if (M_tot <= 0) return hipSuccess;
   const dim3 grid((M_tot + 3) / 4), block(256);
-  if (dtype == 0) hipLaunchKernelGGL(norm_kernel<bf16>, grid, block, 0, s, h32, M_tot, d, eps, (bf16*)x);
-  else hipLaunchKernelGGL(norm_kernel<float>, grid, block, 0, s, h32, M_tot, d, eps, (float*)x);
+  if (dtype == 0) hipLaunchKernelGGL(norm_kernel<bf16>, grid, block, 0, s, h32, M_tot, d, eps, (bf16*)x, m_dev);
+  else hipLaunchKernelGGL(norm_kernel<float>, grid, block, 0, s, h32, M_tot, d, eps, (float*)x, m_dev);
   return hipGetLastError();
 }
 

@@ -49,18 +49,19 @@ class sl_state(C.Structure):
                 ("h_in", C.c_void_p), ("h_out", C.c_void_p), ("logits", C.c_void_p * 2),
                 ("kl", C.c_void_p), ("u", C.c_void_p), ("lse", C.c_void_p), ("conf", C.c_void_p),
                 ("argmax", C.c_void_p), ("gate_thr", C.c_void_p), ("lock_step", C.c_void_p),
-                ("m_tot_host", C.c_void_p)]
+                ("m_tot_host", C.c_void_p), ("t_dev", C.c_void_p), ("kv_head_major", C.c_int)]
 
 
 class sl_step_params(C.Structure):
     _fields_ = [("eps", C.c_float), ("gate_q", C.c_float), ("mask_id", C.c_int), ("do_lock", C.c_int),
-                ("unmask_k", C.c_int), ("no_kv_cache", C.c_int)]
+                ("unmask_k", C.c_int), ("no_kv_cache", C.c_int), ("device_m", C.c_int),
+                ("fuse_head_kl", C.c_int)]
 
 
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
            "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_step_workspace_min", "sl_gemm",
-           "sl_gemm_plan", "sl_kl_lock_noalloc")
+           "sl_gemm_plan", "sl_kl_lock_noalloc", "sl_peak_mfma", "sl_peak_mfma_flops", "sl_peak_stream")
 
 _lib = None
 
@@ -94,6 +95,9 @@ def lib():
         "sl_gemm": (i, [i, i, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp, vp, i, i, vp]),
         "sl_gemm_plan": (i, [i, i, i, i, i, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
                              C.POINTER(C.c_int)]),
+        "sl_peak_mfma": (i, [i, i, vp, vp]),
+        "sl_peak_mfma_flops": (C.c_double, [i, i]),
+        "sl_peak_stream": (i, [vp, vp, sz, i, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -278,3 +282,17 @@ def sl_gemm(epilogue, A, M, K, n_out, w0, w1=None, w2=None, out0=None, out1=None
                        _ptr(act_idx, "act_idx", torch.int32, optional=True),
                        _ptr(act_off, "act_off", torch.int32, optional=True), B, N, _stream(stream))
     _check("sl_gemm", st)
+
+
+# ------------------------------------------------------------------ measurement helpers
+def sl_peak_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
+    """Launch the register-only MFMA loop; returns the FLOPs it performs."""
+    _check("sl_peak_mfma", lib().sl_peak_mfma(workgroups, iters, _ptr(sink, "sink", torch.float32), _stream(stream)))
+    return float(lib().sl_peak_mfma_flops(workgroups, iters))
+
+
+def sl_peak_stream(src, dst, workgroups: int, sink, stream=None):
+    """Stream src (read only when dst is None, else copy into dst) with 16-byte non-temporal accesses."""
+    nbytes = src.numel() * src.element_size()
+    _check("sl_peak_stream", lib().sl_peak_stream(_ptr(src, "src"), _ptr(dst, "dst", optional=True), nbytes,
+                                                  workgroups, _ptr(sink, "sink", torch.float32), _stream(stream)))
