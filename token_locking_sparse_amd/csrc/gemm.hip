@@ -115,30 +115,101 @@ __device__ __forceinline__ void store8(T* dst, const float* y) {
   }
 }
 
-// 8 consecutive elements of the storage type as floats.
-template <typename T>
-__device__ __forceinline__ void load8(const T* src, float* y) {
-  if (sizeof(T) == 2) {
-    Chunk<bf16>::unpack(ld16(src), y);
-  } else {
-    Chunk<float>::unpack(ld16(src), y);
-    Chunk<float>::unpack(ld16((const float*)src + 4), y + 4);
-  }
-}
-
-// A partial from lane (l ^ o).
-__device__ __forceinline__ Part shfl_xor_part(const Part& p, int o) {
-  Part q;
-  q.ma = __shfl_xor(p.ma, o, 64); q.sa = __shfl_xor(p.sa, o, 64); q.ta = __shfl_xor(p.ta, o, 64);
-  q.mb = __shfl_xor(p.mb, o, 64); q.sb = __shfl_xor(p.sb, o, 64);
-  q.best = __shfl_xor(p.best, o, 64); q.bidx = __shfl_xor(p.bidx, o, 64);
-  return q;
-}
-
 __device__ __forceinline__ void lds8(const float* p, float* y) {
   const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) { y[i] = a[i]; y[4 + i] = b[i]; }
+}
+
+// EPI_LOGITS_KL, one pass over PR rows of the fp32 tile (rows from mrow0): the logits as EPI_LOGITS,
+// then, from the stored values a (rounded to the storage type, as a later pass would read them) and
+// the previous posterior's b (prefetched into praw by logits_kl_prefetch), each row's statistics over this tile's BN
+// columns: max a, sum e^(a - max a), sum e^(a - max a) (a - b), max b, sum e^(b - max b), and the
+// largest a other than the [MASK] id with its lowest id.  A row's CPR chunks sit on CPR consecutive
+// lanes (ids are consecutive, CPR divides 64); the lanes first agree on the row maxima, so the sums
+// combine by plain additions.  grow[it] = the row b*N + pos of chunk it, or -1 past the live rows.
+template <typename T, int BN, int LDW, int PR, int NT, int IT, int PW>
+__device__ __forceinline__ void logits_kl_pass(const GemmArgs& a, const float* tile, int mrow0, int n0,
+                                               const u32x4 (&praw)[IT][PW], const int32_t (&grow)[IT]) {
+  constexpr int CPR = BN / 8;
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "fused statistics need BN in {64, 128, 256}");
+  const int tid = threadIdx.x;
+  const int vt = n0 / BN;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int id = tid + it * NT;
+    if (grow[it] < 0) continue;   // uniform over the row's lanes
+    const int r = id / CPR, c = (id % CPR) * 8;
+    const int m = mrow0 + r;
+    float y[8], bv[8];
+    lds8(tile + r * LDW + c, y);
+    store8<T>((T*)a.out0 + (size_t)grow[it] * a.Nv + n0 + c, y);
+    if (sizeof(T) == 2) {
+      Chunk<bf16>::unpack(praw[it][0], bv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = (float)(bf16)y[i];
+    } else {
+      Chunk<float>::unpack(praw[it][0], bv);
+      Chunk<float>::unpack(praw[it][PW - 1], bv + 4);
+    }
+    float ma = y[0], mb = bv[0], best = -INFINITY;
+    int bidx = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ma = fmaxf(ma, y[i]);
+      mb = fmaxf(mb, bv[i]);
+      if (y[i] > best && n0 + c + i != a.mask_id) { best = y[i]; bidx = n0 + c + i; }
+    }
+#pragma unroll
+    for (int o = CPR / 2; o >= 1; o >>= 1) {
+      ma = fmaxf(ma, __shfl_xor(ma, o, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+      const float ob = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bidx, o, 64);
+      if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+    }
+    const float mal = ma * kLog2e, mbl = mb * kLog2e;
+    float sa = 0.f, ta = 0.f, sb = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(y[i], kLog2e, -mal));
+      sa += e;
+      ta = fmaf(e, y[i] - bv[i], ta);
+      sb += __builtin_amdgcn_exp2f(fmaf(bv[i], kLog2e, -mbl));
+    }
+#pragma unroll
+    for (int o = CPR / 2; o >= 1; o >>= 1) {
+      sa += __shfl_xor(sa, o, 64);
+      ta += __shfl_xor(ta, o, 64);
+      sb += __shfl_xor(sb, o, 64);
+    }
+    if (id % CPR == 0) {
+      Part p;
+      p.ma = ma; p.sa = sa; p.ta = ta; p.mb = mb; p.sb = sb; p.best = best; p.bidx = bidx;
+      store_part(a.klp + ((size_t)vt * a.M + m) * kPartWords, p);
+    }
+  }
+}
+
+// The previous posterior's chunks of the PR rows from mrow0 that logits_kl_pass will use.
+template <typename T, int BN, int PR, int NT, int IT, int PW>
+__device__ __forceinline__ void logits_kl_prefetch(const GemmArgs& a, int mrow0, int n0, int Mr, u32x4 (&praw)[IT][PW],
+                                                   int32_t (&grow)[IT]) {
+  constexpr int CPR = BN / 8;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int id = tid + it * NT;
+    const int m = mrow0 + id / CPR;
+    grow[it] = -1;
+    if (id < PR * CPR && m < Mr) {
+      const int b = seq_of_row(a.act_off, a.B, m);
+      grow[it] = b * a.N + a.act_idx[m];
+      const char* src = (const char*)((const T*)a.prev + (size_t)grow[it] * a.Nv + n0 + (id % CPR) * 8);
+#pragma unroll
+      for (int w = 0; w < PW; ++w) praw[it][w] = ld16(src + 16 * w);
+    }
+  }
 }
 
 // One pass of the epilogue over PR rows of the fp32 tile (rows from mrow0).
@@ -175,48 +246,6 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
         y += *(const f32x4*)(tile + r * LDW + c);
         *(f32x4*)h = y;
       }
-    }
-  } else if (EPI == EPI_LOGITS_KL) {
-    // The logits as EPI_LOGITS, then, from the stored values a (rounded to the storage type, as a
-    // later pass would read them) and the previous posterior's b, each row's statistics over this
-    // tile's BN columns: max a, sum e^(a - max a), sum e^(a - max a) (a - b), max b, sum e^(b - max b),
-    // and the largest a other than the [MASK] id with its lowest id.  A row's CPR chunks sit on CPR
-    // consecutive lanes (ids are consecutive, CPR divides 64), combined by lane shuffles.
-    constexpr int CPR = BN / 8;
-    static_assert(EPI != EPI_LOGITS_KL || CPR == 8 || CPR == 16 || CPR == 32, "fused statistics need BN in {64, 128, 256}");
-    const int vt = n0 / BN;
-    for (int id = tid; id < PR * CPR; id += NT) {
-      const int r = id / CPR, c = (id % CPR) * 8;
-      const int m = mrow0 + r;
-      if (m >= Mr) continue;   // uniform over the row's lanes
-      const int b = seq_of_row(a.act_off, a.B, m);
-      const size_t g = (size_t)b * a.N + a.act_idx[m];
-      float y[8], bv[8];
-      lds8(tile + r * LDW + c, y);
-      store8<T>((T*)a.out0 + g * a.Nv + n0 + c, y);
-      load8<T>((const T*)a.prev + g * a.Nv + n0 + c, bv);
-      if (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = (float)(bf16)y[i];
-      }
-      Part p = empty_part();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p.ma = fmaxf(p.ma, y[i]);
-        p.mb = fmaxf(p.mb, bv[i]);
-        if (y[i] > p.best && n0 + c + i != a.mask_id) { p.best = y[i]; p.bidx = n0 + c + i; }
-      }
-      const float mal = p.ma * kLog2e, mbl = p.mb * kLog2e;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(y[i], kLog2e, -mal));
-        p.sa += e;
-        p.ta = fmaf(e, y[i] - bv[i], p.ta);
-        p.sb += __builtin_amdgcn_exp2f(fmaf(bv[i], kLog2e, -mbl));
-      }
-#pragma unroll
-      for (int o = CPR / 2; o >= 1; o >>= 1) p = combine(p, shfl_xor_part(p, o));
-      if (id % CPR == 0) store_part(a.klp + ((size_t)vt * a.M + m) * kPartWords, p);
     }
   } else if (EPI == EPI_LOGITS) {
     constexpr int CPR = BN / 8;
@@ -492,20 +521,43 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   constexpr int PR = (BM * LDW * 4 <= SMEM) ? BM : (BM / 2 * LDW * 4 <= SMEM) ? BM / 2 : (BM / 4 * LDW * 4 <= SMEM) ? BM / 4 : 32;
   static_assert(PR >= 32 && PR % 32 == 0 && BM % PR == 0 && PR * LDW * 4 <= SMEM, "epilogue pass");
   float* tile = (float*)smem;
-  for (int r_lo = 0; r_lo < BM; r_lo += PR) {
+  // Writes the accumulators of rows [r_lo, r_lo + rows) of the tile into the fp32 LDS tile.
+  auto stage_rows = [&](int r_lo, int rows) {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       const int rb = wm * C::TM + i * 32 - r_lo;   // first tile row of this MFMA block in the pass
-      if (rb < 0 || rb >= PR) continue;
+      if (rb < 0 || rb >= rows) continue;
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           tile[(rb + (v >> 2) * 8 + 4 * hl + (v & 3)) * LDW + wn * C::TN + j * 32 + l32] = acc[i][j][v];
     }
-    __syncthreads();
-    epilogue_pass<T, EPI, BN, C::TN, LDW, PR, C::NT>(a, tile, m0 + r_lo, n0, Mr);
-    __syncthreads();
+  };
+  if constexpr (EPI == EPI_LOGITS_KL) {
+    // The previous posterior's chunks of the next row pass are loaded as soon as a pass has used its
+    // own, so their latency overlaps the next pass's staging instead of stalling every wave of the CU.
+    // Passes of at most 4 chunks per thread keep the prefetched registers within the budget.
+    constexpr int KCPR = BN / 8, KPR = PR < 4 * C::NT / KCPR ? PR : 4 * C::NT / KCPR;
+    constexpr int KIT = (KPR * KCPR + C::NT - 1) / C::NT, KPW = sizeof(T) == 2 ? 1 : 2;
+    static_assert(BM % KPR == 0 && KPR % 32 == 0, "fused statistics pass");
+    u32x4 praw[KIT][KPW];
+    int32_t grow[KIT];   // b*N + pos < 2^31, or -1 past the live rows
+    logits_kl_prefetch<T, BN, KPR, C::NT, KIT, KPW>(a, m0, n0, Mr, praw, grow);
+    for (int r_lo = 0; r_lo < BM; r_lo += KPR) {
+      stage_rows(r_lo, KPR);
+      __syncthreads();
+      logits_kl_pass<T, BN, LDW, KPR, C::NT, KIT, KPW>(a, tile, m0 + r_lo, n0, praw, grow);
+      if (r_lo + KPR < BM) logits_kl_prefetch<T, BN, KPR, C::NT, KIT, KPW>(a, m0 + r_lo + KPR, n0, Mr, praw, grow);
+      __syncthreads();
+    }
+  } else {
+    for (int r_lo = 0; r_lo < BM; r_lo += PR) {
+      stage_rows(r_lo, PR);
+      __syncthreads();
+      epilogue_pass<T, EPI, BN, C::TN, LDW, PR, C::NT>(a, tile, m0 + r_lo, n0, Mr);
+      __syncthreads();
+    }
   }
 }
 
