@@ -344,7 +344,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // compiler drain all loads before a slot is used.  Small LDS and register use
 // let two workgroups share a CU.
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI, bool VB>
-__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, 2)))
+__global__ void __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, 2)))
 gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   using C = GemmCfg<T, BM, BN, WM, WN, RB, S>;
   constexpr int kStages = VB ? 2 : S;   // LDS stages
@@ -353,11 +354,17 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int wm = wid / WN, wn = wid % WN;
 
-  // workgroup -> tile; tiles sharing a weight tile are consecutive and sit on one XCD
+  // workgroup -> tile.  Each XCD takes a contiguous range of the tile order (workgroups are dealt
+  // to the 8 XCDs round-robin), and the order walks groups of up to 8 row tiles column by column,
+  // so the workgroups an XCD runs at once cover a block of row and column tiles whose operand
+  // slices they share through its L2.
   const int nb = MT * NT;
   int lid = blockIdx.x;
   if ((nb & 7) == 0) lid = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-  const int bm = lid % MT, bn = lid / MT;
+  constexpr int kGroupRows = 8;
+  const int grp = lid / (kGroupRows * NT), in_grp = lid - grp * (kGroupRows * NT);
+  const int gm = min(kGroupRows, MT - grp * kGroupRows);
+  const int bm = grp * kGroupRows + in_grp % gm, bn = in_grp / gm;
   const int m0 = bm * BM, n0 = bn * BN;
   const int Mr = rows_live(a.M, a.m_dev);   // rows to compute (a.M is their capacity and plane stride)
   if (m0 >= Mr) return;                     // uniform over the workgroup, before any barrier
@@ -415,64 +422,87 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   constexpr int NDMA = C::ADma + C::BDma;
   constexpr int DPS = (NDMA + C::KS - 1) / C::KS;   // direct loads issued per k-step
 
-  // Multiply one k-tile held in LDS (A rows at `as`, B rows at `bs`); step(ks)
-  // issues that k-step's share of the loads in flight.
-  auto mma_tile = [&](const char* as, const char* bs, auto&& step) {
-    u32x4 fa[2][C::FM], fb[2][C::FN];
-    auto frags = [&](int ks, int buf) {
+  // Fragment reads of k-step ks of the k-tile at (as, bs) into register buffer buf.
+  u32x4 fa[2][C::FM], fb[2][C::FN];
+  auto frags = [&](const char* as, const char* bs, int ks, int buf) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = arow[i];
-        fa[buf][i] = *(const u32x4*)(as + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
-      }
+    for (int i = 0; i < C::FM; ++i) {
+      const int r = arow[i];
+      fa[buf][i] = *(const u32x4*)(as + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
+    }
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int r = brow[j];
-        fb[buf][j] = *(const u32x4*)(bs + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
+    for (int j = 0; j < C::FN; ++j) {
+      const int r = brow[j];
+      fb[buf][j] = *(const u32x4*)(bs + r * RB + (swz<RB>(r, 2 * ks + hl) << 4));
+    }
+  };
+  // The MFMAs of k-step ks (register buffer ks & 1), with the fragment reads issued just
+  // before them spread between them.
+  auto mfmas = [&](int ks, bool reads_follow) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) Mfma<T>::run(acc[i][j], fa[ks & 1][i], fb[ks & 1][j]);
+    if (reads_follow) {
+      constexpr int NRD = C::FM + C::FN;
+      constexpr int NM = C::FM * C::FN * (sizeof(T) == 2 ? 1 : 4);
+#pragma unroll
+      for (int g = 0; g < NRD; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / NRD > 0 ? NM / NRD : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-    };
-    frags(0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // Multiply one k-tile held in LDS (A rows at `as`, B rows at `bs`) whose first k-step's
+  // fragments are already in buffer 0; step(ks) issues that k-step's share of the loads in
+  // flight.
+  auto mma_tile = [&](const char* as, const char* bs, auto&& step) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      // this step's share of the next tile's loads, and the fragments of the
-      // next k-step, are spread between this step's MFMAs
       step(ks);
-      if (ks + 1 < C::KS) frags(ks + 1, (ks + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) Mfma<T>::run(acc[i][j], fa[ks & 1][i], fb[ks & 1][j]);
-      if (ks + 1 < C::KS) {
-        // the direct loads go out first; the next step's fragment reads are spread
-        // between this step's MFMAs
-        constexpr int NRD = C::FM + C::FN;
-        constexpr int NM = C::FM * C::FN * (sizeof(T) == 2 ? 1 : 4);
-#pragma unroll
-        for (int g = 0; g < NRD; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, NM / NRD > 0 ? NM / NRD : 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < C::KS) frags(as, bs, ks + 1, (ks + 1) & 1);
+      mfmas(ks, ks + 1 < C::KS);
     }
   };
 
   if constexpr (!VB) {
+    static_assert(C::KS % 2 == 0, "the next tile's first fragments go to buffer 0");
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
       if (kt0 + st < kt1) issue(kt0 + st, st, 0, NDMA);
-    for (int kt = kt0; kt < kt1; ++kt) {
-      // tile kt has landed when at most the (S-2) later tiles are still in flight
-      if (kt + S - 2 < kt1) wait_vmcnt<(S - 2) * NDMA>();
+    // Tile kt's fragments of its first k-step are read during the last k-step of tile kt - 1,
+    // behind that step's barrier, so every k-tile starts with its MFMAs' operands in registers.
+    if (kt0 < kt1) {
+      if (kt0 + S - 2 < kt1) wait_vmcnt<(S - 2) * NDMA>();
       else wait_vmcnt<0>();
       barrier_no_fence();
+      frags(smem, smem + BM * RB, 0, 0);
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
       const bool pre = kt + S - 1 < kt1;
       const int pre_stage = (kt + S - 1 - kt0) % S;
       const char* as = smem + ((kt - kt0) % S) * C::StageBytes;
-      mma_tile(as, as + BM * RB, [&](int ks) {
+      const char* bs = as + BM * RB;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
         if (pre) issue(kt + S - 1, pre_stage, ks * DPS, (ks + 1) * DPS);
-      });
+        if (ks + 1 < C::KS) {
+          frags(as, bs, ks + 1, (ks + 1) & 1);
+        } else {
+          // tile kt + 1 has landed when at most the S - 2 later tiles are in flight; the
+          // barrier also tells that every wave's reads of tile kt (the stage the next
+          // k-tile's loads overwrite) are done.  After the last tile the reads fetch a stale
+          // stage that nothing uses.
+          __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+          if (pre) wait_vmcnt<(S - 2) * NDMA>();
+          else wait_vmcnt<0>();
+          barrier_no_fence();
+          const char* an = smem + ((kt + 1 - kt0) % S) * C::StageBytes;
+          frags(an, an + BM * RB, 0, 0);
+        }
+        mfmas(ks, true);
+      }
     }
   } else {
     constexpr int RS = S - 1;   // register stages
@@ -498,6 +528,8 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
       vload(min(kt + S - 1, kt1 - 1), u);
       __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0): stores done
       barrier_no_fence();
+      frags(as, bs, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
       mma_tile(as, bs, [](int) {});
     };
 #pragma unroll
