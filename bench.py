@@ -60,7 +60,7 @@ def kl_bytes(M, N=N_KL, V=V_KL):
 # the report says null.
 TRAFFIC = {
     "gemm": {"files": ["token_locking_sparse_amd/csrc/gemm.hip"],
-             "sha256": "b0970160526a59e9a2a164c34145ee8db38a2512e277af2b169da52158ccb722", "bytes": 427907904},
+             "sha256": "4a16938212c63a6db4e5f2e4acd8345b339e0cdfcc87c83d4d7ff1caeec6e42d", "bytes": 427940488},
     "kl": {"files": ["token_locking_sparse_amd/csrc/kl_lock.hip"],
            "sha256": "40da225beba0286dac12a659a192a3340e91832b775433aaba3710f142068439", "bytes": 829659917},
 }
@@ -452,16 +452,82 @@ def measured_peaks(reps=7):
     ms_mfma = timed(lambda: sl.sl_peak_mfma(wg, iters, sink))
     ms_read = timed(lambda: sl.sl_peak_stream(src, None, 2048, sink))
     ms_copy = timed(lambda: sl.sl_peak_stream(src, dst, 2048, sink))
+    # the 256 x 256 GEMM tile's LDS-to-MFMA loop alone, one workgroup per CU, then with the k-tile
+    # loop's direct loads (from an L2-resident 1 MiB), waits and barrier
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = 2048
+    l2src = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    fl_loop = sl.sl_peak_gemm_loop(cus, tiles, False, l2src, sink)
+    ms_loop = timed(lambda: sl.sl_peak_gemm_loop(cus, tiles, False, l2src, sink))
+    ms_loop_ld = timed(lambda: sl.sl_peak_gemm_loop(cus, tiles, True, l2src, sink))
     nb = src.numel()
     out = {"mfma_bf16_tflops": round(flops / (ms_mfma * 1e-3) / 1e12, 1),
            "hbm_read_gbs": round(nb / (ms_read * 1e-3) / 1e9, 1),
            "hbm_copy_gbs": round(2 * nb / (ms_copy * 1e-3) / 1e9, 1),
+           "gemm_loop_tflops": round(fl_loop / (ms_loop * 1e-3) / 1e12, 1),
+           "gemm_loop_with_l2_loads_tflops": round(fl_loop / (ms_loop_ld * 1e-3) / 1e12, 1),
            "how": "register-only v_mfma_f32_32x32x16_bf16 loop, %d workgroups x 4 waves x %d x 4 MFMAs; "
                   "1 GiB streamed with 16-byte non-temporal loads (read) and loads + stores (copy, bytes "
-                  "read + written), each workgroup on a contiguous range; medians of %d launches" % (wg, iters, reps)}
-    del src, dst
+                  "read + written), each workgroup on a contiguous range; the 256 x 256 GEMM tile's "
+                  "LDS-to-MFMA loop on %d workgroups x %d k-tiles of 32, alone and with its direct loads "
+                  "from L2, waits and barrier; medians of %d launches" % (wg, iters, cus, tiles, reps)}
+    del src, dst, l2src
     torch.cuda.empty_cache()
     return out
+
+
+def gemm_study(reps=20, warmup=5):
+    """The library's GEMM (with its epilogue) against torch.matmul (the vendor library, plain
+    bf16 output) on the step's shapes and two large ones, weights resident; TFLOP/s of each."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        es = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    rows = []
+    for M, K, Nn, epi in [(1024, 4096, 24576, "swiglu"), (1024, 4096, 12288, "residual"),
+                          (1024, 12288, 4096, "residual"), (4873, 4096, 126464, "logits"),
+                          (8192, 8192, 8192, "logits")]:
+        A = (torch.randn(M, K, generator=g, device=dev) * 0.5).to(bf)
+        Wt = (torch.randn(Nn, K, generator=g, device=dev) * 0.02).to(bf)
+        if epi == "swiglu":
+            w0, w1 = Wt[: Nn // 2].contiguous(), Wt[Nn // 2:].contiguous()
+            out = torch.empty(M, Nn // 2, dtype=bf, device=dev)
+            fn = lambda: sl.sl_gemm(sl.SL_EPI_SWIGLU, A, M, K, Nn, w0, w1, out0=out)
+        elif epi == "residual":
+            out = torch.zeros(M, Nn, dtype=torch.float32, device=dev)
+            fn = lambda: sl.sl_gemm(sl.SL_EPI_RESIDUAL, A, M, K, Nn, Wt, out0=out)
+        else:
+            out = torch.empty(M, Nn, dtype=bf, device=dev)
+            ai = torch.arange(M, dtype=torch.int32, device=dev)
+            ao = torch.tensor([0, M], dtype=torch.int32, device=dev)
+            fn = lambda: sl.sl_gemm(sl.SL_EPI_LOGITS, A, M, K, Nn, Wt, out0=out, act_idx=ai, act_off=ao, B=1, N=M)
+        fl = 2.0 * M * K * Nn
+        ms = timed(fn)
+        ms_t = timed(lambda: torch.matmul(A, Wt.t()))
+        rows.append({"M": M, "K": K, "N": Nn, "epilogue": epi, "tile": list(sl.sl_gemm_plan(bf, {"swiglu": 2, "residual": 1, "logits": 3}[epi], M, K, Nn)),
+                     "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "torch_matmul_ms": round(ms_t, 4), "torch_matmul_tflops": round(fl / ms_t / 1e9, 1)})
+        del A, Wt, out
+        torch.cuda.empty_cache()
+    return rows
 
 
 def tiny_loop(steps=16, B=1, N=64, n_prompt=16, unmask=3, eps=0.05, reps=5):
@@ -825,7 +891,13 @@ def main():
                     help="only launch the roofline kernels and a calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--profile-attention", action="store_true",
                     help="only launch the attention at M = 1024 and 256 (for rocprofv3 --pmc)")
+    ap.add_argument("--gemm-study", action="store_true",
+                    help="only time the library's GEMM against torch.matmul on the step's shapes and two "
+                         "large ones (one JSON line)")
     args = ap.parse_args()
+    if args.gemm_study:
+        print(json.dumps({"gemm_study": gemm_study()}), flush=True)
+        return
     if args.profile_kernels:
         profile_kernels()
         return

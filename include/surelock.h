@@ -344,10 +344,18 @@ size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot);
  * sl_peak_stream     streams `bytes` (a multiple of 16) from src with 16-byte non-temporal loads,
  *                    each workgroup over one contiguous range; dst != NULL: copies them there,
  *                    dst == NULL: only reads.  sink as above.
+ * sl_peak_gemm_loop  the LDS-to-MFMA loop of a 256 x 256 bf16 GEMM tile alone: `workgroups` x 4
+ *                    waves (wave tile 128 x 128) over `tiles` k-tiles of 32, fragments from LDS;
+ *                    with_loads != 0 adds the GEMM's per-k-tile direct global-to-LDS loads (from
+ *                    src: device memory of at least 1 MiB, L2-resident), their waits and a
+ *                    barrier.  sl_peak_gemm_loop_flops gives the FLOPs.  sink as above.
  */
 sl_status sl_peak_mfma(int workgroups, int iters, float* sink, sl_stream stream);
 double sl_peak_mfma_flops(int workgroups, int iters);
 sl_status sl_peak_stream(const void* src, void* dst, size_t bytes, int workgroups, float* sink, sl_stream stream);
+sl_status sl_peak_gemm_loop(int workgroups, int tiles, int with_loads, const void* src, float* sink,
+                            sl_stream stream);
+double sl_peak_gemm_loop_flops(int workgroups, int tiles);
 
 #ifdef __cplusplus
 }

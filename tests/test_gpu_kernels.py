@@ -331,6 +331,7 @@ ATTN_CASES = [
     ("bf16", 128, 16, 1024, [640]),       # several query tiles per head, no split
     ("bf16", 128, 32, 1024, [1024]),      # 128-query workgroups (two key groups)
     ("bf16", 128, 32, 1024, [600, 500]),  # same, ragged tails in both sequences
+    ("bf16", 128, 32, 576, [560]),        # nine key tiles: one key group has none in the last round
     ("bf16", 64, 2, 128, [1, 128, 70]),
     ("bf16", 32, 4, 64, [64]),
     ("f32", 32, 4, 64, [64, 3]),
@@ -410,6 +411,7 @@ ATTN_EXCL_CASES = [
     ("bf16", 128, 32, 1024, [200, 180], "ends"),
     ("bf16", 128, 16, 1024, [200], "ends"),
     ("bf16", 128, 32, 1024, [1024], "random"),
+    ("bf16", 128, 32, 576, [560], "ends"),
     ("bf16", 64, 2, 128, [1, 128, 70], "random"),
     ("f32", 128, 2, 192, [150], "random"),
     ("f32", 32, 4, 128, [3, 64], "first"),

@@ -63,6 +63,95 @@ stream_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n16
   if (acc == 0x9e3779b9u) sink[threadIdx.x] = (float)acc;
 }
 
+// The LDS-to-MFMA loop of a 256 x 256 GEMM tile on its own: 4 waves (one per SIMD), wave
+// tile 128 x 128 (16 accumulators of v_mfma_f32_32x32x16_bf16), 64-byte k-tile rows swizzled
+// as the GEMM's, the next k-step's 8 fragments read between the current step's 16 MFMAs.
+// LOADS adds what the GEMM's k-tile loop adds around it: per k-tile 8 direct global-to-LDS
+// loads of 1 KB per wave into a spare 4-stage ring (from a 1 MiB L2-resident source), the wait
+// for the loads of three tiles back, and a workgroup barrier.  The gap between the two rates
+// and the GEMM's own is what operand latency from beyond the L2 costs.
+typedef __attribute__((address_space(3))) void peak_lds_t;
+typedef __attribute__((address_space(1))) void peak_glb_t;
+
+template <bool LOADS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_loop_kernel(int tiles, const u32x4* __restrict__ src, float* sink) {
+  __shared__ __attribute__((aligned(1024))) char lds[160 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int wm = wid >> 1, wn = wid & 1;
+  for (int i = tid; i < 32 * 1024 / 16; i += 256)
+    ((u32x4*)lds)[i] = u32x4{0x3f803f80u ^ (uint32_t)i, 0x3f003f00u, 0x3e803e80u, 0x3f803f80u};
+  __syncthreads();
+  const char* as = lds;
+  const char* bs = lds + 16384;
+  char* ring = lds + 32768;                                     // 4 stages of 32 KB
+  const u32x4* gsrc = src + (size_t)(blockIdx.x & 31) * (32 * 1024 / 16);
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  u32x4 fa[2][4], fb[2][4];
+  auto rd = [&](int ks, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + l32;
+      fa[buf][i] = *(const u32x4*)(as + r * 64 + (swz<64>(r, 2 * (ks & 1) + hl) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + j * 32 + l32;
+      fb[buf][j] = *(const u32x4*)(bs + r * 64 + (swz<64>(r, 2 * (ks & 1) + hl) << 4));
+    }
+  };
+  auto issue = [&](int t, int j0, int j1) {
+    char* st = ring + (t & 3) * 32768;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < j0 || j >= j1) continue;
+      __builtin_amdgcn_global_load_lds((peak_glb_t*)(gsrc + (j * 4 + wid) * 64 + lane),
+                                       (peak_lds_t*)(st + (j * 4 + wid) * 1024), 16, 0, 0);
+    }
+  };
+  if (LOADS) { issue(0, 0, 8); issue(1, 0, 8); issue(2, 0, 8); }
+  rd(0, 0);
+  for (int t = 0; t < tiles; ++t) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (LOADS) issue(t + 3, ks * 4, ks * 4 + 4);
+      if (LOADS && ks == 1) {
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));              // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(16)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      rd(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mfma<bf16>::run(acc[i][j], fa[ks & 1][i], fb[ks & 1][j]);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  if (s == 1234.5f) sink[tid] = s + (float)ring[tid];
+}
+
 }  // namespace sl
 
 extern "C" {
@@ -84,6 +173,22 @@ sl_status sl_peak_stream(const void* src, void* dst, size_t bytes, int workgroup
   hipLaunchKernelGGL(sl::stream_kernel, dim3(workgroups), dim3(sl::kStreamThreads), 0, (hipStream_t)stream,
                      (const sl::u32x4*)src, (sl::u32x4*)dst, n16, per_block, sink);
   return hipGetLastError() == hipSuccess ? SL_OK : SL_ERR_HIP;
+}
+
+sl_status sl_peak_gemm_loop(int workgroups, int tiles, int with_loads, const void* src, float* sink,
+                            sl_stream stream) {
+  if (workgroups <= 0 || tiles <= 0 || !sink || (with_loads && !src)) return SL_ERR_INVALID;
+  if (with_loads)
+    hipLaunchKernelGGL(sl::gemm_loop_kernel<true>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, tiles,
+                       (const sl::u32x4*)src, sink);
+  else
+    hipLaunchKernelGGL(sl::gemm_loop_kernel<false>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, tiles,
+                       (const sl::u32x4*)src, sink);
+  return hipGetLastError() == hipSuccess ? SL_OK : SL_ERR_HIP;
+}
+
+double sl_peak_gemm_loop_flops(int workgroups, int tiles) {
+  return (double)workgroups * 256.0 * 256.0 * 32.0 * 2.0 * tiles;
 }
 
 }  // extern "C"

@@ -61,7 +61,8 @@ class sl_step_params(C.Structure):
 EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_cache_scatter",
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
            "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_step_workspace_min", "sl_gemm",
-           "sl_gemm_plan", "sl_kl_lock_noalloc", "sl_peak_mfma", "sl_peak_mfma_flops", "sl_peak_stream")
+           "sl_gemm_plan", "sl_kl_lock_noalloc", "sl_peak_mfma", "sl_peak_mfma_flops", "sl_peak_stream",
+           "sl_peak_gemm_loop", "sl_peak_gemm_loop_flops")
 
 _lib = None
 
@@ -98,6 +99,8 @@ def lib():
         "sl_peak_mfma": (i, [i, i, vp, vp]),
         "sl_peak_mfma_flops": (C.c_double, [i, i]),
         "sl_peak_stream": (i, [vp, vp, sz, i, vp, vp]),
+        "sl_peak_gemm_loop": (i, [i, i, i, vp, vp, vp]),
+        "sl_peak_gemm_loop_flops": (C.c_double, [i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -289,6 +292,15 @@ def sl_peak_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
     """Launch the register-only MFMA loop; returns the FLOPs it performs."""
     _check("sl_peak_mfma", lib().sl_peak_mfma(workgroups, iters, _ptr(sink, "sink", torch.float32), _stream(stream)))
     return float(lib().sl_peak_mfma_flops(workgroups, iters))
+
+
+def sl_peak_gemm_loop(workgroups: int, tiles: int, with_loads: bool, src, sink, stream=None) -> float:
+    """Launch the GEMM tile's LDS-to-MFMA loop alone (with_loads: plus its direct loads, waits and
+    barrier, from the L2-resident src); returns the FLOPs it performs."""
+    _check("sl_peak_gemm_loop", lib().sl_peak_gemm_loop(workgroups, tiles, int(bool(with_loads)),
+                                                        _ptr(src, "src", optional=not with_loads),
+                                                        _ptr(sink, "sink", torch.float32), _stream(stream)))
+    return float(lib().sl_peak_gemm_loop_flops(workgroups, tiles))
 
 
 def sl_peak_stream(src, dst, workgroups: int, sink, stream=None):
