@@ -220,6 +220,8 @@ GEMM_CASES = [
     ("qkv", 250, 512, 12288), ("swiglu", 450, 512, 6144), ("resid", 200, 512, 12288), ("logits", 770, 512, 3072),
     ("qkv", 390, 512, 12288), ("swiglu", 200, 512, 18432), ("resid", 700, 512, 6144), ("logits", 450, 512, 12288),
     ("qkv", 520, 512, 6144), ("resid", 900, 512, 8192),
+    # more than 8 row tiles: the tile order walks groups of 8 row tiles, the last group partial
+    ("logits", 2400, 512, 2048), ("swiglu", 2300, 512, 4096), ("resid", 2200, 512, 2048), ("qkv", 2400, 512, 1536),
 ]
 # (tile rows, tile columns, weights through registers instead of direct-to-LDS loads)
 ALL_TILES = {(256, 256, 0), (256, 128, 0), (128, 256, 0), (128, 128, 0), (128, 64, 0), (256, 192, 0), (128, 384, 0),
