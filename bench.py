@@ -117,19 +117,22 @@ def gpu_part(args):
         states[M] = (st, st.struct())
     p_layer = S.sl_step_params(0.0, -1.0, -1, 0, 0)
 
-    # ---------------- KL-lock inputs (2 logits copies)
+    # ---------------- KL-lock inputs: the two posterior buffers of the sampler loop (X1 = X0 plus a
+    # small drift) and their per-position LSE stores.  Pass i reads X[i%2] as the current posterior
+    # and X[(i+1)%2] as the previous one, whose LSE the pass before stored in L[(i+1)%2], and stores
+    # its own in L[i%2]: the loop's steady state, in which each posterior's LSE is computed once, by
+    # the pass that first sees it.  An untimed pass over X1 first stands for the step before.
     locked_np, act_idx_np, act_off_np = W.kl_lock_mask(N_KL, 1, 0.6, 0)
     M_kl = int(act_off_np[-1])
-    kl_sets = []
-    for sidx in range(2):
-        cur = torch.randn((N_KL, V_KL), generator=g, device=dev, dtype=torch.float32).mul_(2.0)
-        rows = torch.randperm(N_KL, generator=g, device=dev)[: int(round(0.7 * N_KL))]
-        toks = torch.randint(0, V_KL, (rows.numel(),), generator=g, device=dev)
-        cur[rows, toks] += 8.0
-        prev = (cur + 0.05 * torch.randn((N_KL, V_KL), generator=g, device=dev, dtype=torch.float32)).to(bf)
-        kl_sets.append((cur.to(bf), prev))
-        del cur
-        torch.cuda.empty_cache()
+    x0 = torch.randn((N_KL, V_KL), generator=g, device=dev, dtype=torch.float32).mul_(2.0)
+    rows = torch.randperm(N_KL, generator=g, device=dev)[: int(round(0.7 * N_KL))]
+    toks = torch.randint(0, V_KL, (rows.numel(),), generator=g, device=dev)
+    x0[rows, toks] += 8.0
+    x1 = (x0 + 0.05 * torch.randn((N_KL, V_KL), generator=g, device=dev, dtype=torch.float32)).to(bf)
+    kl_x = [x0.to(bf), x1]
+    del x0
+    torch.cuda.empty_cache()
+    kl_lse = [torch.zeros(N_KL, device=dev) for _ in range(2)]
     kl_locked0 = torch.from_numpy(locked_np).to(dev)
     kl_locked = kl_locked0.clone()
     kl_ai = torch.from_numpy(act_idx_np).to(dev)
@@ -141,10 +144,16 @@ def gpu_part(args):
     kl_nao = torch.empty(2, dtype=torch.int32, device=dev)
     kl_ws = torch.empty(sl.sl_kl_lock_workspace_size(1, N_KL, M_kl, V_KL), dtype=torch.uint8, device=dev)
 
-    def kl_call(i):
-        cur, prev = kl_sets[i % 2]
-        sl.sl_kl_lock(cur, prev, V_KL, kl_ai, kl_ao, 1, N_KL, M_kl, None, EPS_KL, GATE_KL, -1, True, kl_locked,
-                      kl_out["kl"], kl_out["u"], kl_out["lse"], kl_am, kl_out["conf"], kl_thr, kl_nai, kl_nao, kl_ws)
+    def kl_call(i, cached=True):
+        c, p = i % 2, (i + 1) % 2
+        sl.sl_kl_lock(kl_x[c], kl_x[p], V_KL, kl_ai, kl_ao, 1, N_KL, M_kl, None, EPS_KL, GATE_KL, -1, True, kl_locked,
+                      kl_out["kl"], kl_out["u"], kl_out["lse"], kl_am, kl_out["conf"], kl_thr, kl_nai, kl_nao, kl_ws,
+                      lse_prev=kl_lse[p] if cached else None, lse_pos=kl_lse[c])
+
+    # the step before the first timed one: the pass over X1 (no previous posterior) stores its LSE
+    sl.sl_kl_lock(kl_x[1], None, V_KL, kl_ai, kl_ao, 1, N_KL, M_kl, None, 0.0, -1.0, -1, False, kl_locked.clone(),
+                  kl_out["kl"], kl_out["u"], kl_out["lse"], kl_am, kl_out["conf"], kl_thr, kl_nai, kl_nao, kl_ws,
+                  lse_pos=kl_lse[1])
 
     def layer_call(i, M):
         st, sst = states[M]
@@ -173,6 +182,16 @@ def gpu_part(args):
     ms_M = {M: float(np.median([evs[i][M][0].elapsed_time(evs[i][M][1]) for i in range(args.warmup, n_it)])) for M in MS}
     ms_kl = float(np.median([evk[i][0].elapsed_time(evk[i][1]) for i in range(args.warmup, n_it)]))
     M_after = int(kl_nao[1].item())
+    # the same pass recomputing the previous posterior's LSE from its logits (no store)
+    ekr = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        kl_call(i, cached=False)
+        e1.record()
+        ekr.append((e0, e1))
+    torch.cuda.synchronize()
+    ms_kl_recompute = float(np.median([a.elapsed_time(b) for a, b in ekr[args.warmup:]]))
 
     # ---------------- the no-KV-cache ablation on the same active sets: attention over the M
     # active positions instead of all N (outside `value`)
@@ -247,7 +266,9 @@ def gpu_part(args):
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "per_M": per_M,
         "kl_lock": {"ms": round(ms_kl, 4), "gbs": round(kb / (ms_kl * 1e-3) / 1e9, 1), "bytes": kb, "M": M_kl,
-                    "M_after": M_after, "frac_hbm_peak": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                    "M_after": M_after, "frac_hbm_peak": round(kb / (ms_kl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "previous_lse": "from the store of the pass that produced the previous posterior",
+                    "ms_recomputing_previous_lse": round(ms_kl_recompute, 4)},
         "kernels_ms_M1024": {k: round(v, 4) for k, v in br.items()},
         "ablation_no_kv_cache_ms": {str(M): round(v, 4) for M, v in ms_abl.items()},
         "roofline": {"kernel": "gemm_kernel<bf16,%dx%d,split %d,EPI_SWIGLU> (FFN gate/up + SwiGLU, M=1024)" % gu_plan,
@@ -302,7 +323,7 @@ def e2e_loop(runs=SURELOCK_RUNS, steps=128, N=512, n_prompt=128, unmask=3, B=1, 
     out = {}
     for name, eps, gate, no_kv in runs:
         st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).to(dev),
-                            cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).to(dev))
+                            cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).to(dev), cached_lse=True)
         Ms, ms = [], []
         loop, n_graphs = None, 0
         if captured:
@@ -624,26 +645,12 @@ def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
     vc = randn((1, B, N, H, DH), 1.0)
     locked0 = torch.from_numpy(locked_np).to(dev)
     st = sl.DeviceState(model, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc,
-                        cand=torch.ones(B * N, dtype=torch.uint8, device=dev))
+                        cand=torch.ones(B * N, dtype=torch.uint8, device=dev), cached_lse=True)
     st_l = sl.DeviceState(model_l, B, N, locked=locked0.clone(), h_in=h_in, k_cache=kc, v_cache=vc)
     st_hm = sl.DeviceState(model_l, B, N, locked=locked0.clone(), h_in=h_in, kv_head_major=True,
                            k_cache=kc.permute(0, 1, 3, 2, 4).contiguous(), v_cache=vc.permute(0, 1, 3, 2, 4).contiguous())
     assert st.M_tot == M_tot and st_l.M_tot == M_tot and st_hm.M_tot == M_tot
     ai0, ao0 = st.act_idx.clone(), st.act_off.clone()
-    # previous posterior: this step's logits (t = 0, no lock) plus drift, in buffer 0
-    st.step(0.0, do_lock=False)
-    for r0 in range(0, B * N, 1024):
-        blk = st.logits[0][r0:r0 + 1024]
-        blk.copy_((blk.float() + 0.05 * torch.randn(blk.shape, generator=g, device=dev)).to(bf))
-    st.t = 1
-    sst = st.struct()
-    sst.m_tot_host = None                     # no host copy of M: nothing to wait for inside the timing
-    p_full = S.sl_step_params(eps, gate, -1, 1, 0)
-    p_fused = S.sl_step_params(eps, gate, -1, 1, 0, 0, 0, 1)   # LM head computes the vocabulary statistics
-    sst_l = st_l.struct()
-    sst_hm = st_hm.struct()
-    p_layer = S.sl_step_params(0.0, -1.0, -1, 0, 0)
-    x = randn((M_tot, D), 1.0)
     kl_o = {k: torch.empty(M_tot, device=dev) for k in ("kl", "u", "lse", "conf")}
     kl_am = torch.empty(M_tot, dtype=torch.int32, device=dev)
     kl_thr = torch.empty(B, device=dev)
@@ -651,6 +658,28 @@ def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
     kl_nao = torch.empty(B + 1, dtype=torch.int32, device=dev)
     kl_lk = locked0.clone()
     kl_ws = torch.empty(sl.sl_kl_lock_workspace_size(B, N, M_tot, V), dtype=torch.uint8, device=dev)
+    kl_lse = torch.empty(B * N, device=dev)
+    # previous posterior: this step's logits (t = 0, eps = 0: nothing locks) plus drift, in buffer 0,
+    # and its LSE in the store beside it, as the pass of the step that produced it leaves it
+    st.step(0.0)
+    for r0 in range(0, B * N, 1024):
+        blk = st.logits[0][r0:r0 + 1024]
+        blk.copy_((blk.float() + 0.05 * torch.randn(blk.shape, generator=g, device=dev)).to(bf))
+    sl.sl_kl_lock(st.logits[0], None, V, ai0, ao0, B, N, M_tot, None, 0.0, -1.0, -1, False, kl_lk.clone(),
+                  kl_o["kl"], kl_o["u"], kl_o["lse"], kl_am, kl_o["conf"], kl_thr, kl_nai, kl_nao, kl_ws,
+                  lse_pos=st.lse_pos[0])
+    st.t = 1
+    sst = st.struct()
+    sst.m_tot_host = None                     # no host copy of M: nothing to wait for inside the timing
+    sst_c = st.struct()                       # takes the previous posterior's LSE from the store
+    sst_c.m_tot_host = None
+    sst.lse_pos[0] = sst.lse_pos[1] = None    # recomputes it from the previous logits
+    p_full = S.sl_step_params(eps, gate, -1, 1, 0)
+    p_fused = S.sl_step_params(eps, gate, -1, 1, 0, 0, 0, 1)   # LM head computes the vocabulary statistics
+    sst_l = st_l.struct()
+    sst_hm = st_hm.struct()
+    p_layer = S.sl_step_params(0.0, -1.0, -1, 0, 0)
+    x = randn((M_tot, D), 1.0)
 
     def restore():
         st.locked.copy_(locked0)
@@ -660,6 +689,7 @@ def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
 
     calls = {
         "step": lambda: S.sl_step(model.s, sst, p_full, st.ws),
+        "step_cached_lse": lambda: S.sl_step(model.s, sst_c, p_full, st.ws),
         "step_fused": lambda: S.sl_step(model.s, sst, p_fused, st.ws),
         "layer": lambda: S.sl_step(model_l.s, sst_l, p_layer, st_l.ws),
         "layer_head_major": lambda: S.sl_step(model_l.s, sst_hm, p_layer, st_hm.ws),
@@ -668,6 +698,10 @@ def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
         "kl_lock": lambda: sl.sl_kl_lock(st.logits[1], st.logits[0], V, ai0, ao0, B, N, M_tot, None, eps, gate, -1,
                                          True, kl_lk, kl_o["kl"], kl_o["u"], kl_o["lse"], kl_am, kl_o["conf"],
                                          kl_thr, kl_nai, kl_nao, kl_ws),
+        "kl_lock_cached_lse": lambda: sl.sl_kl_lock(st.logits[1], st.logits[0], V, ai0, ao0, B, N, M_tot, None, eps,
+                                                    gate, -1, True, kl_lk, kl_o["kl"], kl_o["u"], kl_o["lse"], kl_am,
+                                                    kl_o["conf"], kl_thr, kl_nai, kl_nao, kl_ws,
+                                                    lse_prev=st.lse_pos[0], lse_pos=kl_lse),
     }
     ms = {}
     for name, fn in calls.items():
@@ -694,6 +728,8 @@ def batched_step(steps=50, warmup=10, B=8, N=2048, eps=0.05, gate=0.5):
            "ms_layer": round(ms["layer"], 4), "ms_layer_head_major_cache": round(ms["layer_head_major"], 4),
            "ms_lm_head": round(ms["lm_head"], 4),
            "ms_kl_lock": round(ms["kl_lock"], 4),
+           "ms_step_cached_lse": round(ms["step_cached_lse"], 4),
+           "ms_kl_lock_cached_lse": round(ms["kl_lock_cached_lse"], 4),
            "step_tflops": round((fl_layer + fl_head) / (ms["step"] * 1e-3) / 1e12, 2),
            "layer_tflops": round(fl_layer / (ms["layer"] * 1e-3) / 1e12, 2),
            "lm_head": {"kernel": "gemm_kernel<bf16,%dx%d,split %d,EPI_LOGITS>" % head_plan, "bound": "mfma",
@@ -739,10 +775,14 @@ def profile_kernels():
     ws = torch.empty(sl.sl_kl_lock_workspace_size(1, N_KL, M_kl, V_KL), dtype=torch.uint8, device=dev)
     src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
+    # the previous posterior's LSE, as the pass that produced it stores it (the configuration bench.py times)
+    lse_p, lse_c = torch.zeros(N_KL, device=dev), torch.zeros(N_KL, device=dev)
+    sl.sl_kl_lock(prev, None, V_KL, ai, ao, 1, N_KL, M_kl, None, 0.0, -1.0, -1, False, locked.clone(), o["kl"],
+                  o["u"], o["lse"], am, o["conf"], thr, nai, nao, ws, lse_pos=lse_p)
     for _ in range(3):
         sl.sl_gemm(sl.SL_EPI_SWIGLU, x, Mg, D, 2 * F, wg, wu, out0=act)
         sl.sl_kl_lock(cur, prev, V_KL, ai, ao, 1, N_KL, M_kl, None, EPS_KL, GATE_KL, -1, True, locked, o["kl"],
-                      o["u"], o["lse"], am, o["conf"], thr, nai, nao, ws)
+                      o["u"], o["lse"], am, o["conf"], thr, nai, nao, ws, lse_prev=lse_p, lse_pos=lse_c)
         dst.copy_(src)
     torch.cuda.synchronize()
     print("profiled: gate/up GEMM M=%d plan %s, KL-lock pass M=%d, copy of %d bytes" %

@@ -142,6 +142,14 @@ typedef struct {
  *   cand     [B*N] uint8 or NULL.
  *   locked   [B*N] uint8, in/out (only 0 -> 1 transitions).
  *   kl, u, lse, conf [M_tot] float; argmax [M_tot] int32 (conf/argmax may be NULL).
+ *   lse_pos  [B*N] float or NULL: also receives A at each active position b*N + act_idx[r].
+ *   lse_prev [B*N] float or NULL: B = LSE(prev) at each active position, as an earlier call
+ *            stored it in its lse_pos for these same previous logits.  The pass then reads
+ *            prev only for sum_v p(v) (cur(v) - prev(v)), with KL = that sum - A + B: the
+ *            identity the KL is computed from either way, without recomputing the previous
+ *            posterior's normaliser (the pass that produced prev already did).  The caller
+ *            keeps the pairing (two stores beside two logits buffers, as sl_state does);
+ *            a stale lse_prev gives a wrong KL.  Must not alias lse_pos.
  *   gate_thr [B] float or NULL.
  *   new_act_idx [B*N] capacity, new_act_off [B+1] (may alias act_idx / act_off).
  *   ws       at least sl_kl_lock_workspace_size(...) bytes (any contents).
@@ -151,7 +159,8 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
                      const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
                      const uint8_t* cand, const sl_lock_params* params, uint8_t* locked,
                      float* kl, float* u, float* lse, int32_t* argmax, float* conf,
-                     float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                     const float* lse_prev, float* lse_pos, float* gate_thr,
+                     int32_t* new_act_idx, int32_t* new_act_off,
                      int32_t* m_tot_host, void* ws, size_t ws_bytes, sl_stream stream);
 size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V);
 
@@ -159,7 +168,7 @@ size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V);
  * sl_kl_lock_noalloc — sl_kl_lock for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
  * results and limits as sl_kl_lock, without ws / ws_bytes: the partial sums of the vocabulary
- * pass go to a 128 KiB device array inside the library (one per GPU, held until the process
+ * pass go to a 256 KiB device array inside the library (one per GPU, held until the process
  * ends), which covers every size sl_kl_lock accepts.  No allocation, no memset; nothing in the
  * array needs to start at zero.  Calls that overlap on one GPU (two streams at once) share that
  * array and race: serialise them.  Returns SL_ERR_UNSUPPORTED if a size ever needed more scratch.
@@ -168,7 +177,8 @@ sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logi
                              const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
                              const uint8_t* cand, const sl_lock_params* params, uint8_t* locked,
                              float* kl, float* u, float* lse, int32_t* argmax, float* conf,
-                             float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                             const float* lse_prev, float* lse_pos, float* gate_thr,
+                             int32_t* new_act_idx, int32_t* new_act_off,
                              int32_t* m_tot_host, sl_stream stream);
 
 /*
@@ -272,6 +282,12 @@ typedef struct {
                             head's keys are one run of N * Dh elements).  The cache-layout study of
                             gist.science/nl §5 (optimised cache layouts); sl_attn_active and
                             sl_cache_scatter take token-major caches. */
+  float* lse_pos[2];     /* [B*N] float each, or both NULL: per-position LSE store beside logits[2].
+                            Step t writes the LSE of each active row's logits to lse_pos[t%2], and
+                            from t = 1 on takes the previous posterior's LSE from lse_pos[(t+1)%2]
+                            instead of recomputing it from logits[(t+1)%2] (see sl_kl_lock).  Every
+                            step that writes logits must then run the vocabulary pass: a step with
+                            the LM head and do_lock = 0 is rejected. */
 } sl_state;
 
 typedef struct {

@@ -43,7 +43,7 @@ def test_status_strings_and_host_checks():
     assert st == 1
     p = S.sl_lock_params(0.01, 0.5, -1, 1)
     st = L.sl_kl_lock(7, None, None, 8, None, None, 1, 8, 0, None, ctypes.byref(p), None, None, None, None,
-                      None, None, None, None, None, None, None, 0, None)
+                      None, None, None, None, None, None, None, None, None, 0, None)
     assert st == 1 and b"dtype" in L.sl_last_error()
     # unsupported head_dim
     st = L.sl_attn_active(0, None, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, 1, 64, 0, 1,

@@ -60,7 +60,10 @@ def test_compact_rejects_bad_args():
 
 
 # ------------------------------------------------------------------ KL-lock pass
-def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True):
+def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True, cached_lse=False):
+    """cached_lse: the previous posterior's LSE comes from the per-position store that a pass over
+    the previous logits (as that step's current ones) wrote, as in the sampler loop; the store this
+    pass writes is checked against its per-row lse output."""
     sl = _sl()
     B, N, V, M = case.B, case.N, case.V, case.M_tot
     dt = tdtype(case.dtype)
@@ -83,10 +86,27 @@ def _run_kl(case, eps, gate_q, mask_id, have_prev, unlock_rows_nan=True):
     ws = torch.full((sl.sl_kl_lock_workspace_size(B, N, M, V),), 0xA5, dtype=torch.uint8, device="cuda")
     cand = None if case.cand is None else torch.from_numpy(case.cand).cuda()
     m = sl.PinnedInt()
+    lse_prev = lse_pos = None
+    if cached_lse:
+        # the previous step's pass: prev as its current logits (nothing locks, only the store matters)
+        lse_prev = torch.full((B * N,), float("nan"), device="cuda")
+        lse_pos = torch.full((B * N,), float("nan"), device="cuda")
+        scratch = {k: torch.empty_like(v) for k, v in out.items()}
+        sl.sl_kl_lock(prev, None, V, ai, ao, B, N, M, None, 0.0, -1.0, mask_id, False, locked.clone(),
+                      scratch["kl"], scratch["u"], scratch["lse"], scratch["argmax"], scratch["conf"],
+                      scratch["gate_thr"], torch.empty_like(nai), torch.empty_like(nao), ws, lse_pos=lse_prev)
     Mn = sl.sl_kl_lock(cur, prev, V, ai, ao, B, N, M, cand, eps, gate_q, mask_id, have_prev, locked,
                        out["kl"], out["u"], out["lse"], out["argmax"], out["conf"], out["gate_thr"], nai, nao,
-                       ws, m)
+                       ws, m, lse_prev=lse_prev, lse_pos=lse_pos)
     res = {k: v.cpu().numpy() for k, v in out.items()}
+    if cached_lse:
+        lp, lc = lse_prev.cpu().numpy(), lse_pos.cpu().numpy()
+        inactive = np.ones(B * N, bool)
+        inactive[glob] = False
+        # this pass's store holds exactly its per-row LSE at the active positions, nothing elsewhere
+        np.testing.assert_array_equal(lc[glob], res["lse"][:M])
+        assert np.all(np.isnan(lc[inactive])) and np.all(np.isnan(lp[inactive]))
+        res["lse_prev_store"] = lp[glob]
     res["locked"] = locked.cpu().numpy()
     res["act_idx"] = nai.cpu().numpy()
     res["act_off"] = nao.cpu().numpy()
@@ -136,6 +156,21 @@ def test_kl_lock_parity(N, V, B, lf, dtype, eps, gq, mask, hp, cf):
         np.testing.assert_array_equal(g["locked"], case.locked)
 
 
+@pytest.mark.parametrize("N,V,B,lf,dtype,eps,gq,mask,hp,cf", [c for c in KL_CASES if c[8]])
+def test_kl_lock_parity_cached_prev_lse(N, V, B, lf, dtype, eps, gq, mask, hp, cf):
+    """The same cases with the previous posterior's LSE taken from the per-position store of the
+    pass that produced it (the previous logits are then read only for sum p (a - b))."""
+    say("kl_lock cached lse", N, V, B, lf, dtype, eps, gq, mask, hp, cf)
+    case = W.kl_lock_case(N=N, V=V, B=B, locked_frac=lf, dtype=dtype, cand_frac=cf, key=N + V)
+    g = _run_kl(case, eps, gq, mask, hp, cached_lse=True)
+    st, lr = _oracle_kl(case, eps, gq, mask, hp)
+    _compare_kl(case, g, st, lr, eps, gq, hp)
+    if case.M_tot > 0:
+        # the stored previous LSE is the oracle's LSE of the previous logits
+        ref = O.posterior_stats(O.widen(case.prev, case.dtype), None, mask).lse
+        np.testing.assert_allclose(g["lse_prev_store"], ref, rtol=2e-6, atol=2e-5)
+
+
 def test_kl_lock_repeat_reuses_workspace():
     """Two calls in a row on one (garbage-filled) workspace give the same, correct result."""
     say("kl_lock repeat")
@@ -157,6 +192,19 @@ def test_kl_lock_full_size():
     nd = _compare_kl(case, g, st, lr, 0.01, 0.5, True)
     say("full-size KL-lock: new locks gpu %d oracle %d, exempt mismatches %d" % (
         int(g["locked"].sum() - case.locked.sum()), int(lr.locked.sum() - case.locked.sum()), nd))
+    assert nd == 0
+
+
+@pytest.mark.slow
+def test_kl_lock_full_size_cached_prev_lse():
+    """The full-size KL-lock workload in the loop's steady state: the previous posterior's LSE from the
+    store of the pass that produced it (the configuration the benchmark times)."""
+    say("kl_lock full size, cached previous LSE")
+    case = W.kl_lock_case()
+    g = _run_kl(case, 0.01, 0.5, -1, True, cached_lse=True)
+    st, lr = _oracle_kl(case, 0.01, 0.5, -1, True)
+    nd = _compare_kl(case, g, st, lr, 0.01, 0.5, True)
+    say("full-size KL-lock, cached LSE: exempt mismatches %d" % nd)
     assert nd == 0
 
 

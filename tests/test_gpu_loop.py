@@ -28,9 +28,9 @@ def _model(sl, dm, N, seed_key=0):
                           embed=dev(emb, dm.dtype), lm_head=dev(head, dm.dtype), rope_n=N)
 
 
-def _state(sl, model, dm, B, N, tok0):
+def _state(sl, model, dm, B, N, tok0, cached_lse=False):
     return sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
-                          cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+                          cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda(), cached_lse=cached_lse)
 
 
 def _snapshot(st):
@@ -49,14 +49,16 @@ LOOPS = [
 ]
 
 
-@pytest.mark.parametrize("dm,B,N,T,eps,gate,k", LOOPS)
-def test_captured_loop_matches_host_loop(dm, B, N, T, eps, gate, k):
+@pytest.mark.parametrize("dm,B,N,T,eps,gate,k,cached", [c + (False,) for c in LOOPS] + [LOOPS[2] + (True,)])
+def test_captured_loop_matches_host_loop(dm, B, N, T, eps, gate, k, cached):
+    """cached: both loops keep the per-position LSE store (the previous posterior's LSE from the step
+    that produced it), so the graphs also alternate between the two stores."""
     import token_locking_sparse_amd as sl
-    say("captured loop", dm.d, dm.dtype, B, N, T, eps, gate, k)
+    say("captured loop", dm.d, dm.dtype, B, N, T, eps, gate, k, cached)
     model = _model(sl, dm, N)
     tok0 = W.prompt_tokens(dm, B, N, 16)
     # host-driven: every step reads the count back
-    ref = _state(sl, model, dm, B, N, tok0)
+    ref = _state(sl, model, dm, B, N, tok0, cached)
     ms_ref = []
     for t in range(T):
         ms_ref.append(ref.M_tot)
@@ -64,7 +66,7 @@ def test_captured_loop_matches_host_loop(dm, B, N, T, eps, gate, k):
     r = _snapshot(ref)
     # device-resident: the first step eager, then graph replays; a small bucket so that the
     # capacity shrinks (and new graphs are captured) as the loop goes on
-    st = _state(sl, model, dm, B, N, tok0)
+    st = _state(sl, model, dm, B, N, tok0, cached)
     st.step(eps, gate, dm.mask_id, True, k)
     loop = sl.CapturedLoop(st, eps, gate, dm.mask_id, k, bucket=16)
     m_hist = torch.full((T,), -1, dtype=torch.int32, device="cuda")
@@ -79,6 +81,8 @@ def test_captured_loop_matches_host_loop(dm, B, N, T, eps, gate, k):
     for key in ("tok", "locked", "lock_step", "act_off", "act_idx"):
         np.testing.assert_array_equal(g[key], r[key], err_msg=key)
     assert torch.equal(g["l0"], r["l0"]) and torch.equal(g["l1"], r["l1"])
+    if cached:
+        assert torch.equal(st.lse_pos[0], ref.lse_pos[0]) and torch.equal(st.lse_pos[1], ref.lse_pos[1])
     assert int((g["lock_step"] > 0).sum()) > 0          # positions locked at steps the graphs ran
     assert len(loop.graphs) >= 2
 

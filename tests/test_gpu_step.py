@@ -522,8 +522,13 @@ LOOP_RULES = {"surelock": (0.05, -1.0, False), "gate_only": (math.inf, 0.5, Fals
 FUSED_RULES = {"surelock": True, "gate_only": True, "no_kv_cache": False}
 
 
-@pytest.mark.parametrize("rule,fuse", [(r, f) for r in LOOP_RULES for f in ((False, True) if FUSED_RULES[r] else (False,))])
-def test_tiny_loop_teacher_forced(rule, fuse):
+LOOP_CASES = ([(r, f, False) for r in LOOP_RULES for f in ((False, True) if FUSED_RULES[r] else (False,))]
+              # with the per-position LSE store (the previous posterior's LSE from the step that made it)
+              + [("surelock", False, True), ("gate_only", False, True), ("surelock", True, True)])
+
+
+@pytest.mark.parametrize("rule,fuse,cached_lse", LOOP_CASES)
+def test_tiny_loop_teacher_forced(rule, fuse, cached_lse):
     """2-layer fp32 model, d=128, 4x32 heads, FFN 384, V=512, N=64 (16 prompt + 48 masked),
     16 steps, 3 unmasks per step; eps=0.05 with the gate off, or one of the ablations."""
     sl = _sl()
@@ -533,7 +538,7 @@ def test_tiny_loop_teacher_forced(rule, fuse):
     layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
     model = _dev_model(dm, layers, emb, head, rope_n=N)
     st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
-                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda())
+                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda(), cached_lse=cached_lse)
     ost = O.OracleState(B=B, N=N, t=0, locked=np.zeros(B * N, np.uint8),
                         kc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
                         vc=[np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
@@ -641,6 +646,23 @@ def test_tiny_loop_free_running_against_oracle(rule):
                 near_token = top2[1] - top2[0] <= 1e-4          # both picked it, argmax near a tie
                 assert near_pick or near_token, "free-running divergence at step %d: pick %d" % (t, gp)
     say("free-running %s: M_t %s; first divergence: %s" % (rule, Ms, "none" if first is None else "step %d" % first))
+
+
+def test_step_with_lse_store_requires_the_vocabulary_pass():
+    """With the per-position LSE store, a step that writes logits without the vocabulary pass would
+    leave the next step a stale LSE: it is refused on the host, before any launch."""
+    sl = _sl()
+    dm = W.TINY
+    B, N = 1, 64
+    layers, emb, head, om, tok0 = _tiny_setup(dm, B, N, 16)
+    model = _dev_model(dm, layers, emb, head, rope_n=N)
+    st = sl.DeviceState(model, B, N, tok=torch.from_numpy(tok0.copy()).cuda(),
+                        cand=torch.from_numpy((tok0 != dm.mask_id).astype(np.uint8)).cuda(), cached_lse=True)
+    before = st.logits[0].clone()
+    with pytest.raises(sl.SureLockError, match="do_lock"):
+        st.step(0.05, -1.0, dm.mask_id, False, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(st.logits[0], before) and st.t == 0
 
 
 def test_step_with_every_position_locked_is_a_no_op():

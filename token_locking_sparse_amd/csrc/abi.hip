@@ -128,11 +128,11 @@ sl_status check_model(const sl_model* m) {
 
 // Scratch memory of sl_kl_lock_noalloc: the vocabulary pass's per-segment partial sums live in this
 // file-scope device array instead of a caller workspace.  Every (M_tot, V) needs at most
-// (M_tot * ceil(2048 / M_tot)) * 32 < 4096 * 32 bytes of partials (one segment per row once
-// M_tot >= 2048), so 128 KiB covers every size sl_kl_lock accepts.  Each device holds its own
+// (M_tot * ceil(6144 / M_tot)) * 32 < 8192 * 32 bytes of partials (rows are split only while
+// M_tot < 2048), so 256 KiB covers every size sl_kl_lock accepts.  Each device holds its own
 // copy; host code reaches it only through the address hipGetSymbolAddress returns for the current
 // device (the array's name on the host is not a device address).
-constexpr size_t kNoAllocScratchBytes = 128 * 1024;
+constexpr size_t kNoAllocScratchBytes = 256 * 1024;
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
@@ -244,9 +244,9 @@ size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V) {
 sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
                      const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
                      const uint8_t* cand, const sl_lock_params* params, uint8_t* locked, float* kl,
-                     float* u, float* lse, int32_t* argmax, float* conf, float* gate_thr,
-                     int32_t* new_act_idx, int32_t* new_act_off, int32_t* m_tot_host, void* ws,
-                     size_t ws_bytes, sl_stream stream) {
+                     float* u, float* lse, int32_t* argmax, float* conf, const float* lse_prev,
+                     float* lse_pos, float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                     int32_t* m_tot_host, void* ws, size_t ws_bytes, sl_stream stream) {
   g_err[0] = 0;
   sl_status st = check_dtype(dtype);
   if (st != SL_OK) return st;
@@ -263,7 +263,9 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
   SL_REQUIRE(params->mask_id < V, SL_ERR_INVALID, "mask_id >= V");
   const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
   SL_REQUIRE(ws_bytes >= need, SL_ERR_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
-  sl::KLRowParams rp{logits_cur, logits_prev, V, kl, u, lse, argmax, conf};
+  SL_REQUIRE(!(lse_prev && lse_pos) || lse_prev != lse_pos, SL_ERR_INVALID,
+             "lse_prev and lse_pos are the same buffer (keep two, as for the logits)");
+  sl::KLRowParams rp{logits_cur, logits_prev, V, kl, u, lse, argmax, conf, lse_prev, lse_pos};
   sl::TailParams tp{};
   tp.B = B; tp.N = N; tp.M_tot = M_tot;
   tp.eps = params->eps; tp.gate_q = params->gate_q; tp.mask_id = params->mask_id;
@@ -285,8 +287,9 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
 sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logits_prev, int V,
                              const int32_t* act_idx, const int32_t* act_off, int B, int N, int M_tot,
                              const uint8_t* cand, const sl_lock_params* params, uint8_t* locked, float* kl,
-                             float* u, float* lse, int32_t* argmax, float* conf, float* gate_thr,
-                             int32_t* new_act_idx, int32_t* new_act_off, int32_t* m_tot_host, sl_stream stream) {
+                             float* u, float* lse, int32_t* argmax, float* conf, const float* lse_prev,
+                             float* lse_pos, float* gate_thr, int32_t* new_act_idx, int32_t* new_act_off,
+                             int32_t* m_tot_host, sl_stream stream) {
   g_err[0] = 0;
   SL_REQUIRE(B >= 1 && N >= 1 && V > 0 && M_tot >= 0, SL_ERR_INVALID, "bad size");
   const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
@@ -296,8 +299,8 @@ sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logi
   sl_status st = scratch_ptr(&ws);
   if (st != SL_OK) return st;
   return sl_kl_lock(dtype, logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, params, locked, kl, u,
-                    lse, argmax, conf, gate_thr, new_act_idx, new_act_off, m_tot_host, ws, kNoAllocScratchBytes,
-                    stream);
+                    lse, argmax, conf, lse_prev, lse_pos, gate_thr, new_act_idx, new_act_off, m_tot_host, ws,
+                    kNoAllocScratchBytes, stream);
 }
 
 sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_stream stream) {
@@ -390,6 +393,11 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
     SL_REQUIRE(p->gate_q <= 1.f, SL_ERR_INVALID, "gate_q > 1");
     SL_REQUIRE(p->mask_id < m->vocab, SL_ERR_INVALID, "mask_id >= vocab");
   }
+  const bool lse_store = st->lse_pos[0] && st->lse_pos[1];
+  SL_REQUIRE(!(st->lse_pos[0] || st->lse_pos[1]) || lse_store, SL_ERR_INVALID, "only one lse_pos buffer");
+  SL_REQUIRE(!lse_store || st->lse_pos[0] != st->lse_pos[1], SL_ERR_INVALID, "lse_pos buffers alias");
+  SL_REQUIRE(!(lse_store && head && !lock), SL_ERR_INVALID,
+             "with lse_pos set every step that writes logits must run the vocabulary pass (do_lock = 1)");
   if (lock && p->unmask_k > 0) {
     SL_REQUIRE(st->tok && st->cand && st->argmax && st->conf && p->mask_id >= 0, SL_ERR_INVALID,
                "sampler needs tok, cand, argmax, conf and a mask id");
@@ -473,8 +481,12 @@ sl_status sl_step(const sl_model* m, sl_state* st, const sl_step_params* p, void
     }
   }
   if (lock) {
+    // with the per-position LSE store: this step's LSE goes to lse_pos[t%2], and the previous
+    // posterior's is read from lse_pos[(t+1)%2], where step t-1 stored it
     sl::KLRowParams rp{st->logits[st->t & 1], st->logits[(st->t + 1) & 1], m->vocab, st->kl, st->u,
-                       st->lse, st->argmax, st->conf};
+                       st->lse, st->argmax, st->conf,
+                       (lse_store && st->t > 0) ? st->lse_pos[(st->t + 1) & 1] : nullptr,
+                       lse_store ? st->lse_pos[st->t & 1] : nullptr};
     sl::TailParams tp{};
     tp.B = B; tp.N = N; tp.M_tot = M;
     tp.m_dev = m_dev; tp.t_dev = st->t_dev;

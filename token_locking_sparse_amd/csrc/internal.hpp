@@ -51,6 +51,8 @@ struct KLRowParams {
   float* lse;
   int32_t* argmax;  // may be NULL
   float* conf;      // may be NULL
+  const float* lse_prev;  // [B*N] per position: LSE of `prev` from the pass that produced it, or NULL
+  float* lse_pos;         // [B*N] per position: receives this pass's LSE, or NULL
 };
 
 // Workspace of the vocabulary pass: per-segment partials of split rows.

@@ -12,13 +12,17 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "klpart.hpp"
 
 namespace sl {
 
-constexpr int kKLThreads = 512;
+// Workgroups of 4 waves: at the row pass's register use (under 96 VGPRs, 5 waves per SIMD) five of
+// them fit a CU where two of 8 waves would leave a fifth of the wave slots empty.
+constexpr int kKLThreads = 256;
 constexpr int kTailThreads = 1024;
 
 // ------------------------------------------------------------------ compaction
@@ -372,16 +376,54 @@ __device__ __forceinline__ int resolve_argmax(const u32x4& raw, int c, float bes
   return am;
 }
 
+constexpr int GroupChunks = 4;   // chunks per thread per streaming step of the row pass
+
+// Lowest id != mask_id holding `best` in the argmax group g of a row (row bytes at `row`): its
+// chunks g, g + kKLThreads, ... below c1.  INT_MAX when none does.  Every chunk is loaded before
+// any is scanned.
+template <typename T>
+__device__ int resolve_group(const char* row, int g, int c1, float best, int mask_id) {
+  u32x4 raw[GroupChunks];
+#pragma unroll
+  for (int u = 0; u < GroupChunks; ++u)
+    if (g + u * kKLThreads < c1) raw[u] = ld16(row + (size_t)(g + u * kKLThreads) * 16);
+#pragma unroll
+  for (int u = 0; u < GroupChunks; ++u) {
+    if (g + u * kKLThreads < c1) {
+      const int id = resolve_argmax<T>(raw[u], g + u * kKLThreads, best, mask_id);
+      if (id != INT_MAX) return id;   // chunks ascend: the first hit is the lowest id
+    }
+  }
+  return INT_MAX;
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// KL(p || q) of a row from its (combined) partial: with S_a = sum e^(a - max a),
+// A = max a + ln S_a and B the LSE of the previous logits,
+// KL = sum p (a - b) - A + B.  PLSE: B is the partial's mb (known from the pass
+// that produced the previous posterior); otherwise B = mb + ln S_b.
+template <bool PREV, bool PLSE>
+__device__ __forceinline__ float row_kl(const Part& t) {
+  if (!PREV) return INFINITY;
+  if (PLSE) return (t.ta / t.sa - logf(t.sa)) - (t.ma - t.mb);
+  return t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb);
+}
+
 // Row statistics from a (combined) partial whose `bidx` is the exact argmax
-// (INT_MAX: none): with S_a = sum e^(a - max a), A = max a + ln S_a,
-// max p = 1/S_a, KL = sum p (a - b) - A + B.
-template <bool PREV>
-__device__ void finish_row(const KLRowParams& rp, const Part& t, int r) {
+// (INT_MAX: none): A = max a + ln S_a, max p = 1/S_a, and the KL above.  g is
+// the row's position b*N + pos (where the per-position LSE store takes A).
+template <bool PREV, bool PLSE>
+__device__ void finish_row(const KLRowParams& rp, const Part& t, int r, int g) {
   const float A = t.ma + logf(t.sa);
   rp.lse[r] = A;
+  if (rp.lse_pos) rp.lse_pos[g] = A;
   rp.u[r] = 1.f - 1.f / t.sa;
-  if (PREV) rp.kl[r] = t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb);
-  else rp.kl[r] = INFINITY;
+  rp.kl[r] = row_kl<PREV, PLSE>(t);
   if (rp.argmax) rp.argmax[r] = t.bidx == INT_MAX ? 0 : t.bidx;
   if (rp.conf) rp.conf[r] = __expf(t.best - t.ma) / t.sa;
 }
@@ -389,17 +431,22 @@ __device__ void finish_row(const KLRowParams& rp, const Part& t, int r) {
 // Row pass: workgroup (row r, segment) streams its slice of the current and
 // previous logits once.  With one segment per row it finishes the row itself;
 // otherwise it stores its partial for the tail kernel.  No inter-workgroup
-// communication happens inside this kernel.
-template <typename T, bool PREV>
+// communication happens inside this kernel.  PLSE (with PREV): the previous
+// posterior's LSE comes from the pass that produced it (rp.lse_prev), so the
+// previous logits enter only the sum p (a - b): no exponential, maximum or
+// sum of their own.
+template <typename T, bool PREV, bool PLSE>
 __global__ void __launch_bounds__(kKLThreads)
 kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* part) {
   constexpr int E = Chunk<T>::kElems;
   __shared__ Part s_part[kKLThreads / 64];
+  __shared__ int s_id[kKLThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x / n_seg, seg = blockIdx.x - r * n_seg;
   if (r >= rows_live(tp.M_tot, tp.m_dev)) return;   // uniform over the workgroup, before any barrier
   const int b = seq_of_row(tp.act_off, tp.B, r);
   const int64_t g = (int64_t)b * tp.N + tp.act_idx[r];
+  const float lse_b = PLSE ? rp.lse_prev[g] : 0.f;   // consumed after the streaming loop
   const size_t rowbytes = (size_t)rp.V * sizeof(T);
   const char* crow = (const char*)rp.cur + g * rowbytes;
   const char* prow = (const char*)rp.prev + g * rowbytes;
@@ -418,17 +465,40 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
 
   // Groups of U chunks per thread (strided by the workgroup size, so every load
   // instruction of the workgroup covers a contiguous 4 KB): U loads of each row
-  // in flight, one running-max rescale per group.
-  constexpr int U = 4;
-  u32x4 braw = {0u, 0u, 0u, 0u};   // raw bits of chunk acc.bidx
+  // in flight, one running-max rescale per group.  Segments hold whole groups
+  // except at the end of the row, where one last group loads only the chunks
+  // below c1 (the others read as -inf and add nothing), so every thread keeps
+  // U loads per row in flight to the end.  The argmax is tracked per group:
+  // acc.best is the largest value seen over ids != mask_id, acc.bidx the first
+  // chunk of the group that holds it; the exact id is found after the loop,
+  // only by the threads whose value is the workgroup's maximum.
+  constexpr int U = GroupChunks;
+  constexpr uint32_t kNegInfBits = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;   // -inf in every element
   int c = c0 + tid;
-  for (; c + (U - 1) * kKLThreads < c1; c += U * kKLThreads) {
+  auto group = [&](auto partial) {
+    constexpr bool P = decltype(partial)::value;
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ok[u] = !P || c + u * kKLThreads < c1;
+    // past the end: the last chunk again (in bounds), read as -inf
+    uint32_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) off[u] = (uint32_t)(ok[u] ? c + u * kKLThreads : c1 - 1) * 16u;
     u32x4 ra[U], rb[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ra[u] = ld16_stream(crow + (uint32_t)(c + u * kKLThreads) * 16u);
+    for (int u = 0; u < U; ++u) ra[u] = ld16_stream(crow + off[u]);
     if (PREV) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) rb[u] = ld16_stream(prow + (uint32_t)(c + u * kKLThreads) * 16u);
+      for (int u = 0; u < U; ++u) rb[u] = ld16_stream(prow + off[u]);
+    }
+    if (P) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ra[u][q] = ok[u] ? ra[u][q] : kNegInfBits;
+          rb[u][q] = ok[u] ? rb[u][q] : kNegInfBits;
+        }
     }
     float a[U][E];
 #pragma unroll
@@ -441,15 +511,17 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
       for (int j = 1; j < E; ++j) cm[u] = __builtin_fmaxf(cm[u], a[u][j]);
     }
     const float gm = __builtin_fmaxf(__builtin_fmaxf(cm[0], cm[1]), __builtin_fmaxf(cm[2], cm[3]));
+    // the group's maximum over ids != mask_id: the [MASK] chunk, when it is one of the
+    // group's, is left out here and handled after the loop
+    float gx = gm;
+    const unsigned mrel = (unsigned)(mask_chunk - c);
+    if (mrel < (unsigned)(U * kKLThreads) && (mrel & (kKLThreads - 1)) == 0) {
+      gx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {   // selects, not branches; lowest chunk wins ties
-      const float cx = (c + u * kKLThreads == mask_chunk) ? -INFINITY : cm[u];
-      const bool gt = cx > acc.best;
-      acc.bidx = gt ? c + u * kKLThreads : acc.bidx;
-      acc.best = gt ? cx : acc.best;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) braw[q] = gt ? ra[u][q] : braw[q];
+      for (int u = 0; u < U; ++u)
+        if (mrel != (unsigned)(u * kKLThreads)) gx = __builtin_fmaxf(gx, cm[u]);
     }
+    if (gx > acc.best) { acc.best = gx; acc.bidx = c; }   // strictly greater: the earliest group wins
     const float mnew = __builtin_fmaxf(acc.ma, gm);
     const float sc = scale_to(acc.ma, mnew);
     acc.sa *= sc;
@@ -466,84 +538,71 @@ kl_rows_kernel(KLRowParams rp, TailParams tp, int n_seg, int seg_chunks, float* 
         for (int j = 0; j < E; ++j) {
           const float e = __builtin_amdgcn_exp2f(fmaf(a[u][j], kLog2e, -ml));
           acc.sa += e;
-          acc.ta = fmaf(e, a[u][j] - b[u][j], acc.ta);
+          // chunks past the row's end: e = 0, and their a - b (-inf - -inf) must not enter
+          acc.ta = fmaf(e, ok[u] ? a[u][j] - b[u][j] : 0.f, acc.ta);
         }
-      float bm = -INFINITY;
+      if (!PLSE) {
+        float bm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < E; ++j) bm = __builtin_fmaxf(bm, b[u][j]);
-      const float mbn = __builtin_fmaxf(acc.mb, bm);
-      acc.sb *= scale_to(acc.mb, mbn);
-      acc.mb = mbn;
-      const float mbl = mbn * kLog2e;
+          for (int j = 0; j < E; ++j) bm = __builtin_fmaxf(bm, b[u][j]);
+        const float mbn = __builtin_fmaxf(acc.mb, bm);
+        acc.sb *= scale_to(acc.mb, mbn);
+        acc.mb = mbn;
+        const float mbl = mbn * kLog2e;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(b[u][j], kLog2e, -mbl));
+          for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(b[u][j], kLog2e, -mbl));
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < E; ++j) acc.sa += __builtin_amdgcn_exp2f(fmaf(a[u][j], kLog2e, -ml));
     }
-  }
-  // remaining chunks one at a time
-  for (; c < c1; c += kKLThreads) {
-    float a[E], bb[E];
-    const u32x4 rc = ld16_stream(crow + (uint32_t)c * 16u);
-    Chunk<T>::unpack(rc, a);
-    if (PREV) Chunk<T>::unpack(ld16_stream(prow + (uint32_t)c * 16u), bb);
-    float cm = a[0];
-#pragma unroll
-    for (int j = 1; j < E; ++j) cm = __builtin_fmaxf(cm, a[j]);
-    const float cx = (c == mask_chunk) ? -INFINITY : cm;
-    if (cx > acc.best) { acc.best = cx; acc.bidx = c; braw = rc; }
-    const float mnew = __builtin_fmaxf(acc.ma, cm);
-    const float sc = scale_to(acc.ma, mnew);
-    acc.sa *= sc;
-    acc.ta *= sc;
-    acc.ma = mnew;
-    const float ml = mnew * kLog2e;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(a[j], kLog2e, -ml));
-      acc.sa += e;
-      if (PREV) acc.ta = fmaf(e, a[j] - bb[j], acc.ta);
-    }
-    if (PREV) {
-      float bm = bb[0];
-#pragma unroll
-      for (int j = 1; j < E; ++j) bm = __builtin_fmaxf(bm, bb[j]);
-      const float mbn = __builtin_fmaxf(acc.mb, bm);
-      acc.sb *= scale_to(acc.mb, mbn);
-      acc.mb = mbn;
-      const float mbl = mbn * kLog2e;
-#pragma unroll
-      for (int j = 0; j < E; ++j) acc.sb += __builtin_amdgcn_exp2f(fmaf(bb[j], kLog2e, -mbl));
-    }
-  }
-  // the [MASK] chunk, if this thread streamed it: best over its other ids
+  };
+  for (; c + (U - 1) * kKLThreads < c1; c += U * kKLThreads) group(std::false_type{});
+  if (c < c1) group(std::true_type{});
+  // the [MASK] chunk, if this thread streamed it: its largest value over the other ids
+  float mbest = -INFINITY;
+  u32x4 mraw = {0u, 0u, 0u, 0u};
   if (mask_chunk >= c0 && mask_chunk < c1 && (mask_chunk - c0) % kKLThreads == tid) {
     float a[E];
-    const u32x4 rm = ld16(crow + (size_t)mask_chunk * 16);
-    Chunk<T>::unpack(rm, a);
-    float cmn = -INFINITY;
+    mraw = ld16(crow + (size_t)mask_chunk * 16);
+    Chunk<T>::unpack(mraw, a);
     for (int j = 0; j < E; ++j)
-      if (mask_chunk * E + j != mask_id) cmn = __builtin_fmaxf(cmn, a[j]);
-    if (cmn > acc.best || (cmn == acc.best && mask_chunk < acc.bidx)) {
-      acc.best = cmn; acc.bidx = mask_chunk; braw = rm;
-    }
+      if (mask_chunk * E + j != mask_id) mbest = __builtin_fmaxf(mbest, a[j]);
   }
-  acc.bidx = resolve_argmax<T>(braw, acc.bidx, acc.best, mask_id);   // chunk -> exact id
+  const float my_best = acc.best;
+  const int my_grp = acc.bidx;
+  acc.best = __builtin_fmaxf(acc.best, mbest);
+  acc.bidx = INT_MAX;
+  if (PLSE) { acc.mb = lse_b; acc.sb = 0.f; }   // the same on every lane: combine keeps it
   acc = wave_reduce_part(acc);
   if (lane == 0) s_part[wid] = acc;
   __syncthreads();
+  // the workgroup's maximum; the threads holding it find the lowest id with that value
+  float wbest = s_part[0].best;
+#pragma unroll
+  for (int w = 1; w < kKLThreads / 64; ++w) wbest = __builtin_fmaxf(wbest, s_part[w].best);
+  int id = INT_MAX;
+  if (wbest > -INFINITY) {
+    if (my_best == wbest) id = resolve_group<T>(crow, my_grp, c1, wbest, mask_id);
+    if (mbest == wbest) id = min(id, resolve_argmax<T>(mraw, mask_chunk, wbest, mask_id));
+  }
+  id = wave_min_i32(id);
+  if (lane == 0) s_id[wid] = id;
+  __syncthreads();
   if (tid == 0) {
     Part t = s_part[0];
-    for (int w = 1; w < kKLThreads / 64; ++w) t = combine(t, s_part[w]);
-    if (n_seg == 1) finish_row<PREV>(rp, t, r);
-    else store_part(part + ((size_t)seg * tp.M_tot + r) * kPartWords, t);
+    int tid_min = s_id[0];
+    for (int w = 1; w < kKLThreads / 64; ++w) { t = combine(t, s_part[w]); tid_min = min(tid_min, s_id[w]); }
+    t.best = wbest;
+    t.bidx = tid_min;
+    if (n_seg == 1) finish_row<PREV, PLSE>(rp, t, r, (int)g);
+    else store_part(part + ((size_t)seg * tp.M_tot + r) * kPartWords, t, (int)g);
   }
 }
 
@@ -581,7 +640,7 @@ __device__ __forceinline__ u32x4 load_flags16(const uint8_t* f, int p0, int P, u
   return w;
 }
 
-template <typename T, bool PREV>
+template <typename T, bool PREV, bool PLSE>
 __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n_seg, const float* part,
                               TailShared& sh, TailLds& ls) {
   const int tid = threadIdx.x, bd = blockDim.x;
@@ -602,13 +661,14 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
     }
   }
   Part x[kMergeRows][kMaxSeg];
+  int gpos[kMergeRows];   // positions b*N + pos, carried by the first segment's partial
   if (n_seg > 1 && Mt > 0) {   // n_seg > 1 only when M_tot < kMergeRows * blockDim: one round
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
       const int r = min(tid + k * bd, Mt - 1);   // clamped: loads stay in bounds
 #pragma unroll
       for (int s2 = 0; s2 < kMaxSeg; ++s2)
-        if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * Mcap + r) * kPartWords);
+        if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * Mcap + r) * kPartWords, s2 == 0 ? &gpos[k] : nullptr);
     }
   }
   // LDS copies
@@ -631,9 +691,9 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
         if (s2 < n_seg) t = combine(t, x[k][s2]);
       const int r = tid + k * bd;
       if (r < Mt) {
-        finish_row<PREV>(rp, t, r);
+        finish_row<PREV, PLSE>(rp, t, r, gpos[k]);
         ls.u[r] = 1.f - 1.f / t.sa;
-        ls.kl[r] = PREV ? t.ta / t.sa - (t.ma - t.mb) - logf(t.sa / t.sb) : INFINITY;
+        ls.kl[r] = row_kl<PREV, PLSE>(t);
       }
     }
   }
@@ -658,25 +718,27 @@ __device__ void tail_from_lds(const KLRowParams& rp, const TailParams& tp, int n
   }
 }
 
-template <typename T, bool PREV>
+template <typename T, bool PREV, bool PLSE>
 __global__ void __launch_bounds__(kTailThreads)
 kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   __shared__ TailShared sh;
   __shared__ __attribute__((aligned(16))) TailLds ls;
   const int Mt = rows_live(tp.M_tot, tp.m_dev);   // tp.M_tot: capacity and stride of the partials
   if ((long)tp.B * tp.N <= kTailPos && tp.M_tot <= kTailRows && Mt > 0) {
-    tail_from_lds<T, PREV>(rp, tp, n_seg, part, sh, ls);
+    tail_from_lds<T, PREV, PLSE>(rp, tp, n_seg, part, sh, ls);
   } else {
     if (n_seg > 1 && Mt > 0) {
       const int bd = blockDim.x;
       for (int r0 = 0; r0 < Mt; r0 += kMergeRows * bd) {
         Part x[kMergeRows][kMaxSeg];
+        int gpos[kMergeRows];
 #pragma unroll
         for (int k = 0; k < kMergeRows; ++k) {
           const int r = min(r0 + (int)threadIdx.x + k * bd, Mt - 1);   // clamped: loads stay in bounds
 #pragma unroll
           for (int s2 = 0; s2 < kMaxSeg; ++s2)
-            if (s2 < n_seg) x[k][s2] = load_part(part + ((size_t)s2 * tp.M_tot + r) * kPartWords);
+            if (s2 < n_seg)
+              x[k][s2] = load_part(part + ((size_t)s2 * tp.M_tot + r) * kPartWords, s2 == 0 ? &gpos[k] : nullptr);
         }
 #pragma unroll
         for (int k = 0; k < kMergeRows; ++k) {
@@ -685,7 +747,7 @@ kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
           for (int s2 = 1; s2 < kMaxSeg; ++s2)
             if (s2 < n_seg) t = combine(t, x[k][s2]);
           const int r = r0 + (int)threadIdx.x + k * bd;
-          if (r < Mt) finish_row<PREV>(rp, t, r);
+          if (r < Mt) finish_row<PREV, PLSE>(rp, t, r, gpos[k]);
         }
       }
       __syncthreads();
@@ -702,15 +764,35 @@ kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   }
 }
 
-static int kl_nseg(int M_tot, int V, int elem_bytes) {
+// Segments per row: rows are split (into at most kMaxSeg) only while there are fewer than
+// kSplitBelow of them, so that the tail merges every split row in one round (kMergeRows rows per
+// thread), aiming at about 6144 workgroups (24 per CU): short workgroups keep every CU streaming
+// through the ends of the launch.  Partials then take at most M * ceil(6144 / M) < 8192 slots.
+// A segment is a whole number of thread groups (GroupChunks * kKLThreads chunks), so that only
+// the row's last segment ends in a partial group.
+constexpr int kSplitBelow = 2048;
+struct KlSplit {
+  int n_seg, seg_chunks;
+};
+static KlSplit kl_split(int M_tot, int V, int elem_bytes) {
   const int C = V * elem_bytes / 16;
-  if (M_tot <= 0) return 1;
-  const int want = (2048 + M_tot - 1) / M_tot;   // about 2048 workgroups or more
-  const int maxseg = C / (kKLThreads * 4) > 1 ? C / (kKLThreads * 4) : 1;
-  int n = want < maxseg ? want : maxseg;
-  n = n < kMaxSeg ? n : kMaxSeg;
-  return n < 1 ? 1 : n;
+  constexpr int G = GroupChunks * kKLThreads;
+  int n = 1;
+  if (M_tot > 0 && M_tot < kSplitBelow) {
+    const int want = (6144 + M_tot - 1) / M_tot;
+    const int maxseg = C / G > 1 ? C / G : 1;
+    n = want < maxseg ? want : maxseg;
+    n = n < kMaxSeg ? n : kMaxSeg;
+    n = n < 1 ? 1 : n;
+  }
+  int seg = (C + n - 1) / n;
+  seg = (seg + G - 1) / G * G;
+  if (seg <= 0) seg = G;
+  n = (C + seg - 1) / seg;   // no empty segment after the rounding
+  return KlSplit{n < 1 ? 1 : n, seg};
 }
+static int kl_nseg(int M_tot, int V, int elem_bytes) { return kl_split(M_tot, V, elem_bytes).n_seg; }
+static_assert(kSplitBelow <= kMergeRows * kTailThreads, "split rows must merge in one tail round");
 
 size_t kl_part_bytes(int M_tot, int V, int elem_bytes) {
   const int n_seg = kl_nseg(M_tot, V, elem_bytes);
@@ -718,16 +800,15 @@ size_t kl_part_bytes(int M_tot, int V, int elem_bytes) {
   return (size_t)(M_tot > 0 ? M_tot : 1) * n_seg * kPartWords * 4;
 }
 
-template <typename T, bool PREV>
+template <typename T, bool PREV, bool PLSE>
 static void kl_launch_t(const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s) {
-  const int n_seg = kl_nseg(tp.M_tot, rp.V, sizeof(T));
+  const KlSplit sp = kl_split(tp.M_tot, rp.V, sizeof(T));
+  const int n_seg = sp.n_seg;
   if (tp.M_tot > 0) {
-    const int C = rp.V * (int)sizeof(T) / 16;
-    const int seg_chunks = (C + n_seg - 1) / n_seg;
-    hipLaunchKernelGGL((kl_rows_kernel<T, PREV>), dim3((unsigned)tp.M_tot * n_seg), dim3(kKLThreads), 0, s, rp, tp,
-                       n_seg, seg_chunks, part);
+    hipLaunchKernelGGL((kl_rows_kernel<T, PREV, PLSE>), dim3((unsigned)tp.M_tot * n_seg), dim3(kKLThreads), 0, s, rp,
+                       tp, n_seg, sp.seg_chunks, part);
   }
-  hipLaunchKernelGGL((kl_tail_kernel<T, PREV>), dim3(1), dim3(kTailThreads), 0, s, rp, tp,
+  hipLaunchKernelGGL((kl_tail_kernel<T, PREV, PLSE>), dim3(1), dim3(kTailThreads), 0, s, rp, tp,
                      tp.M_tot > 0 ? n_seg : 1, (const float*)part);
 }
 
@@ -737,9 +818,12 @@ static void kl_launch_t(const KLRowParams& rp, const TailParams& tp, float* part
 constexpr int kMergeLoads = 8;
 
 __global__ void __launch_bounds__(256)
-kl_merge_kernel(KLRowParams rp, int M_cap, const int32_t* __restrict__ m_dev, int n_vt, const float* __restrict__ klp) {
+kl_merge_kernel(KLRowParams rp, TailParams tp, int n_vt, const float* __restrict__ klp) {
+  const int M_cap = tp.M_tot;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= rows_live(M_cap, m_dev)) return;   // uniform over the wave
+  if (m >= rows_live(M_cap, tp.m_dev)) return;   // uniform over the wave
+  // the row's position, for the per-position LSE store (loaded before the partials are combined)
+  const int g = rp.lse_pos ? seq_of_row(tp.act_off, tp.B, m) * tp.N + tp.act_idx[m] : 0;
   Part acc = empty_part();
   for (int v0 = lane; v0 < n_vt; v0 += 64 * kMergeLoads) {
     Part x[kMergeLoads];
@@ -753,14 +837,15 @@ kl_merge_kernel(KLRowParams rp, int M_cap, const int32_t* __restrict__ m_dev, in
       if (v0 + 64 * k < n_vt) acc = combine(acc, x[k]);
   }
   acc = wave_reduce_part(acc);
-  if (lane == 0) finish_row<true>(rp, acc, m);
+  if (lane == 0) finish_row<true, false>(rp, acc, m, g);
 }
 
 template <typename T>
 static void kl_merge_tail_t(const KLRowParams& rp, const TailParams& tp, const float* klp, int n_vt, hipStream_t s) {
   if (tp.M_tot > 0)
-    hipLaunchKernelGGL(kl_merge_kernel, dim3((tp.M_tot + 3) / 4), dim3(256), 0, s, rp, tp.M_tot, tp.m_dev, n_vt, klp);
-  hipLaunchKernelGGL((kl_tail_kernel<T, true>), dim3(1), dim3(kTailThreads), 0, s, rp, tp, 1, (const float*)nullptr);
+    hipLaunchKernelGGL(kl_merge_kernel, dim3((tp.M_tot + 3) / 4), dim3(256), 0, s, rp, tp, n_vt, klp);
+  hipLaunchKernelGGL((kl_tail_kernel<T, true, false>), dim3(1), dim3(kTailThreads), 0, s, rp, tp, 1,
+                     (const float*)nullptr);
 }
 
 hipError_t launch_kl_merge_tail(int dtype, const KLRowParams& rp, const TailParams& tp, const float* klp, int n_vt,
@@ -773,12 +858,15 @@ hipError_t launch_kl_merge_tail(int dtype, const KLRowParams& rp, const TailPara
 
 hipError_t launch_kl_lock(int dtype, const KLRowParams& rp, const TailParams& tp, float* part, hipStream_t s) {
   const bool prev = tp.have_prev != 0;
+  const bool plse = prev && rp.lse_prev != nullptr;
   if (dtype == 0) {
-    if (prev) kl_launch_t<bf16, true>(rp, tp, part, s);
-    else kl_launch_t<bf16, false>(rp, tp, part, s);
+    if (plse) kl_launch_t<bf16, true, true>(rp, tp, part, s);
+    else if (prev) kl_launch_t<bf16, true, false>(rp, tp, part, s);
+    else kl_launch_t<bf16, false, false>(rp, tp, part, s);
   } else {
-    if (prev) kl_launch_t<float, true>(rp, tp, part, s);
-    else kl_launch_t<float, false>(rp, tp, part, s);
+    if (plse) kl_launch_t<float, true, true>(rp, tp, part, s);
+    else if (prev) kl_launch_t<float, true, false>(rp, tp, part, s);
+    else kl_launch_t<float, false, false>(rp, tp, part, s);
   }
   return hipGetLastError();
 }

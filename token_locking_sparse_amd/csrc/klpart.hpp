@@ -13,7 +13,8 @@ namespace sl {
 
 struct Part {
   float ma, sa, ta;  // running max of cur (all ids), sum e^(a-ma), sum e^(a-ma) (a-b)
-  float mb, sb;      // running max of prev, sum e^(b-mb)
+  float mb, sb;      // running max of prev, sum e^(b-mb); when the previous posterior's LSE is
+                     // known from the pass that produced it: mb = that LSE, sb unused (0)
   float best;        // max of cur over ids != mask
   int bidx;          // where `best` is (lowest on ties): its 16-byte chunk while a row is
                      // streamed, its exact id once resolved (and in every stored partial)
@@ -50,20 +51,23 @@ __device__ __forceinline__ Part combine(const Part& x, const Part& y) {
 }
 
 // Segment partials: 8 words per (segment, row), segment-major, so the tail
-// reads one segment of consecutive rows with consecutive lanes.
-__device__ __forceinline__ void store_part(float* pp, const Part& t) {
+// reads one segment of consecutive rows with consecutive lanes.  The eighth
+// word carries an int beside the partial (the vocabulary pass: the row's
+// position b*N + pos).
+__device__ __forceinline__ void store_part(float* pp, const Part& t, int word7 = 0) {
   f32x4 x0, x1;
   x0[0] = t.ma; x0[1] = t.sa; x0[2] = t.ta; x0[3] = t.mb;
-  x1[0] = t.sb; x1[1] = t.best; x1[2] = __int_as_float(t.bidx); x1[3] = 0.f;
+  x1[0] = t.sb; x1[1] = t.best; x1[2] = __int_as_float(t.bidx); x1[3] = __int_as_float(word7);
   reinterpret_cast<f32x4*>(pp)[0] = x0;
   reinterpret_cast<f32x4*>(pp)[1] = x1;
 }
-__device__ __forceinline__ Part load_part(const float* pp) {
+__device__ __forceinline__ Part load_part(const float* pp, int* word7 = nullptr) {
   const f32x4 x0 = reinterpret_cast<const f32x4*>(pp)[0];
   const f32x4 x1 = reinterpret_cast<const f32x4*>(pp)[1];
   Part t;
   t.ma = x0[0]; t.sa = x0[1]; t.ta = x0[2]; t.mb = x0[3];
   t.sb = x1[0]; t.best = x1[1]; t.bidx = __float_as_int(x1[2]);
+  if (word7) *word7 = __float_as_int(x1[3]);
   return t;
 }
 

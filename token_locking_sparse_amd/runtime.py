@@ -54,7 +54,10 @@ class DeviceState:
 
     def __init__(self, model: DeviceModel, B: int, N: int, *, tok=None, cand=None, locked=None, h_in=None,
                  k_cache=None, v_cache=None, with_h_out=False, minimal_workspace=False, kv_head_major=False,
-                 device="cuda"):
+                 cached_lse=False, device="cuda"):
+        """cached_lse: keep a per-position LSE store beside the two posterior buffers, so that each
+        step's vocabulary pass takes the previous posterior's LSE from the step that produced it
+        (every step with the LM head must then run the pass: do_lock=True)."""
         dm = model.dims
         L, d, H, Dh, V = dm["n_layers"], dm["d"], dm["n_heads"], dm["head_dim"], dm["vocab"]
         dt = model.dtype
@@ -71,8 +74,11 @@ class DeviceState:
         self.v_cache = v_cache if v_cache is not None else torch.zeros(shape, dtype=dt, device=device)
         self.h_in = h_in
         self.logits = None
+        self.lse_pos = None
         if model.lm_head is not None:
             self.logits = [torch.zeros(B * N, V, dtype=dt, device=device) for _ in range(2)]
+            if cached_lse:
+                self.lse_pos = [torch.zeros(B * N, dtype=torch.float32, device=device) for _ in range(2)]
         rows = B * N
         self.kl = torch.zeros(rows, dtype=torch.float32, device=device)
         self.u = torch.zeros(rows, dtype=torch.float32, device=device)
@@ -104,6 +110,8 @@ class DeviceState:
         st.m_tot_host = self.m_host.ptr
         st.t_dev = _dptr(self.t_dev)
         st.kv_head_major = int(self.kv_head_major)
+        if self.lse_pos is not None:
+            st.lse_pos[0], st.lse_pos[1] = self.lse_pos[0].data_ptr(), self.lse_pos[1].data_ptr()
         return st
 
     def step(self, eps: float, gate_q: float = -1.0, mask_id: int = -1, do_lock: bool = True,

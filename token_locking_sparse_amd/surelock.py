@@ -49,7 +49,8 @@ class sl_state(C.Structure):
                 ("h_in", C.c_void_p), ("h_out", C.c_void_p), ("logits", C.c_void_p * 2),
                 ("kl", C.c_void_p), ("u", C.c_void_p), ("lse", C.c_void_p), ("conf", C.c_void_p),
                 ("argmax", C.c_void_p), ("gate_thr", C.c_void_p), ("lock_step", C.c_void_p),
-                ("m_tot_host", C.c_void_p), ("t_dev", C.c_void_p), ("kv_head_major", C.c_int)]
+                ("m_tot_host", C.c_void_p), ("t_dev", C.c_void_p), ("kv_head_major", C.c_int),
+                ("lse_pos", C.c_void_p * 2)]
 
 
 class sl_step_params(C.Structure):
@@ -85,10 +86,10 @@ def lib():
         "sl_attn_active": (i, [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]),
         "sl_attn_workspace_size": (sz, [i, i, i, i, i]),
         "sl_kl_lock": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
-                           vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+                           vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sl_kl_lock_workspace_size": (sz, [i, i, i, i]),
         "sl_kl_lock_noalloc": (i, [i, vp, vp, i, vp, vp, i, i, i, vp, C.POINTER(sl_lock_params), vp, vp, vp, vp,
-                                   vp, vp, vp, vp, vp, vp, vp]),
+                                   vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "sl_rope_table": (i, [i, i, f, vp, vp]),
         "sl_step": (i, [C.POINTER(sl_model), C.POINTER(sl_state), C.POINTER(sl_step_params), vp, sz, vp]),
         "sl_step_workspace_size": (sz, [C.POINTER(sl_model), i, i, i]),
@@ -201,7 +202,9 @@ def sl_kl_lock_workspace_size(B, N, M_tot, V) -> int:
 
 def sl_kl_lock(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, eps, gate_q, mask_id,
                have_prev, locked, kl, u, lse, argmax, conf, gate_thr, new_act_idx, new_act_off, ws,
-               m_tot_host: PinnedInt | None = None, stream=None):
+               m_tot_host: PinnedInt | None = None, stream=None, lse_prev=None, lse_pos=None):
+    """lse_prev / lse_pos: optional [B*N] float32 per-position LSE stores (the previous pass's, and
+    this pass's); with lse_prev the previous logits' own normaliser is not recomputed."""
     dt = dtype_code(logits_cur.dtype)
     p = sl_lock_params(float(eps), float(gate_q), int(mask_id), int(bool(have_prev)))
     st = lib().sl_kl_lock(dt, _ptr(logits_cur, "logits_cur", logits_cur.dtype),
@@ -212,6 +215,8 @@ def sl_kl_lock(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, 
                           _ptr(u, "u", torch.float32), _ptr(lse, "lse", torch.float32),
                           _ptr(argmax, "argmax", torch.int32, optional=True),
                           _ptr(conf, "conf", torch.float32, optional=True),
+                          _ptr(lse_prev, "lse_prev", torch.float32, optional=True),
+                          _ptr(lse_pos, "lse_pos", torch.float32, optional=True),
                           _ptr(gate_thr, "gate_thr", torch.float32, optional=True),
                           _ptr(new_act_idx, "new_act_idx", torch.int32), _ptr(new_act_off, "new_act_off", torch.int32),
                           m_tot_host.ptr if m_tot_host else None, _ptr(ws, "ws"), ws.numel() * ws.element_size(),
@@ -222,7 +227,7 @@ def sl_kl_lock(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, 
 
 def sl_kl_lock_noalloc(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot, cand, eps, gate_q, mask_id,
                        have_prev, locked, kl, u, lse, argmax, conf, gate_thr, new_act_idx, new_act_off,
-                       m_tot_host: PinnedInt | None = None, stream=None):
+                       m_tot_host: PinnedInt | None = None, stream=None, lse_prev=None, lse_pos=None):
     """sl_kl_lock without a workspace argument (the library's own per-GPU scratch array)."""
     dt = dtype_code(logits_cur.dtype)
     p = sl_lock_params(float(eps), float(gate_q), int(mask_id), int(bool(have_prev)))
@@ -235,6 +240,8 @@ def sl_kl_lock_noalloc(logits_cur, logits_prev, V, act_idx, act_off, B, N, M_tot
                                   _ptr(u, "u", torch.float32), _ptr(lse, "lse", torch.float32),
                                   _ptr(argmax, "argmax", torch.int32, optional=True),
                                   _ptr(conf, "conf", torch.float32, optional=True),
+                                  _ptr(lse_prev, "lse_prev", torch.float32, optional=True),
+                                  _ptr(lse_pos, "lse_pos", torch.float32, optional=True),
                                   _ptr(gate_thr, "gate_thr", torch.float32, optional=True),
                                   _ptr(new_act_idx, "new_act_idx", torch.int32),
                                   _ptr(new_act_off, "new_act_off", torch.int32),
