@@ -113,12 +113,18 @@ hipError_t launch_compact(const uint8_t* locked, int B, int N, int32_t* act_idx,
 }
 
 // ------------------------------------------------------------------ tail
+// Sequences whose gate quantile and lock update run side by side (a group of waves each).
+constexpr int kSelGroups = 8;
+constexpr int kGrpRegs = 16;   // values a thread of a group holds
+
 struct TailShared {
   int w[16];
   uint32_t hist[3][256];   // radix-select histograms, used round-robin
   uint32_t mm[32];         // per-wave min / max of the select's values
   float fv[16];
   int iv[32];
+  uint32_t ghist[kSelGroups][3][256];   // per-group histograms of the grouped select
+  int gpass[kSelGroups];                 // digit passes each group needs
 };
 
 // Up to kRegSel values of a sequence per thread are held in registers; longer
@@ -220,6 +226,122 @@ __device__ float block_select_kth(const uint32_t (&v)[kRegSel], bool from_regs, 
   return __uint_as_float(prefix);
 }
 
+// Gate quantile and lock update of several sequences at once (B > 1, gate on): the workgroup's waves
+// form min(B, kSelGroups) groups, each taking one sequence per round; a group holds up to kGrpRegs
+// consecutive rows per thread in registers and runs the same radix select as block_select_kth on
+// histograms of its own, every group advancing one digit per workgroup barrier.  Returns false
+// (and does nothing) when a sequence does not fit its group's registers.
+__device__ bool tail_select_lock_grouped(const TailParams& p, TailShared& sh, int t_now) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
+  const int G = p.B < kSelGroups ? p.B : kSelGroups;
+  const int wpg = nw / G;                       // waves per group
+  const int cap = wpg * 64 * kGrpRegs;
+  for (int b = 0; b < p.B; ++b)
+    if (p.act_off[b + 1] - p.act_off[b] > cap) return false;   // uniform: every thread reads the same
+  const int g = wid / wpg, gt = tid - g * wpg * 64;   // group, thread within it
+  const bool in_group = g < G;
+  const bool can_lock = p.eps > 0.f && p.have_prev;
+  for (int b0 = 0; b0 < p.B; b0 += G) {
+    const int b = b0 + g;
+    const bool live = in_group && b < p.B;
+    int o0 = 0, o1 = 0;
+    if (live) { o0 = p.act_off[b]; o1 = p.act_off[b + 1]; }
+    const int n = o1 - o0;
+    uint32_t uv[kGrpRegs];
+    float kv[kGrpRegs];
+    int pv[kGrpRegs];
+#pragma unroll
+    for (int i = 0; i < kGrpRegs; ++i) {
+      const int m = o0 + gt * kGrpRegs + i;   // dense: only the group's first waves hold values
+      const bool in = live && m < o1;
+      uv[i] = in ? __float_as_uint(p.u[m]) : kNoValue;
+      kv[i] = in ? p.kl[m] : INFINITY;
+      pv[i] = in ? p.act_idx[m] : -1;
+    }
+    // the group's min and max, and the digit passes it needs
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < kGrpRegs; ++i)
+      if (uv[i] != kNoValue) { lo = min(lo, uv[i]); hi = max(hi, uv[i]); }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    __syncthreads();   // earlier readers of sh.mm / sh.ghist / sh.gpass are done
+    if (lane == 0) { sh.mm[wid] = lo; sh.mm[16 + wid] = hi; }
+    if (in_group)
+      for (int i = gt; i < 256; i += wpg * 64) sh.ghist[g][0][i] = 0;
+    __syncthreads();
+    lo = 0xffffffffu; hi = 0u;
+    if (in_group)
+      for (int w = g * wpg; w < (g + 1) * wpg; ++w) { lo = min(lo, sh.mm[w]); hi = max(hi, sh.mm[16 + w]); }
+    const bool sel = live && n > 0;
+    const int k = sel ? (int)floor((double)p.gate_q * (double)(n - 1)) : 0;
+    int free_bits = 0, passes = 0;
+    uint32_t pmask = 0u, prefix = lo;
+    if (sel && lo != hi) {
+      free_bits = 32 - __clz((int)(lo ^ hi));
+      pmask = free_bits >= 32 ? 0u : ~((1u << free_bits) - 1u);
+      prefix = lo & pmask;
+      passes = (free_bits + 7) / 8;
+    }
+    if (in_group && gt == 0) sh.gpass[g] = passes;
+    __syncthreads();
+    int max_pass = 0;
+    for (int j = 0; j < G; ++j) max_pass = max(max_pass, sh.gpass[j]);
+    int kk = k;
+    int shift = free_bits > 8 ? free_bits - 8 : 0;
+    for (int q = 0; q < max_pass; ++q) {
+      const bool act = q < passes;   // uniform over the group
+      uint32_t* h = sh.ghist[in_group ? g : 0][q % 3];
+      if (act) {
+#pragma unroll
+        for (int i = 0; i < kGrpRegs; ++i) {
+          bool a = uv[i] != kNoValue && (uv[i] & pmask) == prefix;
+          const uint32_t d = (uv[i] >> shift) & 255u;
+          // lanes sharing the first active lane's digit add once (values cluster)
+          const unsigned long long m = __ballot(a);
+          if (m != 0ull) {
+            const int leader = __ffsll(m) - 1;
+            const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+            const unsigned long long same = __ballot(a && d == dl);
+            if (lane == leader) atomicAdd(&h[dl], (uint32_t)__popcll(same));
+            a = a && d != dl;
+          }
+          if (a) atomicAdd(&h[d], 1u);
+        }
+      }
+      if (in_group)
+        for (int i = gt; i < 256; i += wpg * 64) sh.ghist[g][(q + 1) % 3][i] = 0;
+      __syncthreads();
+      if (act) {
+        radix_digit(h, kk, shift, prefix, pmask);
+        shift = shift > 8 ? shift - 8 : 0;
+      }
+    }
+    const float thr = sel ? __uint_as_float(prefix) : INFINITY;
+    if (live && gt == 0 && p.gate_thr) p.gate_thr[b] = thr;
+    if (live && can_lock) {
+      const int64_t gb = (int64_t)b * p.N;
+      bool ok[kGrpRegs];
+#pragma unroll
+      for (int i = 0; i < kGrpRegs; ++i)
+        ok[i] = pv[i] >= 0 && kv[i] <= p.eps && __uint_as_float(uv[i]) <= thr;
+      if (p.cand) {
+#pragma unroll
+        for (int i = 0; i < kGrpRegs; ++i) ok[i] = ok[i] && (p.cand[gb + (ok[i] ? pv[i] : 0)] != 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kGrpRegs; ++i) {
+        if (ok[i]) {
+          p.locked[gb + pv[i]] = 1;
+          if (p.lock_step) p.lock_step[gb + pv[i]] = t_now;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
 // Gate quantile, lock update, optional sampler, compaction — one workgroup.
 // A sequence of at most kRegSel * blockDim active rows is read once into
 // registers, kRegSel consecutive rows per thread (positions, u, KL, then the
@@ -230,56 +352,61 @@ __device__ void tail_phase(const TailParams& p, TailShared& sh) {
   const bool gate = p.gate_q >= 0.f;
   const bool can_lock = p.eps > 0.f && p.have_prev;
   const int t_now = p.t_dev ? p.t_dev[0] : p.t;   // step index recorded in lock_step
+  // several sequences with the gate: their selects and lock updates side by side
+  const bool grouped = gate && p.B > 1 && tail_select_lock_grouped(p, sh, t_now);
   for (int b = 0; b < p.B; ++b) {
     const int o0 = p.act_off[b], o1 = p.act_off[b + 1];
     const int n = o1 - o0;
-    const bool regs = n <= kRegSel * bd;
-    uint32_t uv[kRegSel];
-    float kv[kRegSel];
-    int pv[kRegSel];
+    if (grouped && p.unmask_k <= 0) break;   // nothing left per sequence
+    if (!grouped) {   // select and lock update of this sequence alone
+      const bool regs = n <= kRegSel * bd;
+      uint32_t uv[kRegSel];
+      float kv[kRegSel];
+      int pv[kRegSel];
 #pragma unroll
-    for (int i = 0; i < kRegSel; ++i) {
-      const int m = o0 + tid * kRegSel + i;   // dense: only the first waves hold values
-      const bool in = regs && m < o1;
-      uv[i] = in ? __float_as_uint(p.u[m]) : kNoValue;
-      kv[i] = in ? p.kl[m] : INFINITY;
-      pv[i] = in ? p.act_idx[m] : -1;
-    }
-    float thr = INFINITY;
-    if (gate && n > 0) {
-      const int k = (int)floor((double)p.gate_q * (double)(n - 1));
-      thr = block_select_kth(uv, regs, p.u, o0, o1, k, sh);
-    }
-    if (tid == 0 && p.gate_thr) p.gate_thr[b] = thr;
-    if (can_lock) {
-      const int64_t gb = (int64_t)b * p.N;
-      if (regs) {
-        bool ok[kRegSel];
+      for (int i = 0; i < kRegSel; ++i) {
+        const int m = o0 + tid * kRegSel + i;   // dense: only the first waves hold values
+        const bool in = regs && m < o1;
+        uv[i] = in ? __float_as_uint(p.u[m]) : kNoValue;
+        kv[i] = in ? p.kl[m] : INFINITY;
+        pv[i] = in ? p.act_idx[m] : -1;
+      }
+      float thr = INFINITY;
+      if (gate && n > 0) {
+        const int k = (int)floor((double)p.gate_q * (double)(n - 1));
+        thr = block_select_kth(uv, regs, p.u, o0, o1, k, sh);
+      }
+      if (tid == 0 && p.gate_thr) p.gate_thr[b] = thr;
+      if (can_lock) {
+        const int64_t gb = (int64_t)b * p.N;
+        if (regs) {
+          bool ok[kRegSel];
 #pragma unroll
-        for (int i = 0; i < kRegSel; ++i) {
-          ok[i] = pv[i] >= 0 && kv[i] <= p.eps;
-          if (gate) ok[i] = ok[i] && (__uint_as_float(uv[i]) <= thr);
-        }
-        if (p.cand) {
-#pragma unroll
-          for (int i = 0; i < kRegSel; ++i) ok[i] = ok[i] && (p.cand[gb + (ok[i] ? pv[i] : 0)] != 0);
-        }
-#pragma unroll
-        for (int i = 0; i < kRegSel; ++i) {
-          if (ok[i]) {
-            p.locked[gb + pv[i]] = 1;
-            if (p.lock_step) p.lock_step[gb + pv[i]] = t_now;
+          for (int i = 0; i < kRegSel; ++i) {
+            ok[i] = pv[i] >= 0 && kv[i] <= p.eps;
+            if (gate) ok[i] = ok[i] && (__uint_as_float(uv[i]) <= thr);
           }
-        }
-      } else {
-        for (int m = o0 + tid; m < o1; m += bd) {
-          const int64_t g = gb + p.act_idx[m];
-          bool ok = (p.cand == nullptr) || (p.cand[g] != 0);
-          ok = ok && (p.kl[m] <= p.eps);
-          if (gate) ok = ok && (p.u[m] <= thr);
-          if (ok) {
-            p.locked[g] = 1;
-            if (p.lock_step) p.lock_step[g] = t_now;
+          if (p.cand) {
+#pragma unroll
+            for (int i = 0; i < kRegSel; ++i) ok[i] = ok[i] && (p.cand[gb + (ok[i] ? pv[i] : 0)] != 0);
+          }
+#pragma unroll
+          for (int i = 0; i < kRegSel; ++i) {
+            if (ok[i]) {
+              p.locked[gb + pv[i]] = 1;
+              if (p.lock_step) p.lock_step[gb + pv[i]] = t_now;
+            }
+          }
+        } else {
+          for (int m = o0 + tid; m < o1; m += bd) {
+            const int64_t g = gb + p.act_idx[m];
+            bool ok = (p.cand == nullptr) || (p.cand[g] != 0);
+            ok = ok && (p.kl[m] <= p.eps);
+            if (gate) ok = ok && (p.u[m] <= thr);
+            if (ok) {
+              p.locked[g] = 1;
+              if (p.lock_step) p.lock_step[g] = t_now;
+            }
           }
         }
       }
