@@ -62,7 +62,7 @@ TRAFFIC = {
     "gemm": {"files": ["token_locking_sparse_amd/csrc/gemm.hip"],
              "sha256": "4a16938212c63a6db4e5f2e4acd8345b339e0cdfcc87c83d4d7ff1caeec6e42d", "bytes": 427940488},
     "kl": {"files": ["token_locking_sparse_amd/csrc/kl_lock.hip"],
-           "sha256": "b4e4357740702cfe0bfeaaff55f09310dfc9975b85a65a6a179c6f2e6d7713fd", "bytes": 833697690},
+           "sha256": "f38cbbea90dbd2f404b9e21b23e019c800d9688967011235dcd549e04537b831", "bytes": 833704141},
 }
 
 
