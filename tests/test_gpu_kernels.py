@@ -142,6 +142,9 @@ KL_CASES = [
     (10000, 256, 2, 0.7, "bf16", 0.05, 0.5, -1, True, 0.8),           # B*N above the tail's LDS copies
     (20000, 256, 1, 0.3, "bf16", 0.05, 0.5, -1, True, None),          # 14000 rows: tail reads global memory
     (512, 4096, 2, 0.4, "bf16", math.inf, 0.5, -1, True, 0.8),        # eps = +inf: confidence gate only
+    (256, 1024, 12, 0.5, "bf16", 0.05, 0.5, -1, True, 0.8),           # 12 sequences: two rounds of grouped selects
+    (3276, 512, 5, (0.02, 0.9, 0.9, 0.9, 0.9), "bf16", 0.05, 0.5, 511, True, None),   # one sequence beyond
+                                                                      # its group's registers: one at a time
 ]
 
 
