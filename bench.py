@@ -34,6 +34,9 @@ if ROOT not in sys.path:
 METRIC = "SureLock step ms & TFLOP/s vs M/N at LLaDA-8B layer shape; KL-lock HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# dense bf16 MFMA FLOPs per GHz of shader clock: 256 CUs x 4 matrix cores x 1024 FLOP per cycle
+# (one v_mfma_f32_32x32x16_bf16, 32768 FLOP, every 32 cycles); 2.5 PFLOP/s is this at 2.4 GHz
+MFMA_TFLOPS_PER_GHZ = 256 * 4096 * 1e9 / 1e12
 D, H, DH, F, N_LAYER = 4096, 32, 128, 12288, 1024
 MS = (1024, 512, 256, 64)
 N_KL, V_KL, EPS_KL, GATE_KL = 4096, 126464, 0.01, 0.5
@@ -60,7 +63,7 @@ def kl_bytes(M, N=N_KL, V=V_KL):
 # the report says null.
 TRAFFIC = {
     "gemm": {"files": ["token_locking_sparse_amd/csrc/gemm.hip"],
-             "sha256": "4a16938212c63a6db4e5f2e4acd8345b339e0cdfcc87c83d4d7ff1caeec6e42d", "bytes": 427940488},
+             "sha256": "00b9cdb5bc034fbda4bc5f9d2755e0462b3222fae296ee047fbf9e7f2d4f46a4", "bytes": 427923810},
     "kl": {"files": ["token_locking_sparse_amd/csrc/kl_lock.hip"],
            "sha256": "f38cbbea90dbd2f404b9e21b23e019c800d9688967011235dcd549e04537b831", "bytes": 833704141},
 }
@@ -482,7 +485,30 @@ def measured_peaks(reps=7):
     ms_loop = timed(lambda: sl.sl_peak_gemm_loop(cus, tiles, False, l2src, sink))
     ms_loop_ld = timed(lambda: sl.sl_peak_gemm_loop(cus, tiles, True, l2src, sink))
     nb = src.numel()
+    # the same MFMA loop on operands read from memory (eight sets per lane, rotated): random bf16 values,
+    # as the step's weights and activations are, then all ones and all zeros.  The matrix cores' power
+    # depends on the operand bits, and the clock the chip holds with it; each launch also reports its
+    # workgroups' shader-clock cycles against 100 MHz real-time ticks.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    n_ops = 16 * 256 * 8
+    operand_sets = {"random": torch.randn(n_ops, generator=gen, device=dev).to(torch.bfloat16),
+                    "ones": torch.ones(n_ops, device=dev, dtype=torch.bfloat16),
+                    "zeros": torch.zeros(n_ops, device=dev, dtype=torch.bfloat16)}
+    clocks = torch.zeros(2 * wg, dtype=torch.int64, device=dev)
+    by_operands = {}
+    for name, ops in operand_sets.items():
+        ms_op = timed(lambda: sl.sl_peak_mfma_operands(wg, iters, ops, sink))
+        clocks.zero_()
+        sl.sl_peak_mfma_operands(wg, iters, ops, sink, clocks)
+        torch.cuda.synchronize()
+        c = clocks.view(wg, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.median(c[:, 0] / c[:, 1] / 10.0))
+        tf = flops / (ms_op * 1e-3) / 1e12
+        by_operands[name] = {"tflops": round(tf, 1), "ghz": round(ghz, 3),
+                             "frac_at_clock": round(tf / (MFMA_TFLOPS_PER_GHZ * ghz), 3)}
     out = {"mfma_bf16_tflops": round(flops / (ms_mfma * 1e-3) / 1e12, 1),
+           "mfma_bf16_by_operands": by_operands,
            "hbm_read_gbs": round(nb / (ms_read * 1e-3) / 1e9, 1),
            "hbm_copy_gbs": round(2 * nb / (ms_copy * 1e-3) / 1e9, 1),
            "gemm_loop_tflops": round(fl_loop / (ms_loop * 1e-3) / 1e12, 1),
@@ -491,10 +517,71 @@ def measured_peaks(reps=7):
                   "1 GiB streamed with 16-byte non-temporal loads (read) and loads + stores (copy, bytes "
                   "read + written), each workgroup on a contiguous range; the 256 x 256 GEMM tile's "
                   "LDS-to-MFMA loop on %d workgroups x %d k-tiles of 32, alone and with its direct loads "
-                  "from L2, waits and barrier; medians of %d launches" % (wg, iters, cus, tiles, reps)}
-    del src, dst, l2src
+                  "from L2, waits and barrier; medians of %d launches; mfma_bf16_by_operands: the MFMA loop "
+                  "on operands from memory (random N(0,1) bf16, ones, zeros), clock = median over workgroups "
+                  "of s_memtime cycles / s_memrealtime ticks, frac_at_clock = TFLOP/s over 256 CUs x 4096 "
+                  "FLOP per cycle at that clock" % (wg, iters, cus, tiles, reps)}
+    del src, dst, l2src, operand_sets, clocks
     torch.cuda.empty_cache()
     return out
+
+
+def gemm_clock_study(reps=20, warmup=5):
+    """The dominant kernel (FFN gate/up + SwiGLU at M = 1024) on random operands, as in the step, and on
+    all-zero operands: its rate (product kernel, HIP events), then one launch of its clock-recording
+    variant, which gives the clock the chip held (shader-clock cycles over 100 MHz ticks, median over
+    workgroups) and the k-tile loop's MFMA utilisation at that clock (the workgroup's FLOPs over the
+    loop's cycles x 4096 FLOP per CU-cycle)."""
+    import numpy as np
+    import torch
+
+    import token_locking_sparse_amd as sl
+
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    M, K, n_out = 1024, D, 2 * F
+    bm, bn, split = sl.sl_gemm_plan(bf, sl.SL_EPI_SWIGLU, M, K, n_out)
+    nwg = -(-M // bm) * (n_out // bn) * split
+    clocks = torch.zeros(4 * nwg, dtype=torch.int64, device=dev)
+    out = torch.empty(M, F, dtype=bf, device=dev)
+    res = {"tile": [bm, bn], "split_k": split, "workgroups": nwg}
+    for name in ("random", "zeros"):
+        if name == "random":
+            A = torch.randn(M, K, generator=g, device=dev).to(bf)
+            wg_ = (torch.randn(F, K, generator=g, device=dev) * 0.02).to(bf)
+            wu_ = (torch.randn(F, K, generator=g, device=dev) * 0.02).to(bf)
+        else:
+            A = torch.zeros(M, K, device=dev, dtype=bf)
+            wg_ = torch.zeros(F, K, device=dev, dtype=bf)
+            wu_ = torch.zeros(F, K, device=dev, dtype=bf)
+        call = lambda: sl.sl_gemm(sl.SL_EPI_SWIGLU, A, M, K, n_out, wg_, wu_, out0=out)
+        for _ in range(warmup):
+            call()
+        es = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in es]))
+        clocks.zero_()
+        sl.sl_gemm_clocked(sl.SL_EPI_SWIGLU, A, M, K, n_out, wg_, wu_, out0=out, clocks=clocks)
+        torch.cuda.synchronize()
+        c = clocks.view(nwg, 4).cpu().numpy().astype(np.float64)
+        c = c[c[:, 1] > 0]
+        ghz = float(np.median(c[:, 0] / c[:, 1] / 10.0))
+        util = float(np.median(bm * bn * c[:, 3] * 2.0 / 4096.0 / c[:, 2]))
+        tf = 2.0 * M * K * n_out / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "ghz": round(ghz, 3),
+                     "frac_at_clock": round(tf / (MFMA_TFLOPS_PER_GHZ * ghz), 3),
+                     "kloop_mfma_util_at_clock": round(util, 3)}
+        del A, wg_, wu_
+    del clocks, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def gemm_study(reps=20, warmup=5):
@@ -934,7 +1021,13 @@ def main():
     ap.add_argument("--gemm-study", action="store_true",
                     help="only time the library's GEMM against torch.matmul on the step's shapes and two "
                          "large ones (one JSON line)")
+    ap.add_argument("--clock-study", action="store_true",
+                    help="only measure the MFMA loop on random / constant operands and the dominant GEMM's "
+                         "clock and k-loop MFMA utilisation (one JSON line)")
     args = ap.parse_args()
+    if args.clock_study:
+        print(json.dumps({"measured_peaks": measured_peaks(), "gemm_clock": gemm_clock_study()}), flush=True)
+        return
     if args.gemm_study:
         print(json.dumps({"gemm_study": gemm_study()}), flush=True)
         return
@@ -976,6 +1069,7 @@ def main():
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
         "measured_peaks": peaks,
+        "gemm_clock": gemm_clock_study(),
         "cache_layout": cache_layout_study(),
         "batched_step": None if args.no_batched else batched_step(),
         "tiny_loop": tiny_loop(),
@@ -988,6 +1082,9 @@ def main():
     # fractions of the measured ceilings, beside the vendor ones
     line["roofline"]["frac_of_measured_peak"] = round(line["roofline"]["achieved"] / peaks["mfma_bf16_tflops"], 4)
     line["roofline"]["measured_peak"] = peaks["mfma_bf16_tflops"]
+    rnd = peaks["mfma_bf16_by_operands"]["random"]["tflops"]
+    line["roofline"]["frac_of_random_operand_mfma_peak"] = round(line["roofline"]["achieved"] / rnd, 4)
+    line["roofline"]["random_operand_mfma_peak"] = rnd
     line["roofline_kl"]["frac_of_measured_peak"] = round(line["roofline_kl"]["achieved"] / peaks["hbm_read_gbs"], 4)
     line["roofline_kl"]["measured_peak"] = peaks["hbm_read_gbs"]
     for r in line["per_M"]:

@@ -365,9 +365,27 @@ size_t sl_step_workspace_min(const sl_model* model, int B, int N, int M_tot);
  *                    with_loads != 0 adds the GEMM's per-k-tile direct global-to-LDS loads (from
  *                    src: device memory of at least 1 MiB, L2-resident), their waits and a
  *                    barrier.  sl_peak_gemm_loop_flops gives the FLOPs.  sink as above.
+ * sl_peak_mfma_operands  sl_peak_mfma's loop on operands read from `operands` (device memory of
+ *                    16 x 256 16-byte chunks, e.g. random bf16 values: the matrix cores' power, and
+ *                    the clock the chip holds, depend on the operand bits), eight operand sets per
+ *                    lane rotated between consecutive MFMAs; iters a multiple of 8, FLOPs as
+ *                    sl_peak_mfma_flops.  clocks (device, 2 x workgroups entries, or NULL): per
+ *                    workgroup the shader-clock cycles and the 100 MHz real-time ticks it took.
+ * sl_gemm_clocked    sl_gemm (bf16; SL_EPI_SWIGLU with w0, w1, out0, or SL_EPI_LOGITS with w0,
+ *                    out0, act_idx, act_off, B, N; the same launch plan) in a variant that records
+ *                    per workgroup w < clock_slots, in clocks[4 w .. 4 w + 3]: shader-clock cycles
+ *                    and 100 MHz real-time ticks of the workgroup, cycles of its k-tile loop, and the
+ *                    K elements it multiplied.  Workgroups past the live rows leave their slots as
+ *                    they were (the caller clears them).  Workgroup w of a launch is tile w of
+ *                    sl_gemm_plan's grid (K splits: w = split * tiles + tile).
  */
 sl_status sl_peak_mfma(int workgroups, int iters, float* sink, sl_stream stream);
 double sl_peak_mfma_flops(int workgroups, int iters);
+sl_status sl_peak_mfma_operands(int workgroups, int iters, const void* operands, float* sink,
+                                unsigned long long* clocks, sl_stream stream);
+sl_status sl_gemm_clocked(int epilogue, const void* A, int M, int K, int n_out, const void* w0, const void* w1,
+                          void* out0, const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                          unsigned long long* clocks, int clock_slots, sl_stream stream);
 sl_status sl_peak_stream(const void* src, void* dst, size_t bytes, int workgroups, float* sink, sl_stream stream);
 sl_status sl_peak_gemm_loop(int workgroups, int tiles, int with_loads, const void* src, float* sink,
                             sl_stream stream);

@@ -58,6 +58,13 @@ def test_status_strings_and_host_checks():
     st = L.sl_gemm(0, 1, dummy, 300000, 8192, 4096, dummy, None, None, dummy, None, None, None, 0, 0, None, None,
                    1, 1, None)
     assert st == 2 and b"4 GiB" in L.sl_last_error()
+    # the clock-recording GEMM takes the SwiGLU or logits epilogue only, and a clock record
+    st = L.sl_gemm_clocked(0, dummy, 16, 512, 1536, dummy, None, dummy, None, None, 1, 16, dummy, 4, None)
+    assert st == 2
+    st = L.sl_gemm_clocked(2, dummy, 16, 512, 1536, dummy, dummy, dummy, None, None, 1, 16, None, 0, None)
+    assert st == 1 and b"clock" in L.sl_last_error()
+    # the operand MFMA loop rotates 8 operand sets: iters must be a multiple of 8
+    assert L.sl_peak_mfma_operands(4, 12, dummy, dummy, None, None) == 1
 
 
 def test_workspace_sizes_are_monotone_in_rows():

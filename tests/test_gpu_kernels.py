@@ -370,6 +370,74 @@ def test_gemm_parity(kind, M, K, n_out):
     assert np.all(np.delete(gk, glob, axis=0) == 5.0) and np.all(np.delete(gv, glob, axis=0) == 5.0)
 
 
+# ------------------------------------------------------------------ measurement variants
+@pytest.mark.parametrize("kind,M,K,n_out", [("swiglu", 300, 512, 12288), ("swiglu", 1024, 1024, 6144),
+                                             ("logits", 130, 512, 6144), ("logits", 700, 1024, 3072)])
+def test_gemm_clocked_matches_gemm(kind, M, K, n_out):
+    """The clock-recording GEMM variant stores exactly what sl_gemm stores (the same launch plan and
+    arithmetic), and fills one plausible record per workgroup: a clock between 0.3 and 4 GHz, a k-tile
+    loop shorter than the workgroup, K elements multiplied."""
+    sl = _sl()
+    epi = sl.SL_EPI_SWIGLU if kind == "swiglu" else sl.SL_EPI_LOGITS
+    bm, bn, split = sl.sl_gemm_plan(torch.bfloat16, epi, M, K, n_out)
+    nwg = -(-M // bm) * (n_out // bn) * split
+    say("gemm_clocked", kind, M, K, n_out, (bm, bn, split), nwg)
+    g = W.rng(W.SEED_ACT, 9100 + M + K + n_out)
+    A = dev(W.to_storage(W.normal(g, (M, K), 1.0), "bf16"), "bf16")
+    clocks = torch.full((4 * nwg + 4,), -1, dtype=torch.int64, device="cuda")
+    clocks[: 4 * nwg].zero_()
+    if kind == "swiglu":
+        F = n_out // 2
+        w0 = dev(W.to_storage(W.normal(g, (F, K), 0.02), "bf16"), "bf16")
+        w1 = dev(W.to_storage(W.normal(g, (F, K), 0.02), "bf16"), "bf16")
+        ref = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+        got = torch.empty_like(ref)
+        sl.sl_gemm(epi, A, M, K, n_out, w0, w1, out0=ref)
+        sl.sl_gemm_clocked(epi, A, M, K, n_out, w0, w1, out0=got, clocks=clocks[: 4 * nwg])
+    else:
+        B, N = 2, max(512, M)
+        m0 = M // 3
+        acts = [np.sort(g.permutation(N)[:m0]), np.sort(g.permutation(N)[:M - m0])]
+        ai = torch.from_numpy(np.concatenate(acts).astype(np.int32)).cuda()
+        ao = torch.tensor([0, m0, M], dtype=torch.int32, device="cuda")
+        w0 = dev(W.to_storage(W.normal(g, (n_out, K), 0.02), "bf16"), "bf16")
+        ref = torch.full((B * N, n_out), 3.0, dtype=torch.bfloat16, device="cuda")
+        got = ref.clone()
+        sl.sl_gemm(epi, A, M, K, n_out, w0, out0=ref, act_idx=ai, act_off=ao, B=B, N=N)
+        sl.sl_gemm_clocked(epi, A, M, K, n_out, w0, out0=got, act_idx=ai, act_off=ao, B=B, N=N,
+                           clocks=clocks[: 4 * nwg])
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    c = clocks.cpu().numpy()
+    assert np.all(c[4 * nwg:] == -1)   # nothing past the record
+    c = c[: 4 * nwg].reshape(nwg, 4).astype(np.float64)
+    ghz = c[:, 0] / c[:, 1] / 10.0
+    say("clock GHz min %.2f median %.2f max %.2f" % (ghz.min(), np.median(ghz), ghz.max()))
+    assert np.all(c[:, 1] > 0) and np.all((ghz > 0.3) & (ghz < 4.0))
+    assert np.all((c[:, 2] > 0) & (c[:, 2] < c[:, 0]))
+    assert np.all(c[:, 3] * split == K)
+
+
+def test_peak_mfma_operands_clocks():
+    """The operand-dependent MFMA loop fills one clock record per workgroup and nothing beyond."""
+    sl = _sl()
+    wg, iters = 64, 256
+    ops = torch.randn(16 * 256 * 8, device="cuda").to(torch.bfloat16)
+    sink = torch.zeros(256, device="cuda")
+    clocks = torch.full((2 * wg + 2,), -1, dtype=torch.int64, device="cuda")
+    flops = sl.sl_peak_mfma_operands(wg, iters, ops, sink, clocks[: 2 * wg])
+    torch.cuda.synchronize()
+    assert flops == wg * 4 * iters * 4 * 2.0 * 32 * 32 * 16
+    c = clocks.cpu().numpy()
+    assert np.all(c[2 * wg:] == -1)
+    c = c[: 2 * wg].reshape(wg, 2).astype(np.float64)
+    assert np.all(c[:, 1] > 0)
+    ghz = c[:, 0] / c[:, 1] / 10.0
+    assert np.all((ghz > 0.3) & (ghz < 4.0))
+    with pytest.raises(Exception):
+        sl.sl_peak_mfma_operands(wg, iters + 3, ops, sink)   # not a multiple of the 8 operand sets
+
+
 # ------------------------------------------------------------------ attention
 ATTN_CASES = [
     # dtype, Dh, H, N, Ms

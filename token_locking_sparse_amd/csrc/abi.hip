@@ -311,15 +311,17 @@ sl_status sl_rope_table(int n_pos, int head_dim, float theta, float* table, sl_s
   return SL_OK;
 }
 
-sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
-                  const void* w1, const void* w2, void* out0, void* out1, void* out2, const float* rope,
-                  int d, int head_dim, const int32_t* act_idx, const int32_t* act_off, int B, int N,
-                  sl_stream stream) {
-  g_err[0] = 0;
+// Checks sl_gemm's arguments and fills g (M == 0 passes with nothing to launch).
+static sl_status gemm_args(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
+                           const void* w1, const void* w2, void* out0, void* out1, void* out2, const float* rope,
+                           int d, int head_dim, const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                           sl::GemmArgs& g) {
   sl_status st = check_dtype(dtype);
   if (st != SL_OK) return st;
   SL_REQUIRE(epilogue >= SL_EPI_QKV_ROPE && epilogue <= SL_EPI_LOGITS, SL_ERR_INVALID, "bad epilogue %d", epilogue);
   SL_REQUIRE(M >= 0 && K > 0 && n_out > 0, SL_ERR_INVALID, "bad size");
+  g = sl::GemmArgs{};
+  g.M = 0;
   if (M == 0) return SL_OK;
   SL_REQUIRE(A && w0 && out0, SL_ERR_INVALID, "NULL pointer argument");
   const sl::EpiKind epi = (sl::EpiKind)epilogue;
@@ -333,11 +335,39 @@ sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_ou
   }
   if (epi == sl::EPI_SWIGLU) SL_REQUIRE(w1, SL_ERR_INVALID, "SwiGLU needs the up matrix");
   if (epi == sl::EPI_LOGITS) SL_REQUIRE(act_idx && act_off && B >= 1 && N >= 1, SL_ERR_INVALID, "LOGITS needs act lists");
-  sl::GemmArgs g{};
   g.A = A; g.M = M; g.K = K; g.Nv = n_out; g.w0 = w0; g.w1 = w1; g.w2 = w2;
   g.out0 = out0; g.out1 = out1; g.out2 = out2; g.rope = rope; g.d = d; g.Dh = head_dim;
   g.act_idx = act_idx; g.act_off = act_off; g.B = B; g.N = N; g.split_k = 1;
-  SL_TRY(sl::launch_gemm(dtype, epi, g, (hipStream_t)stream), "sl_gemm launch");
+  return SL_OK;
+}
+
+sl_status sl_gemm(int dtype, int epilogue, const void* A, int M, int K, int n_out, const void* w0,
+                  const void* w1, const void* w2, void* out0, void* out1, void* out2, const float* rope,
+                  int d, int head_dim, const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                  sl_stream stream) {
+  g_err[0] = 0;
+  sl::GemmArgs g;
+  const sl_status st = gemm_args(dtype, epilogue, A, M, K, n_out, w0, w1, w2, out0, out1, out2, rope, d, head_dim,
+                                 act_idx, act_off, B, N, g);
+  if (st != SL_OK || g.M == 0) return st;
+  SL_TRY(sl::launch_gemm(dtype, (sl::EpiKind)epilogue, g, (hipStream_t)stream), "sl_gemm launch");
+  return SL_OK;
+}
+
+sl_status sl_gemm_clocked(int epilogue, const void* A, int M, int K, int n_out, const void* w0, const void* w1,
+                          void* out0, const int32_t* act_idx, const int32_t* act_off, int B, int N,
+                          unsigned long long* clocks, int clock_slots, sl_stream stream) {
+  g_err[0] = 0;
+  SL_REQUIRE(epilogue == SL_EPI_SWIGLU || epilogue == SL_EPI_LOGITS, SL_ERR_UNSUPPORTED,
+             "sl_gemm_clocked takes the SwiGLU or logits epilogue");
+  SL_REQUIRE(clocks && clock_slots > 0, SL_ERR_INVALID, "NULL clock record");
+  sl::GemmArgs g;
+  const sl_status st = gemm_args(SL_BF16, epilogue, A, M, K, n_out, w0, w1, nullptr, out0, nullptr, nullptr, nullptr,
+                                 0, 0, act_idx, act_off, B, N, g);
+  if (st != SL_OK || g.M == 0) return st;
+  g.clk = clocks;
+  g.clk_slots = clock_slots;
+  SL_TRY(sl::launch_gemm_clocked((sl::EpiKind)epilogue, g, (hipStream_t)stream), "sl_gemm_clocked launch");
   return SL_OK;
 }
 

@@ -343,7 +343,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // conditional load, or a direct-to-LDS load in the same kernel, makes the
 // compiler drain all loads before a slot is used.  Small LDS and register use
 // let two workgroups share a CU.
-template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI, bool VB>
+//
+// CLK (a measurement variant) records per workgroup the shader-clock cycles (s_memtime) and the
+// 100 MHz real-time ticks (s_memrealtime) it took, and the cycles of its k-tile loop: their ratio is
+// the clock the chip sustained under this load, and the loop's cycles against BM*BN*K*2 / 4096 (the
+// FLOPs one CU's four matrix cores retire per cycle) its MFMA utilisation at that clock.
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int EPI, bool VB, bool CLK = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, 2)))
 gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
@@ -368,6 +373,11 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
   const int m0 = bm * BM, n0 = bn * BN;
   const int Mr = rows_live(a.M, a.m_dev);   // rows to compute (a.M is their capacity and plane stride)
   if (m0 >= Mr) return;                     // uniform over the workgroup, before any barrier
+  unsigned long long clk_c0 = 0, clk_r0 = 0, clk_m0 = 0, clk_m1 = 0;
+  if constexpr (CLK) {
+    clk_c0 = __builtin_amdgcn_s_memtime();
+    clk_r0 = __builtin_amdgcn_s_memrealtime();
+  }
   const int split = blockIdx.z;
   const int KI = a.K * (int)sizeof(T) / RB;
   const int kt0 = split * k_iters_per_split;
@@ -479,6 +489,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
       barrier_no_fence();
       frags(smem, smem + BM * RB, 0, 0);
     }
+    if constexpr (CLK) clk_m0 = __builtin_amdgcn_s_memtime();
     for (int kt = kt0; kt < kt1; ++kt) {
       const bool pre = kt + S - 1 < kt1;
       const int pre_stage = (kt + S - 1 - kt0) % S;
@@ -534,6 +545,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
     };
 #pragma unroll
     for (int st = 0; st < RS; ++st) vload(min(kt0 + st, kt1 - 1), st);
+    if constexpr (CLK) clk_m0 = __builtin_amdgcn_s_memtime();
     int kb = kt0;
     for (; kb + RS <= kt1; kb += RS)
       static_for<0, RS>([&](auto U) { vtile(kb + decltype(U)::value, U); });
@@ -541,6 +553,7 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
       if (kb + decltype(U)::value < kt1) vtile(kb + decltype(U)::value, U);
     });
   }
+  if constexpr (CLK) clk_m1 = __builtin_amdgcn_s_memtime();
   __syncthreads();   // every wave is done with the pipeline's LDS
 
   // ---------------------------------------------------------------- epilogue
@@ -591,6 +604,17 @@ gemm_kernel(GemmArgs a, int MT, int NT, int k_iters_per_split) {
       __syncthreads();
     }
   }
+  if constexpr (CLK) {
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    const long w = (long)blockIdx.z * gridDim.x + blockIdx.x;
+    if (tid == 0 && a.clk && w < a.clk_slots) {
+      unsigned long long* o = a.clk + 4 * w;
+      o[0] = c1 - clk_c0;
+      o[1] = r1 - clk_r0;
+      o[2] = clk_m1 - clk_m0;
+      o[3] = (unsigned long long)(kt1 - kt0) * RB / sizeof(T);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -600,7 +624,7 @@ static int splits_launched(int KI, int split) {
   return (KI + kps - 1) / kps;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int RB, int S, bool VB = false>
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, bool VB = false, bool CLK = false>
 static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int split) {
   const int MT = (a.M + BM - 1) / BM, NT = a.Nv / BN;
   const int KI = a.K * (int)sizeof(T) / RB;
@@ -609,6 +633,14 @@ static hipError_t run_cfg(EpiKind epi, const GemmArgs& a, hipStream_t s, int spl
   GemmArgs b = a;
   b.split_k = nsplit;
   const dim3 grid(MT * NT, 1, nsplit), block(64 * WM * WN);
+  if constexpr (CLK) {
+    switch (epi) {
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_SWIGLU, VB, true>), grid, block, 0, s, b, MT, NT, kps); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_LOGITS, VB, true>), grid, block, 0, s, b, MT, NT, kps); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (epi) {
     case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_QKV, VB>), grid, block, 0, s, b, MT, NT, kps); break;
     case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, EPI_RESID, VB>), grid, block, 0, s, b, MT, NT, kps); break;
@@ -710,24 +742,24 @@ int gemm_supported(int dtype, EpiKind epi, int Nv, int K, int d, int Dh) {
   return 1;
 }
 
-template <typename T>
+template <typename T, bool CLK = false>
 static hipError_t launch_t(EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit) {
   int c, split;
   pick_cfg(a, epi, (int)sizeof(T), a.part != nullptr, c, split);
   if (nsplit) *nsplit = c >= 0 ? splits_launched(a.K * (int)sizeof(T) / kCfgs[c].RB, split) : 1;
   switch (c) {
-    case 0: return run_cfg<T, 256, 256, 2, 4, 64, 4>(epi, a, s, split);
-    case 1: return run_cfg<T, 256, 128, 4, 2, 128, 3>(epi, a, s, split);
-    case 2: return run_cfg<T, 128, 256, 2, 4, 128, 3>(epi, a, s, split);
-    case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3>(epi, a, s, split);
-    case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4>(epi, a, s, split);
-    case 5: return run_cfg<T, 256, 192, 2, 2, 64, 4>(epi, a, s, split);
-    case 6: return run_cfg<T, 128, 384, 2, 2, 64, 4>(epi, a, s, split);
-    case 7: return run_cfg<T, 64, 128, 1, 4, 128, 6>(epi, a, s, split);
-    case 8: return run_cfg<T, 64, 64, 2, 2, 128, 8>(epi, a, s, split);
-    case 9: return run_cfg<T, 64, 128, 1, 4, 128, 6, true>(epi, a, s, split);
-    case 10: return run_cfg<T, 128, 96, 4, 1, 128, 4>(epi, a, s, split);
-    case 11: return run_cfg<T, 128, 192, 2, 2, 128, 3>(epi, a, s, split);
+    case 0: return run_cfg<T, 256, 256, 2, 4, 64, 4, false, CLK>(epi, a, s, split);
+    case 1: return run_cfg<T, 256, 128, 4, 2, 128, 3, false, CLK>(epi, a, s, split);
+    case 2: return run_cfg<T, 128, 256, 2, 4, 128, 3, false, CLK>(epi, a, s, split);
+    case 3: return run_cfg<T, 128, 128, 2, 2, 128, 3, false, CLK>(epi, a, s, split);
+    case 4: return run_cfg<T, 128, 64, 4, 1, 128, 4, false, CLK>(epi, a, s, split);
+    case 5: return run_cfg<T, 256, 192, 2, 2, 64, 4, false, CLK>(epi, a, s, split);
+    case 6: return run_cfg<T, 128, 384, 2, 2, 64, 4, false, CLK>(epi, a, s, split);
+    case 7: return run_cfg<T, 64, 128, 1, 4, 128, 6, false, CLK>(epi, a, s, split);
+    case 8: return run_cfg<T, 64, 64, 2, 2, 128, 8, false, CLK>(epi, a, s, split);
+    case 9: return run_cfg<T, 64, 128, 1, 4, 128, 6, true, CLK>(epi, a, s, split);
+    case 10: return run_cfg<T, 128, 96, 4, 1, 128, 4, false, CLK>(epi, a, s, split);
+    case 11: return run_cfg<T, 128, 192, 2, 2, 128, 3, false, CLK>(epi, a, s, split);
   }
   return hipErrorInvalidValue;
 }
@@ -750,6 +782,12 @@ int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv) {
   int c, sp;
   pick_cfg(a, epi, eb, true, c, sp);
   return c >= 0 ? splits_launched(K * eb / kCfgs[c].RB, sp) : 1;
+}
+
+hipError_t launch_gemm_clocked(EpiKind epi, const GemmArgs& a, hipStream_t s) {
+  if (epi != EPI_SWIGLU && epi != EPI_LOGITS) return hipErrorInvalidValue;
+  if (a.M <= 0) return hipSuccess;
+  return launch_t<bf16, true>(epi, a, s, nullptr);
 }
 
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit) {

@@ -121,9 +121,16 @@ struct GemmArgs {
   float* klp;
   int mask_id;           // id left out of the argmax (-1: none)
   int kv_hm;             // QKV: caches head-major [B][H][N][Dh] (0: token-major [B][N][H][Dh])
+  // clock record (launch_gemm_clocked only): per workgroup w < clk_slots, clk[4w..4w+3] = shader-clock
+  // cycles and 100 MHz real-time ticks of the whole workgroup, cycles of its k-tile loop, K elements it
+  // multiplied (slots of workgroups past the live rows are left untouched)
+  unsigned long long* clk;
+  int clk_slots;
 };
 // nsplit (may be NULL) receives the number of K splits launched.
 hipError_t launch_gemm(int dtype, EpiKind epi, const GemmArgs& a, hipStream_t s, int* nsplit = nullptr);
+// launch_gemm with the clock record of GemmArgs::clk (bf16, SwiGLU or logits epilogue only).
+hipError_t launch_gemm_clocked(EpiKind epi, const GemmArgs& a, hipStream_t s);
 // Number of K splits launch_gemm runs for this shape when partial-sum planes are
 // provided (GemmArgs::part set; 1 = none): the planes' workspace is sized from it.
 int gemm_split(int dtype, EpiKind epi, int M, int K, int Nv);

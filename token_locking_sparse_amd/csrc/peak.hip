@@ -34,6 +34,49 @@ __global__ void __launch_bounds__(256) mfma_peak_kernel(int iters, float* sink) 
   if (s == 1234.5f) sink[threadIdx.x] = s;
 }
 
+// The same loop on operands read from memory: eight A and eight B fragments per lane (16-byte chunk
+// (2 i) * 256 + t and (2 i + 1) * 256 + t of `ops` for set i, thread t), rotated so that consecutive
+// MFMAs of a chain multiply different values.  The matrix cores' power, and with it the clock the chip
+// sustains, depends on the operand bits: random bf16 operands hold it well below what constant ones
+// do.  clocks[2 w], clocks[2 w + 1] (w < nclk) receive the shader-clock cycles (s_memtime) and the
+// 100 MHz real-time ticks (s_memrealtime) that workgroup w took.
+constexpr int kOperandSets = 8;
+
+__global__ void __launch_bounds__(256)
+mfma_operand_kernel(int iters, const u32x4* __restrict__ ops, float* sink, unsigned long long* clocks, int nclk) {
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  const int t = threadIdx.x;
+  u32x4 a[kOperandSets], b[kOperandSets];
+#pragma unroll
+  for (int i = 0; i < kOperandSets; ++i) {
+    a[i] = ops[(2 * i) * 256 + t];
+    b[i] = ops[(2 * i + 1) * 256 + t];
+  }
+  f32x16 acc[kPeakChains];
+#pragma unroll
+  for (int c = 0; c < kPeakChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+  for (int i = 0; i < iters; i += kOperandSets) {
+#pragma unroll
+    for (int u = 0; u < kOperandSets; ++u)
+#pragma unroll
+      for (int c = 0; c < kPeakChains; ++c)
+        Mfma<bf16>::run(acc[c], a[(u + c) % kOperandSets], b[(u + 3 * c + 1) % kOperandSets]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kPeakChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[c][v];
+  if (s == 1234.5f) sink[t] = s;
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (clocks && t == 0 && (int)blockIdx.x < nclk) {
+    clocks[2 * blockIdx.x] = c1 - c0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 // Streaming copy (16-byte non-temporal loads and stores, each workgroup on a
 // contiguous range) and streaming read (the loads summed into a register).
 constexpr int kStreamThreads = 256, kStreamUnroll = 8;
@@ -164,6 +207,14 @@ sl_status sl_peak_mfma(int workgroups, int iters, float* sink, sl_stream stream)
 
 double sl_peak_mfma_flops(int workgroups, int iters) {
   return (double)workgroups * 4 /* waves */ * iters * sl::kPeakChains * 2.0 * 32 * 32 * 16;
+}
+
+sl_status sl_peak_mfma_operands(int workgroups, int iters, const void* operands, float* sink,
+                                unsigned long long* clocks, sl_stream stream) {
+  if (workgroups <= 0 || iters <= 0 || iters % sl::kOperandSets || !operands || !sink) return SL_ERR_INVALID;
+  hipLaunchKernelGGL(sl::mfma_operand_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters,
+                     (const sl::u32x4*)operands, sink, clocks, clocks ? workgroups : 0);
+  return hipGetLastError() == hipSuccess ? SL_OK : SL_ERR_HIP;
 }
 
 sl_status sl_peak_stream(const void* src, void* dst, size_t bytes, int workgroups, float* sink, sl_stream stream) {

@@ -63,7 +63,7 @@ EXPORTS = ("sl_status_string", "sl_last_error", "sl_version", "sl_compact", "sl_
            "sl_attn_active", "sl_attn_workspace_size", "sl_kl_lock", "sl_kl_lock_workspace_size",
            "sl_rope_table", "sl_step", "sl_step_workspace_size", "sl_step_workspace_min", "sl_gemm",
            "sl_gemm_plan", "sl_kl_lock_noalloc", "sl_peak_mfma", "sl_peak_mfma_flops", "sl_peak_stream",
-           "sl_peak_gemm_loop", "sl_peak_gemm_loop_flops")
+           "sl_peak_gemm_loop", "sl_peak_gemm_loop_flops", "sl_peak_mfma_operands", "sl_gemm_clocked")
 
 _lib = None
 
@@ -102,6 +102,8 @@ def lib():
         "sl_peak_stream": (i, [vp, vp, sz, i, vp, vp]),
         "sl_peak_gemm_loop": (i, [i, i, i, vp, vp, vp]),
         "sl_peak_gemm_loop_flops": (C.c_double, [i, i]),
+        "sl_peak_mfma_operands": (i, [i, i, vp, vp, vp, vp]),
+        "sl_gemm_clocked": (i, [i, vp, i, i, i, vp, vp, vp, vp, vp, i, i, vp, i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -299,6 +301,35 @@ def sl_peak_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
     """Launch the register-only MFMA loop; returns the FLOPs it performs."""
     _check("sl_peak_mfma", lib().sl_peak_mfma(workgroups, iters, _ptr(sink, "sink", torch.float32), _stream(stream)))
     return float(lib().sl_peak_mfma_flops(workgroups, iters))
+
+
+def sl_peak_mfma_operands(workgroups: int, iters: int, operands, sink, clocks=None, stream=None) -> float:
+    """The MFMA loop on operands read from `operands` (16 x 256 chunks of 16 bytes); clocks (int64,
+    2 x workgroups, optional) receives per workgroup its shader-clock cycles and 100 MHz ticks.
+    Returns the FLOPs it performs."""
+    if operands.numel() * operands.element_size() < 16 * 256 * 16:
+        raise ValueError("operands must hold 16 x 256 chunks of 16 bytes")
+    if clocks is not None and (clocks.dtype != torch.int64 or clocks.numel() < 2 * workgroups):
+        raise ValueError("clocks must be int64 with 2 x workgroups entries")
+    _check("sl_peak_mfma_operands", lib().sl_peak_mfma_operands(workgroups, iters, _ptr(operands, "operands"),
+                                                                _ptr(sink, "sink", torch.float32),
+                                                                _ptr(clocks, "clocks", optional=True),
+                                                                _stream(stream)))
+    return float(lib().sl_peak_mfma_flops(workgroups, iters))
+
+
+def sl_gemm_clocked(epilogue, A, M, K, n_out, w0, w1=None, out0=None, act_idx=None, act_off=None, B=0, N=0,
+                    clocks=None, stream=None):
+    """sl_gemm (bf16, SwiGLU or logits epilogue) recording per workgroup, in clocks (int64, 4 per
+    workgroup): shader-clock cycles, 100 MHz ticks, cycles of the k-tile loop, K elements multiplied."""
+    if clocks is None or clocks.dtype != torch.int64 or clocks.numel() < 4:
+        raise ValueError("clocks must be an int64 device tensor of 4 x workgroups entries")
+    st = lib().sl_gemm_clocked(int(epilogue), _ptr(A, "A", torch.bfloat16), M, K, n_out,
+                               _ptr(w0, "w0", torch.bfloat16), _ptr(w1, "w1", torch.bfloat16, optional=True),
+                               _ptr(out0, "out0"), _ptr(act_idx, "act_idx", torch.int32, optional=True),
+                               _ptr(act_off, "act_off", torch.int32, optional=True), B, N,
+                               _ptr(clocks, "clocks"), clocks.numel() // 4, _stream(stream))
+    _check("sl_gemm_clocked", st)
 
 
 def sl_peak_gemm_loop(workgroups: int, tiles: int, with_loads: bool, src, sink, stream=None) -> float:
