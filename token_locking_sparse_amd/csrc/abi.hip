@@ -128,8 +128,9 @@ sl_status check_model(const sl_model* m) {
 
 // Scratch memory of sl_kl_lock_noalloc: the vocabulary pass's per-segment partial sums live in this
 // file-scope device array instead of a caller workspace.  Every (M_tot, V) needs at most
-// (M_tot * ceil(6144 / M_tot)) * 32 < 8192 * 32 bytes of partials (rows are split only while
-// M_tot < 2048), so 256 KiB covers every size sl_kl_lock accepts.  Each device holds its own
+// M_tot * (segments per row) * 32 < 4096 * 32 bytes of partials (rows are split only while
+// M_tot < 2048: into at most four below 768 rows, two from there on), so 256 KiB covers every
+// size sl_kl_lock accepts.  Each device holds its own
 // copy; host code reaches it only through the address hipGetSymbolAddress returns for the current
 // device (the array's name on the host is not a device address).
 constexpr size_t kNoAllocScratchBytes = 256 * 1024;

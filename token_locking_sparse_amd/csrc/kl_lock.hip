@@ -891,13 +891,18 @@ kl_tail_kernel(KLRowParams rp, TailParams tp, int n_seg, const float* part) {
   }
 }
 
-// Segments per row: rows are split (into at most kMaxSeg) only while there are fewer than
-// kSplitBelow of them, so that the tail merges every split row in one round (kMergeRows rows per
-// thread), aiming at about 6144 workgroups (24 per CU): short workgroups keep every CU streaming
-// through the ends of the launch.  Partials then take at most M * ceil(6144 / M) < 8192 slots.
-// A segment is a whole number of thread groups (GroupChunks * kKLThreads chunks), so that only
-// the row's last segment ends in a partial group.
+// Segments per row: rows are split only while there are fewer than kSplitBelow of them, so that
+// the tail merges every split row in one round (kMergeRows rows per thread): into kMaxSeg below
+// kFourSegBelow rows, where fewer workgroups would leave CUs idle through the ends of the launch,
+// and into two from there on.  Measured at N = 4096, V = 126464 (bf16, previous LSE from the
+// store), two segments per row against four: 82.0 / 92.5 / 115.8 / 137.0 / 159.8 us against
+// 81.9 / 95.0 / 117.2 / 141.8 / 161.6 us at 799 / 1024 / 1311 / 1639 / 1926 rows, three segments
+// no better than four: half the partials for the one-workgroup tail to merge, and fewer, longer
+// workgroups.  Partials then take at most 4 * 767 or 2 * 2047 < 4096 slots.  A segment is a whole
+// number of thread groups (GroupChunks * kKLThreads chunks), so that only the row's last segment
+// ends in a partial group.
 constexpr int kSplitBelow = 2048;
+constexpr int kFourSegBelow = 768;
 struct KlSplit {
   int n_seg, seg_chunks;
 };
@@ -906,7 +911,7 @@ static KlSplit kl_split(int M_tot, int V, int elem_bytes) {
   constexpr int G = GroupChunks * kKLThreads;
   int n = 1;
   if (M_tot > 0 && M_tot < kSplitBelow) {
-    const int want = (6144 + M_tot - 1) / M_tot;
+    const int want = M_tot < kFourSegBelow ? kMaxSeg : 2;
     const int maxseg = C / G > 1 ? C / G : 1;
     n = want < maxseg ? want : maxseg;
     n = n < kMaxSeg ? n : kMaxSeg;
