@@ -1005,6 +1005,15 @@ def cpu_configs():
     return out
 
 
+def leg(name, fn):
+    """Run one leg of the bench and note its end on stderr (the JSON line stays alone on stdout)."""
+    import time
+    t0 = time.time()
+    r = fn()
+    print("bench: %s done in %.1f s" % (name, time.time() - t0), file=sys.stderr, flush=True)
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1043,8 +1052,8 @@ def main():
               "(sequences are independent, so data parallelism needs no collective). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    res = gpu_part(args)
-    peaks = measured_peaks()
+    res = leg("layer sweep and KL-lock pass", lambda: gpu_part(args))
+    peaks = leg("measured peaks", measured_peaks)
     line = {
         "metric": METRIC,
         "value": res["value"],
@@ -1069,14 +1078,14 @@ def main():
         "roofline": res["roofline"],
         "roofline_kl": res["roofline_kl"],
         "measured_peaks": peaks,
-        "gemm_clock": gemm_clock_study(),
-        "cache_layout": cache_layout_study(),
-        "batched_step": None if args.no_batched else batched_step(),
-        "tiny_loop": tiny_loop(),
-        "e2e_loop": None if args.no_e2e else e2e_loop(runs=SURELOCK_RUNS + ABLATION_RUNS),
-        "e2e_loop_b8": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[0], SURELOCK_RUNS[2]), B=8),
-        "e2e_loop_captured": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[2],), captured=True),
-        "e2e_loop_b8_captured": None if args.no_e2e else e2e_loop(runs=(SURELOCK_RUNS[2],), B=8, captured=True),
+        "gemm_clock": leg("GEMM clock", gemm_clock_study),
+        "cache_layout": leg("cache layout", cache_layout_study),
+        "batched_step": None if args.no_batched else leg("batched step", batched_step),
+        "tiny_loop": leg("tiny loop", tiny_loop),
+        "e2e_loop": None if args.no_e2e else leg("sampler loop", lambda: e2e_loop(runs=SURELOCK_RUNS + ABLATION_RUNS)),
+        "e2e_loop_b8": None if args.no_e2e else leg("sampler loop B=8", lambda: e2e_loop(runs=(SURELOCK_RUNS[0], SURELOCK_RUNS[2]), B=8)),
+        "e2e_loop_captured": None if args.no_e2e else leg("captured loop", lambda: e2e_loop(runs=(SURELOCK_RUNS[2],), captured=True)),
+        "e2e_loop_b8_captured": None if args.no_e2e else leg("captured loop B=8", lambda: e2e_loop(runs=(SURELOCK_RUNS[2],), B=8, captured=True)),
         "cpu_baseline": None,
     }
     # fractions of the measured ceilings, beside the vendor ones
@@ -1090,8 +1099,8 @@ def main():
     for r in line["per_M"]:
         r["frac_measured_mfma_peak"] = round(r["tflops"] / peaks["mfma_bf16_tflops"], 4)
     if not args.no_cpu:
-        cb = cpu_part(args.cpu_seconds)
-        cb["per_config"] = cpu_configs()
+        cb = leg("oracle baseline", lambda: cpu_part(args.cpu_seconds))
+        cb["per_config"] = leg("oracle per configuration", cpu_configs)
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
