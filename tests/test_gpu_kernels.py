@@ -5,7 +5,7 @@ bit-exact, except (for sl_kl_lock) positions whose oracle KL lies within 1e-3
 of eps (the tolerance band the lock rule allows) or whose oracle u lies within
 GATE_BAND = 4e-6 of the oracle gate threshold (twice the asserted 2e-6 bound on
 the fp32 u: an fp32 u and the fp64 u can order values that close differently).
-Floating-point outputs: KL within 2e-5 (the benchmark spec's band is 1e-3); LSE, u,
+Floating-point outputs: KL within 2e-5 (the lock rule's band is 1e-3); LSE, u,
 conf within the fp32 accumulation error of a V-term sum; bf16 GEMM outputs within
 half a bf16 ulp plus fp32 accumulation; bf16 attention outputs within the margin
 over the bf16-storage emulation (tests/bf16_emulation.py) of the same inputs.
