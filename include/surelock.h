@@ -152,7 +152,8 @@ typedef struct {
  *            a stale lse_prev gives a wrong KL.  Must not alias lse_pos.
  *   gate_thr [B] float or NULL.
  *   new_act_idx [B*N] capacity, new_act_off [B+1] (may alias act_idx / act_off).
- *   ws       at least sl_kl_lock_workspace_size(...) bytes (any contents).
+ *   ws       at least sl_kl_lock_workspace_size(B, N, M_tot, V) bytes (any contents); that size
+ *            serves every call with at most M_tot active rows.
  * Limits: V % 8 == 0 (bf16) or V % 4 == 0 (f32); N <= 65536.
  */
 sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,

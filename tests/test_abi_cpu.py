@@ -86,6 +86,11 @@ def test_workspace_sizes_are_monotone_in_rows():
     a = S.sl_kl_lock_workspace_size(1, 4096, 100, 126464)
     b = S.sl_kl_lock_workspace_size(1, 4096, 1639, 126464)
     assert b >= a > 0
+    # a KL-lock workspace sized for M rows serves every call with fewer: the size never falls with M,
+    # across the changes of segments per row (768 rows) and the end of splitting (2048 rows)
+    kl_sorted_m = [S.sl_kl_lock_workspace_size(1, 4096, M, 126464) for M in sorted(list(range(1, 2200, 13)) + [767, 768, 2047, 2048, 4096])]
+    assert all(x <= y for x, y in zip(kl_sorted_m, kl_sorted_m[1:]))
+    assert kl_sorted_m[-1] <= 256 * 1024   # within sl_kl_lock_noalloc's scratch
     assert S.sl_attn_workspace_size(1, 1024, 64, 32, 128) > 0
 
 

@@ -235,11 +235,26 @@ sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const vo
   return SL_OK;
 }
 
-size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V) {
-  // segment partials, sized for whichever element type splits rows more
-  (void)B; (void)N;
+namespace {
+// Segment partials one call with M_tot active rows needs, sized for whichever element type splits
+// rows more.
+size_t kl_ws_exact(int M_tot, int V) {
   const size_t p2 = sl::kl_part_bytes(M_tot, V, 2), p4 = sl::kl_part_bytes(M_tot, V, 4);
   return align256(p2 > p4 ? p2 : p4);
+}
+}  // namespace
+
+size_t sl_kl_lock_workspace_size(int B, int N, int M_tot, int V) {
+  // The largest any call with at most M_tot rows needs: rows split into more segments below 768
+  // rows than above, and not at all from 2048 rows on, so the need is not monotone in M_tot.
+  (void)B; (void)N;
+  size_t best = kl_ws_exact(M_tot, V);
+  const int top = M_tot < 2048 ? M_tot : 2047;
+  for (int m = 1; m <= top; ++m) {
+    const size_t b = kl_ws_exact(m, V);
+    if (b > best) best = b;
+  }
+  return best;
 }
 
 sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev, int V,
@@ -262,7 +277,7 @@ sl_status sl_kl_lock(int dtype, const void* logits_cur, const void* logits_prev,
   SL_REQUIRE(M_tot == 0 || !params->have_prev || logits_prev, SL_ERR_INVALID, "NULL logits_prev");
   SL_REQUIRE(params->gate_q <= 1.f, SL_ERR_INVALID, "gate_q > 1");
   SL_REQUIRE(params->mask_id < V, SL_ERR_INVALID, "mask_id >= V");
-  const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
+  const size_t need = kl_ws_exact(M_tot, V);
   SL_REQUIRE(ws_bytes >= need, SL_ERR_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
   SL_REQUIRE(!(lse_prev && lse_pos) || lse_prev != lse_pos, SL_ERR_INVALID,
              "lse_prev and lse_pos are the same buffer (keep two, as for the logits)");
@@ -293,7 +308,7 @@ sl_status sl_kl_lock_noalloc(int dtype, const void* logits_cur, const void* logi
                              int32_t* m_tot_host, sl_stream stream) {
   g_err[0] = 0;
   SL_REQUIRE(B >= 1 && N >= 1 && V > 0 && M_tot >= 0, SL_ERR_INVALID, "bad size");
-  const size_t need = sl_kl_lock_workspace_size(B, N, M_tot, V);
+  const size_t need = kl_ws_exact(M_tot, V);
   SL_REQUIRE(need <= kNoAllocScratchBytes, SL_ERR_UNSUPPORTED,
              "sl_kl_lock_noalloc: %zu bytes of partial sums exceed its %zu-byte scratch", need, kNoAllocScratchBytes);
   void* ws = nullptr;
