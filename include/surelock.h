@@ -108,8 +108,9 @@ sl_status sl_cache_scatter(int dtype, void* k_cache, void* v_cache, const void* 
  *            page, 消融实验: locked positions cannot be attended; pass the
  *            lock mask).  Every query row must keep at least one key.
  *   out      [M_tot][H*Dh] of `dtype`.
- *   ws       workspace of at least sl_attn_workspace_size(...) bytes (any
- *            contents; used for split-KV partial results).
+ *   ws       workspace of at least sl_attn_workspace_size(B, N, M_tot, H, Dh)
+ *            bytes (any contents; used for split-KV partial results); that
+ *            size serves every call with at most M_tot query rows.
  * Limits: Dh in {32, 64, 128}; N % 64 == 0.
  */
 sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -92,6 +92,9 @@ def test_workspace_sizes_are_monotone_in_rows():
     assert all(x <= y for x, y in zip(kl_sorted_m, kl_sorted_m[1:]))
     assert kl_sorted_m[-1] <= 256 * 1024   # within sl_kl_lock_noalloc's scratch
     assert S.sl_attn_workspace_size(1, 1024, 64, 32, 128) > 0
+    # likewise the attention's: key splits come and go with M, the size never falls
+    at = [S.sl_attn_workspace_size(1, 1024, M, 32, 128) for M in range(1, 1025, 9)]
+    assert all(x <= y for x, y in zip(at, at[1:]))
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -211,7 +211,16 @@ sl_status sl_cache_scatter(int dtype, void* k_cache, void* v_cache, const void* 
 }
 
 size_t sl_attn_workspace_size(int B, int N, int M_tot, int H, int Dh) {
-  return sl::attn_ws_bytes(B, N, M_tot, H, Dh);
+  // The largest any call with at most M_tot rows needs: keys are split (and per-split partials
+  // stored) only when few query tiles would leave the chip idle, so the need is not monotone in M_tot.
+  // Splits need fewer than 64 workgroups of at most 128 queries: none from 8192 rows on.
+  size_t best = sl::attn_ws_bytes(B, N, M_tot, H, Dh);
+  const int top = M_tot < 8192 ? M_tot : 8192;
+  for (int m = 1; m < top; ++m) {
+    const size_t b = sl::attn_ws_bytes(B, N, m, H, Dh);
+    if (b > best) best = b;
+  }
+  return best;
 }
 
 sl_status sl_attn_active(int dtype, const void* q, const void* k_cache, const void* v_cache,
