@@ -451,6 +451,8 @@ ATTN_CASES = [
     ("bf16", 128, 8, 512, [300, 1, 77]),  # heads a multiple of 8 (XCD placement), ragged
     ("bf16", 128, 16, 1024, [640]),       # several query tiles per head, no split
     ("bf16", 128, 32, 1024, [1024]),      # 128-query workgroups (two key groups)
+    ("bf16", 128, 32, 1024, [256]),       # 64-query workgroups, four key groups of 256 keys, half the chip
+    ("bf16", 128, 32, 1024, [100, 28]),   # the same with two sequences and ragged tiles
     ("bf16", 128, 32, 1024, [600, 500]),  # same, ragged tails in both sequences
     ("bf16", 128, 32, 576, [560]),        # nine key tiles: one key group has none in the last round
     ("bf16", 64, 2, 128, [1, 128, 70]),
