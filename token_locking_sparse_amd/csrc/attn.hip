@@ -484,6 +484,21 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   const int g16 = lane >> 4, s16 = lane & 15;
   const int tr_dhalf = 16 * (g16 & 1);            // d0 within the 32-wide d-tile
   const int tr_khalf = 4 * (g16 >> 1);            // 4 hl
+  // Per-lane byte offsets of every LDS read of a tile, fixed across tiles: the swizzles depend on the
+  // key row only through row % 16 (K) and row % 4 (V), which the lane fixes, so what remains per read
+  // (32-key subtile, 16-key k-step, second half of the transpose pair) is a constant immediate.
+  // K fragment kk: row l32 (+ 32 sub), chunk (2 kk + hl) ^ (l32 % 16).
+  uint32_t kofs[nKK];
+#pragma unroll
+  for (int kk = 0; kk < nKK; ++kk) kofs[kk] = l32 * kTrRB + swz<kTrRB>(l32, 2 * kk + hl) * 16;
+  // V^T d-tile dt: row tr_khalf + s16 / 4 (+ 16 m, + 8 for the second read), column
+  // 32 dt + tr_dhalf + 4 (s16 % 4), chunk placed by vswz of that row.
+  uint32_t vofs[Dh / 32];
+#pragma unroll
+  for (int dt = 0; dt < Dh / 32; ++dt) {
+    const int kr = tr_khalf + (s16 >> 2), d = 32 * dt + tr_dhalf + 4 * (s16 & 3);
+    vofs[dt] = kr * kTrRB + vswz(kr, d >> 3) * 16 + (d & 7) * 2;
+  }
   f32x16 oacc[Dh / 32];
 #pragma unroll
   for (int i = 0; i < Dh / 32; ++i)
@@ -517,10 +532,9 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
     for (int sub = 0; sub < NS; ++sub) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[sub][v] = 0.f;
-      const int kr = sub * 32 + l32;
 #pragma unroll
       for (int kk = 0; kk < nKK; ++kk) {
-        const u32x4 a = *(const u32x4*)(ks + kr * kTrRB + swz<kTrRB>(kr, 2 * kk + hl) * 16);
+        const u32x4 a = *(const u32x4*)(ks + kofs[kk] + sub * 32 * kTrRB);
         Mfma<bf16>::run(sc[sub], a, qf[kk]);
       }
       if constexpr (EXCL) mask_scores(sc[sub], mcur[sub]);
@@ -564,14 +578,10 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
       u32x4 pb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = pack_bf16x2(sc[sub][r0 + 2 * i], sc[sub][r0 + 2 * i + 1]);
-      const int kr0 = 16 * m + tr_khalf + (s16 >> 2);   // key row of the first read
-      const int kr1 = kr0 + 8;
 #pragma unroll
       for (int dt = 0; dt < Dh / 32; ++dt) {
-        const int d = 32 * dt + tr_dhalf + 4 * (s16 & 3);
-        const int c = d >> 3, cb = (d & 7) * 2;
-        const uint2 x0 = lds_tr16(vs + kr0 * kTrRB + vswz(kr0, c) * 16 + cb);
-        const uint2 x1 = lds_tr16(vs + kr1 * kTrRB + vswz(kr1, c) * 16 + cb);
+        const uint2 x0 = lds_tr16(vs + vofs[dt] + 16 * m * kTrRB);
+        const uint2 x1 = lds_tr16(vs + vofs[dt] + (16 * m + 8) * kTrRB);
         u32x4 a;
         a[0] = x0.x; a[1] = x0.y; a[2] = x1.x; a[3] = x1.y;
         Mfma<bf16>::run(oacc[dt], a, pb);
