@@ -590,14 +590,16 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   }
   __syncthreads();   // stages free
 
-  // groups 1 .. G-1 hand their partials (O^T registers, m, l; lane and register
-  // order) to the group-0 wave of the same queries, which merges the online softmaxes
+  // groups 1 .. G-1 hand their partials (O^T registers in runs of four, m, l) to the group-0
+  // wave of the same queries, which merges the online softmaxes
   if (grp > 0) {
     float* mg = (float*)smem + ((grp - 1) * QW + wq) * kTrMergeWave;
 #pragma unroll
     for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mg[(dt * 16 + v) * 64 + lane] = oacc[dt][v];
+      for (int vb = 0; vb < 4; ++vb)
+        *(f32x4*)(mg + ((dt * 4 + vb) * 64 + lane) * 4) =
+            f32x4{oacc[dt][4 * vb], oacc[dt][4 * vb + 1], oacc[dt][4 * vb + 2], oacc[dt][4 * vb + 3]};
     mg[64 * (Dh / 2) + lane] = m_run;
     mg[64 * (Dh / 2) + 64 + lane] = l_run;
   }
@@ -612,30 +614,35 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
 #pragma unroll
       for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][v] = oacc[dt][v] * a0 + mg[(dt * 16 + v) * 64 + lane] * a1;
+        for (int vb = 0; vb < 4; ++vb) {
+          const f32x4 o = *(const f32x4*)(mg + ((dt * 4 + vb) * 64 + lane) * 4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[dt][4 * vb + r] = oacc[dt][4 * vb + r] * a0 + o[r] * a1;
+        }
       l_run = l_run * a0 + l_o * a1;
       m_run = m_new;
     }
   }
-  __syncthreads();   // merge area free for the output staging
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool final_out = (nsplit == 1);
-  const float inv = (final_out && l_tot > 0.f) ? 1.f / l_tot : 1.f;
-  float* ep = (float*)smem + wq * 32 * (Dh + 1);
-  if (grp == 0) {
+  const int nrow = min(32, row_end - wrow0);
+  if (nsplit == 1) {
+    // the normalised bf16 output, staged through LDS as a row-major fp32 tile so that every store
+    // writes 16 consecutive bytes of a row (measured faster than 8-byte stores from the registers)
+    __syncthreads();   // merge area free for the output staging
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 1.f;
+    float* ep = (float*)smem + wq * 32 * (Dh + 1);
+    if (grp == 0) {
 #pragma unroll
-    for (int dt = 0; dt < Dh / 32; ++dt)
+      for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
-        ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
-      }
-  }
-  __syncthreads();
-  if (grp == 0 && wave_live) {
-    const int nrow = min(32, row_end - wrow0);
-    if (final_out) {
+        for (int v = 0; v < 16; ++v) {
+          const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
+          ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
+        }
+    }
+    __syncthreads();
+    if (grp == 0 && wave_live) {
       constexpr int CPR = Dh / E;
       for (int id = lane; id < 32 * CPR; id += 64) {
         const int rr = id / CPR, c = id % CPR;
@@ -647,23 +654,21 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
           st16((char*)(out + (size_t)(wrow0 + rr) * HD + (size_t)h * Dh) + c * 16, w);
         }
       }
-    } else {
-      constexpr int CPR = Dh / 4;
-      for (int id = lane; id < 32 * CPR; id += 64) {
-        const int rr = id / CPR, c = id % CPR;
-        if (rr < nrow) {
-          const float* src = ep + rr * (Dh + 1) + c * 4;
-          u32x4 w;
+    }
+  } else if (grp == 0 && wave_live && l32 < nrow) {
+    // this split's fp32 partial straight from the registers: lane (l32, hl) holds, for d-tile dt
+    // and register run vb, O^T[d0 .. d0 + 3][query l32] with d0 = 32 dt + 8 vb + 4 hl
+    float* prow = part_o + (((size_t)split * M_tot + wrow0 + l32) * H + h) * Dh;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(src[i]);
-          st16(part_o + (((size_t)split * M_tot + wrow0 + rr) * H + h) * Dh + c * 4, w);
-        }
-      }
-      if (hl == 0 && l32 < nrow) {
-        float* ml = part_ml + (((size_t)split * M_tot + wrow0 + l32) * H + h) * 2;
-        ml[0] = m_run;
-        ml[1] = l_tot;
-      }
+    for (int dt = 0; dt < Dh / 32; ++dt)
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+        *(f32x4*)(prow + 32 * dt + 8 * vb + 4 * hl) =
+            f32x4{oacc[dt][4 * vb], oacc[dt][4 * vb + 1], oacc[dt][4 * vb + 2], oacc[dt][4 * vb + 3]};
+    if (hl == 0) {
+      float* ml = part_ml + (((size_t)split * M_tot + wrow0 + l32) * H + h) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
     }
   }
 }
