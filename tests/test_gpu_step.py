@@ -230,6 +230,16 @@ def _deep_logits_check(gz, z, ez, what):
     return E.bounds(es)[1]
 
 
+def _kl_band(ez, z, prev64, mask_id, what):
+    """Bound on the GPU's step KL against the oracle's after many bf16 layers: the target's 1e-3, or,
+    where the bf16 storage alone moves the KL further, the margin over the largest KL error of the
+    bf16-storage emulation of the step against the same previous posterior."""
+    d = np.abs(O.posterior_stats(ez, prev64, mask_id).kl - O.posterior_stats(z, prev64, mask_id).kl)
+    band = max(KL_BAND, E.MARGIN * float(d.max()))
+    say("%s: emulated max |d| %.3e, bound %.3e" % (what, float(d.max()), band))
+    return band
+
+
 def _argmax_check(gz, z, mask_id, zbound, what):
     """argmax over ids other than [MASK]: a mismatch only where the oracle's top two are within
     twice the logits bound (each of the two may move by that much)."""
@@ -292,8 +302,9 @@ def test_full_model_steps_t0_t1_32_layers():
     Logits: within 1.25x the error of the bf16-storage emulation of the t = 0 step (after 32 layers
     the roundings compound to a relative L2 near 1.2e-2; the t = 1 step differs from it in three
     tokens only); the LM head alone within max-abs 2e-2 of the product of the GPU's own final hidden
-    rows.  KL within 1e-3 of the oracle's.  Gate, lock, compaction and sampler against the oracle's
-    rules on the GPU's own logits."""
+    rows.  KL within 1e-3 of the oracle's, or within 1.25x the KL error of the same emulation where
+    that is larger (after 32 layers the bf16 storage alone moves the KL of some rows by about 1e-3).
+    Gate, lock, compaction and sampler against the oracle's rules on the GPU's own logits."""
     sl = _sl()
     dm = W.LLADA_8B
     B, N, n_prompt, k_unmask, eps = 1, 512, 128, 3, 0.05
@@ -345,6 +356,15 @@ def test_full_model_steps_t0_t1_32_layers():
     ost.t = 1
     out1 = O.step(om, ost, eps, -1.0, True, dm.mask_id, prev_logits=prev64)
     z1 = out1.logits
+    # the KL bound of t = 1 from the bf16-storage emulation of this step: the three tokens unmasked at
+    # t = 0 move their rows' posteriors far from the previous ones, where the KL is most sensitive to
+    # the logits' error
+    say("32-layer step t=1: bf16-storage emulation")
+    ez1 = _emulated_logits(layers, om.embed[tok1], act, off,
+                           [np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)],
+                           [np.zeros((B, N, dm.n_heads, dm.head_dim)) for _ in range(dm.n_layers)], head64)
+    kl_band1 = _kl_band(ez1, z1, prev64, dm.mask_id, "t=1 KL")
+    del ez1
     say("32-layer step t=1: GPU, teacher-forced; oracle locks %d" % int(out1.lock.new_lock.sum()))
     st.tok.copy_(torch.from_numpy(tok1).cuda())
     st.cand.copy_(torch.from_numpy(cand1).cuda())
@@ -361,8 +381,9 @@ def test_full_model_steps_t0_t1_32_layers():
     _argmax_check(gz1, z1, dm.mask_id, zb, "t=1")
     _head_from_own_hidden_check(gz1, gh1, head64, dm.rms_eps, "t=1")
     kl1 = st.kl[:N].cpu().numpy()
-    assert np.max(np.abs(kl1 - out1.stats.kl)) <= KL_BAND
-    say("t=1 KL: max |d| against the oracle %.3e" % float(np.max(np.abs(kl1 - out1.stats.kl))))
+    say("t=1 KL: max |d| against the oracle %.3e (bound %.3e)" % (float(np.max(np.abs(kl1 - out1.stats.kl))),
+                                                                  kl_band1))
+    assert np.max(np.abs(kl1 - out1.stats.kl)) <= kl_band1
     # gate (off), lock and compaction on identical inputs: the GPU's logits, the same previous posterior
     stg1 = O.posterior_stats(gz1, prev64, dm.mask_id)
     lr1 = O.lock_update(np.zeros(N, np.uint8), act, off, B, N, stg1.kl, stg1.u, cand1, eps, -1.0, True)
@@ -388,8 +409,9 @@ def test_full_model_late_step_32_layers():
     Attending to random unit-variance caches grows the residual stream faster than at t = 0, and the
     bf16 roundings compound with it: the logits are held to 1.25x the bf16-storage emulation of this
     very step (relative L2 near 2.2e-2); the LM head alone to max-abs 2e-2 against the product of the
-    GPU's own final hidden rows.  KL within 1e-3 of the oracle's.  Gate, lock, compaction and sampler
-    against the oracle's rules on the GPU's own logits and the same previous posterior."""
+    GPU's own final hidden rows.  KL within 1e-3 of the oracle's, or 1.25x the KL error of the same
+    emulation where that is larger.  Gate, lock, compaction and sampler against the oracle's rules on
+    the GPU's own logits and the same previous posterior."""
     sl = _sl()
     dm = W.LLADA_8B
     B, N, t, eps, gate, k_unmask = 1, 512, 40, 0.05, 0.5, 3
@@ -424,6 +446,7 @@ def test_full_model_late_step_32_layers():
     ez = _emulated_logits(layers, om.embed[tok0[act]], act, off, [O.widen(k, "bf16") for k in kc_st],
                           [O.widen(v, "bf16") for v in vc_st], head64)
     es = E.err_stats(ez, z)
+    kl_band = _kl_band(ez, z, prev64, dm.mask_id, "late-step KL")
     del ez
     # GPU: the same state at step t
     say("32-layer late step: GPU")
@@ -450,7 +473,8 @@ def test_full_model_late_step_32_layers():
     # locked rows' caches untouched in every layer
     assert torch.equal(kc[:, 0, lk], kc_lock0) and torch.equal(vc[:, 0, lk], vc_lock0)
     kl = st.kl[:M].cpu().numpy()
-    assert np.max(np.abs(kl - ref.kl)) <= KL_BAND
+    say("late-step KL: max |d| against the oracle %.3e (bound %.3e)" % (float(np.max(np.abs(kl - ref.kl))), kl_band))
+    assert np.max(np.abs(kl - ref.kl)) <= kl_band
     # gate, lock, compaction and sampler on identical inputs: the GPU's logits, the same previous posterior
     stg = O.posterior_stats(gz, prev64, dm.mask_id)
     lr = O.lock_update(locked, act, off, B, N, stg.kl, stg.u, cand0, eps, gate, True)
