@@ -381,7 +381,7 @@ struct TrCfg {
   static constexpr int kStage = 2 * kTile;             // K + V of one group's tile
   static constexpr int kPipe = 2 * G * kStage;
   static constexpr int kMerge = (G - 1) * QW * kTrMergeWave * 4;
-  static constexpr int kEpi = QW * 32 * (kTrDh + 1) * 4;
+  static constexpr int kEpi = QW * 32 * (kTrDh + 4) * 4;
   static constexpr int kSmem = kPipe > kMerge ? (kPipe > kEpi ? kPipe : kEpi) : (kMerge > kEpi ? kMerge : kEpi);
   static constexpr int kDma = kTile / (64 * QW * 16);  // direct loads per thread per K (or V) tile
   static_assert(kThreads == 512 && kDma >= 1 && kTile % (64 * QW * 16) == 0 && BKV % 32 == 0, "shape");
@@ -628,18 +628,21 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
   const int nrow = min(32, row_end - wrow0);
   if (nsplit == 1) {
     // the normalised bf16 output, staged through LDS as a row-major fp32 tile so that every store
-    // writes 16 consecutive bytes of a row (measured faster than 8-byte stores from the registers)
+    // writes 16 consecutive bytes of a row (measured faster than 8-byte stores from the registers).
+    // Rows of Dh + 4 floats: a lane's run of four columns is one 16-byte write, and the 16 lanes a
+    // 16-byte access serves at a time (rows l32 .. l32 + 15) start on 16 distinct 4-bank groups.
+    constexpr int LDE = Dh + 4;
     __syncthreads();   // merge area free for the output staging
     const float inv = l_tot > 0.f ? 1.f / l_tot : 1.f;
-    float* ep = (float*)smem + wq * 32 * (Dh + 1);
+    float* ep = (float*)smem + wq * 32 * LDE;
     if (grp == 0) {
 #pragma unroll
       for (int dt = 0; dt < Dh / 32; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int d = dt * 32 + (v >> 2) * 8 + 4 * hl + (v & 3);
-          ep[l32 * (Dh + 1) + d] = oacc[dt][v] * inv;
-        }
+        for (int vb = 0; vb < 4; ++vb)
+          *(f32x4*)(ep + l32 * LDE + dt * 32 + vb * 8 + 4 * hl) =
+              f32x4{oacc[dt][4 * vb] * inv, oacc[dt][4 * vb + 1] * inv, oacc[dt][4 * vb + 2] * inv,
+                    oacc[dt][4 * vb + 3] * inv};
     }
     __syncthreads();
     if (grp == 0 && wave_live) {
@@ -647,10 +650,13 @@ attn_tr_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf
       for (int id = lane; id < 32 * CPR; id += 64) {
         const int rr = id / CPR, c = id % CPR;
         if (rr < nrow) {
-          const float* src = ep + rr * (Dh + 1) + c * E;
+          const float* src = ep + rr * LDE + c * E;
+          const f32x4 y0 = *(const f32x4*)src, y1 = *(const f32x4*)(src + 4);
           u32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(src[2 * i], src[2 * i + 1]);
+          w[0] = pack_bf16x2(y0[0], y0[1]);
+          w[1] = pack_bf16x2(y0[2], y0[3]);
+          w[2] = pack_bf16x2(y1[0], y1[1]);
+          w[3] = pack_bf16x2(y1[2], y1[3]);
           st16((char*)(out + (size_t)(wrow0 + rr) * HD + (size_t)h * Dh) + c * 16, w);
         }
       }
